@@ -1,0 +1,37 @@
+"""fp64 CPU oracle of streaming chunk-causal attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library (no kernels, headers,
+helpers, tables or pre/post-processing); both sides only consume the same seeded
+inputs from the separate `synth` package.
+
+What it computes (StreamRender-H3 project page, "3.1.2 Historical Context and
+Temporal Consistency", prefix-cache paragraph, and "3.3 Inference Acceleration
+and End-to-End Deployment", static-context KV caching and persistent KV layout):
+the current chunk's query tokens attend, with one softmax per row, over the
+persistent (reference image + prompt) tokens of the denoising step's bank, the
+recent history chunks kept in the rolling window, and the current chunk itself,
+bidirectionally inside each causal block of the current chunk.  The method
+reaches the plain masked softmax-attention result exactly (the online softmax
+only reorders the rounding), so the oracle is that definition written out.
+
+Modules
+  attention      masked scaled-dot-product attention, the definition (fp64)
+  cache_model    the streaming cache: persistent banks, rolling window, current chunk
+  chunk_attention  one attention call of the current chunk over the cache model
+  full_sequence  an independent dense path over the whole stream with an explicit mask
+  brute          arbitrary-precision (decimal) brute force for tiny inputs
+
+Every function has at least one pin in tests/test_oracle_pins.py that does not
+go through the function itself (closed forms, invariants, brute force, an
+independent path).  Parity status: pinned, except where a docstring says
+"parity unpinned".
+"""
+from .attention import masked_attention, widen
+from .cache_model import StreamingCache, CacheStateError
+from .chunk_attention import chunk_attention, current_block_mask
+from .full_sequence import full_sequence_attention
+from .brute import brute_attention
+
+__all__ = ["masked_attention", "widen", "StreamingCache", "CacheStateError", "chunk_attention",
+           "current_block_mask", "full_sequence_attention", "brute_attention"]

@@ -1,0 +1,204 @@
+"""Workload recipes: shapes, distributions and chunk processes of the streaming attention.
+
+Shapes follow the resolutions and chunk sizes on the StreamRender-H3 pages (an
+832x480 or 1280x720 frame downsampled 16x per side gives 52x30 = 1560 or
+80x45 = 3600 tokens per latent frame; chunks of three or two latent frames), with
+the sink/prefix of reference-image tokens plus 512 prompt tokens and a rolling
+window of past chunks ("A window that slides, and a prefix that doesn't" on the
+teardown page; "3.1.2 Historical Context and Temporal Consistency" on the
+project page).  Head counts and head width are stand-ins: the pages do not give
+H3's attention geometry.
+
+Every tensor is drawn from a named counter-based sub-stream (see rng.py), as
+fp32 (Gaussian * std) and, for bf16 workloads, rounded to bf16 bit patterns.
+Layouts are token-major: chunk tensors [n][H][D], persistent banks [banks][P][H][D].
+"""
+from dataclasses import dataclass, replace
+import math
+import numpy as np
+
+from .rng import substream_seed, uniform01
+from ._native import normal_f64, f32_to_bf16
+
+_SIGMA = 1.0 / math.sqrt(128.0)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int            # seed offset: base seed = 20261012 + index
+    dtype: str            # "bf16" or "f32" storage / input type
+    heads: int
+    head_dim: int
+    persistent: int       # P: reference-image + prompt tokens per bank
+    chunk: int            # tokens per chunk (= queries per attention call)
+    window: int           # W: past chunks kept in the window
+    causal_block: int     # tokens per causal block inside the current chunk
+    banks: int            # persistent banks (one per denoising step)
+    chunks: int           # chunks streamed in the session
+    steps: int            # denoising steps per chunk
+    qk_std: float
+    v_std: float
+    boost_fraction: float = 0.0   # fraction of visible key tokens scaled by `boost`
+    boost: float = 30.0
+    ar_rho: float = 0.0           # AR(1) coefficient of the chunk process (0: iid)
+    single_step: bool = True      # only the last chunk-step (full window) is of interest
+
+    @property
+    def seed(self):
+        return 20261012 + self.index
+
+    @property
+    def visible_keys(self):
+        """Keys visible to the last block of the current chunk at full window."""
+        return self.persistent + min(self.window, self.chunks - 1) * self.chunk + self.chunk
+
+    def scaled(self, **kw):
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny oracle check: fp32, 2 heads x 64, 16 persistent tokens, window 2 x 32, 4 chunks streamed
+    "c0": Workload("c0", 0, "f32", 2, 64, 16, 32, 2, 32, 1, 4, 1, 1.0, 1.0, single_step=False),
+    # 832x480 chunk-step: 24 heads, 1560 ref + 512 prompt, 2 past chunks of 3 frames x 1560
+    "c1": Workload("c1", 1, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, _SIGMA, _SIGMA),
+    # streaming session at c1 shapes: 32 chunks x 2 steps, bank per step, AR(1) rho=0.9 chunk process
+    "c2": Workload("c2", 2, "bf16", 24, 128, 2072, 4680, 2, 4680, 2, 32, 2, _SIGMA, _SIGMA,
+                   ar_rho=0.9, single_step=False),
+    # 720p chunk-step: 40 heads, 3600 ref + 512 prompt, 3 past chunks of 2 frames x 3600
+    "c3": Workload("c3", 3, "bf16", 40, 128, 4112, 7200, 3, 7200, 1, 4, 1, _SIGMA, _SIGMA),
+    # semantic-conditioned stress: frames of 1560 video + 1560 semantic tokens, frame-causal,
+    # 32 heads, 1% of visible keys scaled x30
+    "c4": Workload("c4", 4, "bf16", 32, 128, 2072, 9360, 2, 3120, 1, 3, 1, _SIGMA, _SIGMA,
+                   boost_fraction=0.01),
+    # stress variants: unit-variance Q,K so logits are O(1) (and O(100) on boosted keys)
+    "c1s": Workload("c1s", 11, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, 1.0, _SIGMA),
+    "c4s": Workload("c4s", 14, "bf16", 32, 128, 2072, 9360, 2, 3120, 1, 3, 1, 1.0, _SIGMA,
+                    boost_fraction=0.01),
+    # reduced shapes the oracle finishes in seconds; they still span several tiles and ragged tails
+    "t_stream": Workload("t_stream", 21, "bf16", 3, 128, 300, 600, 2, 600, 2, 5, 2, 1.0, 1.0,
+                         ar_rho=0.9, single_step=False),
+    "t_frame": Workload("t_frame", 22, "bf16", 2, 128, 200, 780, 2, 390, 1, 3, 1, 1.0, _SIGMA,
+                        boost_fraction=0.01),
+    "t_d64": Workload("t_d64", 23, "bf16", 3, 64, 130, 333, 1, 111, 1, 3, 1, 1.0, 1.0),
+    "t_f32": Workload("t_f32", 24, "f32", 2, 128, 70, 200, 2, 200, 1, 4, 1, 1.0, 1.0, single_step=False),
+}
+
+
+def get_workload(name):
+    return WORKLOADS[name]
+
+
+def _draw(w, tag, shape, std, chunk=0, step=0, bank=0):
+    n = int(np.prod(shape))
+    return normal_f64(substream_seed(w.seed, tag, chunk, step, bank), n, std).reshape(shape)
+
+
+def _store(w, x64):
+    """fp64 draw -> storage array (fp32, or bf16 bit patterns as uint16)."""
+    f = np.asarray(x64, dtype=np.float32)
+    return f32_to_bf16(f) if w.dtype == "bf16" else f
+
+
+def _boost_positions(w):
+    """Partial Fisher-Yates over the logical visible key sequence of the last chunk-step."""
+    nk = w.visible_keys
+    m = int(math.floor(w.boost_fraction * nk))
+    if m == 0:
+        return np.zeros(0, dtype=np.int64)
+    u = uniform01(substream_seed(w.seed, "X30"), m)
+    perm = np.arange(nk, dtype=np.int64)
+    for i in range(m):
+        j = i + int(math.floor(u[i] * (nk - i)))
+        j = min(j, nk - 1)
+        perm[i], perm[j] = perm[j], perm[i]
+    return np.sort(perm[:m])
+
+
+def persistent_inputs(w):
+    """Persistent K/V banks, [banks][P][H][D] fp64 draws (before the boost and rounding)."""
+    shape = (w.persistent, w.heads, w.head_dim)
+    pk = np.stack([_draw(w, "PK", shape, w.qk_std, bank=b) for b in range(w.banks)]) if w.persistent else \
+        np.zeros((w.banks, 0, w.heads, w.head_dim))
+    pv = np.stack([_draw(w, "PV", shape, w.v_std, bank=b) for b in range(w.banks)]) if w.persistent else \
+        np.zeros((w.banks, 0, w.heads, w.head_dim))
+    return pk, pv
+
+
+class SessionStream:
+    """Seeded chunk-step stream of a workload.
+
+    `persistent()` gives the stored persistent banks.  Iterating yields one dict per
+    chunk-step in order: {"chunk", "step", "bank", "evict_before", "k", "v", "q"}.
+    `evict_before` is True on the first step of a chunk that needs the oldest history
+    chunk dropped (the window already holds W chunks).  For chunk processes with
+    rho > 0 the last step of chunk c carries the committed K*_c, V*_c with
+    K*_c = rho K*_{c-1} + sqrt(1 - rho^2) std eps_c; earlier steps carry
+    rho K*_c + sqrt(1 - rho^2) std eta_c (a noisier version of the same chunk).
+    """
+
+    def __init__(self, w):
+        self.w = w
+        self._boost = _boost_positions(w) if w.boost_fraction > 0 else None
+
+    def _boost_rows(self, x, start):
+        """Scale the boosted logical key positions that fall in [start, start + len(x))."""
+        if self._boost is None:
+            return x
+        sel = self._boost[(self._boost >= start) & (self._boost < start + x.shape[0])] - start
+        if sel.size:
+            x = x.copy()
+            x[sel] *= self.w.boost
+        return x
+
+    def persistent(self):
+        pk, pv = persistent_inputs(self.w)
+        pk = np.stack([self._boost_rows(pk[b], 0) for b in range(self.w.banks)])
+        return _store(self.w, pk), _store(self.w, pv)
+
+    def __iter__(self):
+        w = self.w
+        shape = (w.chunk, w.heads, w.head_dim)
+        kstar = vstar = None
+        for c in range(w.chunks):
+            if w.ar_rho > 0:
+                a, b = w.ar_rho, math.sqrt(1.0 - w.ar_rho ** 2)
+                ek = _draw(w, "KSTAR", shape, w.qk_std, chunk=c)
+                ev = _draw(w, "VSTAR", shape, w.v_std, chunk=c)
+                kstar = ek if kstar is None else a * kstar + b * ek
+                vstar = ev if vstar is None else a * vstar + b * ev
+            # before chunk c the window holds min(c - 1, W) committed chunks; it is full from c = W + 1 on
+            evict = w.window > 0 and c >= w.window + 1
+            # logical start of this chunk's keys in the last chunk-step's visible sequence (None: evicted)
+            age = w.chunks - 1 - c
+            start = w.persistent + (w.window - age) * w.chunk if (w.single_step and age <= w.window) else None
+            for s in range(w.steps):
+                if w.ar_rho > 0:
+                    if s == w.steps - 1:
+                        k, v = kstar, vstar
+                    else:
+                        k = a * kstar + b * _draw(w, "K_STEP0", shape, w.qk_std, chunk=c, step=s)
+                        v = a * vstar + b * _draw(w, "V_STEP0", shape, w.v_std, chunk=c, step=s)
+                else:
+                    k = _draw(w, "K", shape, w.qk_std, chunk=c, step=s)
+                    v = _draw(w, "V", shape, w.v_std, chunk=c, step=s)
+                if start is not None:
+                    k = self._boost_rows(k, start)
+                q = _draw(w, "Q", shape, w.qk_std, chunk=c, step=s)
+                yield {"chunk": c, "step": s, "bank": s % w.banks, "evict_before": evict and s == 0,
+                       "k": _store(w, k), "v": _store(w, v), "q": _store(w, q)}
+
+
+def single_step_inputs(w):
+    """Persistent banks, the W history chunks and the current chunk of a single-step workload.
+
+    Returns (pk, pv, history [(k, v)] oldest first, (k, v, q) current)."""
+    pk, pv = SessionStream(w).persistent()
+    hist, cur = [], None
+    for ev in SessionStream(w):
+        if ev["chunk"] < w.chunks - 1:
+            if ev["step"] == w.steps - 1:
+                hist.append((ev["k"], ev["v"]))
+        else:
+            cur = (ev["k"], ev["v"], ev["q"])
+    return pk, pv, hist[-w.window:] if w.window else [], cur

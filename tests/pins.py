@@ -1,0 +1,204 @@
+"""Pins of the oracle against facts fixed by the pages and by the mathematics.
+
+Each pin takes the oracle callables it checks as arguments, so that
+test_oracle_mutations.py can run the same pins against copies of the oracle
+with a planted mistake and show that the pin catches it.
+"""
+import math
+
+import numpy as np
+
+from oracle import brute_attention
+from oracle.full_sequence import stream_mask
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def pin_rows_sum_to_one(attn):
+    """Every softmax row over the visible keys sums to 1 (hidden keys get 0)."""
+    r = _rng(1)
+    q, k, v = r.standard_normal((7, 5)), r.standard_normal((11, 5)), r.standard_normal((11, 3))
+    vis = r.random((7, 11)) < 0.6
+    vis[:, 0] = True
+    _, _, p = attn(q, k, v, vis, 0.7, return_probs=True)
+    assert np.abs(p.sum(axis=1) - 1.0).max() <= 1e-14
+    assert (p[~vis] == 0).all()
+
+
+def pin_single_key(attn):
+    """One visible key: the output is that key's value, exactly; lse is its logit."""
+    r = _rng(2)
+    q, k, v = r.standard_normal((4, 6)), r.standard_normal((5, 6)), r.standard_normal((5, 6))
+    vis = np.zeros((4, 5), dtype=bool)
+    for i, j in enumerate([3, 0, 4, 3]):
+        vis[i, j] = True
+    o, lse = attn(q, k, v, vis, 0.3)
+    for i, j in enumerate([3, 0, 4, 3]):
+        assert (o[i] == v[j]).all()
+        assert abs(lse[i] - 0.3 * float(q[i] @ k[j])) <= 1e-14 * max(1.0, abs(lse[i]))
+
+
+def pin_equal_scores_mean(attn):
+    """Equal logits (q = 0) give the mean of the visible values, and lse = ln(#visible)."""
+    r = _rng(3)
+    q = np.zeros((3, 4))
+    k, v = r.standard_normal((9, 4)), r.standard_normal((9, 2))
+    vis = np.ones((3, 9), dtype=bool)
+    vis[1, 5:] = False
+    vis[2, ::2] = False
+    o, lse = attn(q, k, v, vis, 1.0)
+    for i in range(3):
+        m = v[vis[i]].mean(axis=0)
+        assert np.abs(o[i] - m).max() <= 1e-15 * 10 * max(1.0, np.abs(m).max())
+        assert abs(lse[i] - math.log(vis[i].sum())) <= 1e-14
+
+
+def pin_two_key_closed_form(attn):
+    """Logits {0, ln 3} give o = (v1 + 3 v2) / 4 and lse = ln 4 (scale != 1 on purpose)."""
+    scale = 0.125
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[0.0, 5.0], [math.log(3.0) / scale, -2.0]])
+    v = np.array([[1.0, -2.0, 0.5], [3.0, 4.0, -1.5]])
+    o, lse = attn(q, k, v, np.ones((1, 2), dtype=bool), scale)
+    assert np.abs(o[0] - (v[0] + 3 * v[1]) / 4).max() <= 1e-15 * 4
+    assert abs(lse[0] - math.log(4.0)) <= 1e-15 * 2
+
+
+def pin_brute_force(attn, seeds=range(6)):
+    """Random tiny problems against the decimal brute force (no max shift)."""
+    for s in seeds:
+        r = _rng(100 + s)
+        nq, nk, d, dv = r.integers(1, 5), r.integers(1, 7), r.integers(1, 5), r.integers(1, 4)
+        q, k, v = r.standard_normal((nq, d)) * 2, r.standard_normal((nk, d)) * 2, r.standard_normal((nk, dv))
+        vis = r.random((nq, nk)) < 0.7
+        vis[np.arange(nq), r.integers(0, nk, nq)] = True
+        scale = float(r.uniform(0.1, 1.5))
+        o, lse = attn(q, k, v, vis, scale)
+        ob, lb = brute_attention(q.tolist(), k.tolist(), v.tolist(), vis.tolist(), scale)
+        assert np.abs(o - np.array(ob)).max() <= 1e-13 * max(1.0, np.abs(ob).max())
+        assert np.abs(lse - np.array(lb)).max() <= 1e-13 * max(1.0, np.abs(lb).max())
+
+
+def pin_invariants(attn):
+    """Shift of all keys by u, affine map of V, permutation of keys, convex hull."""
+    r = _rng(4)
+    q, k, v = r.standard_normal((6, 8)), r.standard_normal((13, 8)), r.standard_normal((13, 5))
+    vis = r.random((6, 13)) < 0.5
+    vis[:, 7] = True
+    o, _ = attn(q, k, v, vis, 0.4)
+    u = r.standard_normal(8)
+    o2, _ = attn(q, k + u, v, vis, 0.4)          # adds 0.4*q.u to every logit of a row
+    assert np.abs(o2 - o).max() <= 1e-12
+    o3, _ = attn(q, k, 2.5 * v - 1.25, vis, 0.4)
+    assert np.abs(o3 - (2.5 * o - 1.25)).max() <= 1e-12
+    perm = r.permutation(13)
+    o4, _ = attn(q, k[perm], v[perm], vis[:, perm], 0.4)
+    assert np.abs(o4 - o).max() <= 1e-12
+    for i in range(6):
+        lo, hi = v[vis[i]].min(axis=0), v[vis[i]].max(axis=0)
+        assert (o[i] >= lo - 1e-12).all() and (o[i] <= hi + 1e-12).all()
+
+
+ALL_ATTENTION_PINS = [pin_rows_sum_to_one, pin_single_key, pin_equal_scores_mean, pin_two_key_closed_form,
+                      pin_brute_force, pin_invariants]
+
+
+# ---------------------------------------------------------------- streaming pins
+
+def _tiny_stream(seed, n_chunks, steps, banks, P, Tc, H, D, dtype="f32"):
+    r = _rng(seed)
+    cast = (lambda a: a.astype(np.float32))
+    pk = cast(r.standard_normal((banks, P, H, D)))
+    pv = cast(r.standard_normal((banks, P, H, D)))
+    chunks = []
+    for c in range(n_chunks):
+        chunks.append([(cast(r.standard_normal((Tc, H, D))), cast(r.standard_normal((Tc, H, D))),
+                        cast(r.standard_normal((Tc, H, D)))) for _ in range(steps)])
+    return pk, pv, chunks
+
+
+def pin_stream_equals_full_sequence(cache_cls, chunk_attn, full_attn, window=2, causal_block=3, n_chunks=6,
+                                    steps=2, banks=2, P=5, Tc=7, H=2, D=4, seed=7):
+    """Chunk-by-chunk through the cache == one dense pass over the whole stream with the window mask."""
+    pk, pv, chunks = _tiny_stream(seed, n_chunks, steps, banks, P, Tc, H, D)
+    cache = cache_cls(pk, pv, window)
+    committed_k, committed_v = [], []
+    scale = 0.45
+    for c in range(n_chunks):
+        if window > 0 and c >= window + 1:
+            cache.evict()
+        for s in range(steps):
+            k, v, q = chunks[c][s]
+            cache.append(c, k, v)
+            bank = s % banks
+            o, lse = chunk_attn(cache, bank, q, scale, causal_block, "f32")
+            of, lf = full_attn(pk[bank], pv[bank], committed_k + [k], committed_v + [v], q, window,
+                               causal_block, scale, "f32")
+            assert np.abs(o - of).max() <= 1e-12, (c, s)
+            assert np.abs(lse - lf).max() <= 1e-12, (c, s)
+        committed_k.append(chunks[c][steps - 1][0])
+        committed_v.append(chunks[c][steps - 1][1])
+
+
+def pin_stream_brute_force(cache_cls, chunk_attn, seeds=range(4)):
+    """Tiny streams (all chunk-steps, evictions included) against the decimal brute force,
+    the visible set written out from the window rule: prefix, last W committed chunks, own block."""
+    for sd in seeds:
+        r = _rng(200 + sd)
+        W, cb, P, Tc, H, D = int(r.integers(0, 3)), int(r.integers(1, 5)), int(r.integers(1, 4)), \
+            int(r.integers(1, 5)), int(r.integers(1, 3)), int(r.integers(1, 5))
+        pk, pv, chunks = _tiny_stream(300 + sd, 4, 2, 1, P, Tc, H, D)
+        cache = cache_cls(pk, pv, W)
+        done = []
+        for c in range(4):
+            if W > 0 and c >= W + 1:
+                cache.evict()
+            for s in range(2):
+                k, v, q = chunks[c][s]
+                cache.append(c, k, v)
+                o, _ = chunk_attn(cache, 0, q, 0.6, cb, "f32")
+                hist = done[-W:] if W else []
+                K = np.concatenate([pk[0]] + [x[0] for x in hist] + [k]).astype(np.float64)
+                V = np.concatenate([pv[0]] + [x[1] for x in hist] + [v]).astype(np.float64)
+                nfix = K.shape[0] - Tc
+                for h in range(H):
+                    vis = [[j < nfix or (j - nfix) // cb <= i // cb for j in range(K.shape[0])] for i in range(Tc)]
+                    ob, _ = brute_attention(q[:, h].astype(np.float64).tolist(), K[:, h].tolist(), V[:, h].tolist(),
+                                            vis, 0.6)
+                    assert np.abs(o[:, h] - np.array(ob)).max() <= 1e-13 * max(1.0, np.abs(ob).max()), (sd, c, s, h)
+            done.append(chunks[c][1])
+
+
+def pin_window_rule(cache_cls, seed=11, n_ops=400):
+    """After any valid sequence of appends/evicts, the visible chunk ids are the last
+    (<= W) committed ids in order, then the current id; invalid calls change nothing."""
+    r = _rng(seed)
+    for W in range(0, 4):
+        pk = np.zeros((1, 1, 1, 1), np.float32)
+        cache = cache_cls(pk, pk, W)
+        cur, hist = None, []
+        x = np.zeros((1, 1, 1), np.float32)
+        for _ in range(n_ops):
+            op = r.integers(0, 4)
+            if op == 0:
+                try:
+                    e = cache.evict()
+                    assert hist and e == hist.pop(0)
+                except Exception as ex:
+                    assert not hist, ex
+            else:
+                cid = (int(r.integers(0, 1000)) if cur is None else
+                       cur + (0 if op == 1 else 1 if op == 2 else int(r.integers(-3, 4))))
+                ok = cid >= 0 and (cur is None or cid == cur or
+                                   (cid == cur + 1 and (W == 0 or len(hist) < W)))
+                try:
+                    cache.append(cid, x, x)
+                    assert ok
+                    if cur is not None and cid == cur + 1 and W > 0:
+                        hist.append(cur)
+                    cur = cid
+                except Exception as ex:
+                    assert not ok, ex
+            assert cache.visible_ids() == hist + ([cur] if cur is not None else [])

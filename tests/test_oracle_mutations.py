@@ -1,0 +1,133 @@
+"""Each plausible mistake planted in a copy of the oracle is caught by at least one pin.
+
+The mutants are written here, on the CPU, as small variants of the oracle's
+functions; the real oracle is untouched.  A mutant "survives" if every pin in
+its list passes -- that would mean the pins cannot tell it from the real oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from oracle.attention import widen
+from oracle.chunk_attention import current_block_mask
+
+
+def _attn_variant(kind):
+    def attn(q, k, v, visible, scale, return_probs=False):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        visible = np.asarray(visible, dtype=bool)
+        if kind == "no_scale":
+            s = q @ k.T
+        elif kind == "sign":
+            s = -scale * (q @ k.T)
+        elif kind == "dropped_dim":
+            s = scale * (q[:, :-1] @ k[:, :-1].T) if q.shape[1] > 1 else scale * 0 * (q @ k.T)
+        else:
+            s = scale * (q @ k.T)
+        if kind != "ignore_mask":
+            s = np.where(visible, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        l = w.sum(axis=1, keepdims=True)
+        o = (w @ v) if kind == "no_normalise" else (w @ v) / l
+        if kind == "value_transposed" and v.shape[0] == v.shape[1]:
+            o = (w @ v.T) / l
+        lse = (np.log(l[:, 0]) if kind == "lse_no_max" else m[:, 0] + np.log(l[:, 0]))
+        if return_probs:
+            return o, lse, w / l if kind != "no_normalise" else w
+        return o, lse
+    return attn
+
+
+ATTENTION_MUTANTS = ["no_scale", "sign", "dropped_dim", "ignore_mask", "no_normalise", "lse_no_max"]
+
+
+def _caught(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ATTENTION_MUTANTS)
+def test_attention_mutant_is_caught(kind):
+    attn = _attn_variant(kind)
+    assert any(_caught(p, attn) for p in pins.ALL_ATTENTION_PINS), kind
+
+
+def _chunk_attention_variant(kind):
+    def chunk_attn(cache, bank, q, scale, causal_block, dtype):
+        if kind == "bank0":
+            bank = 0
+        k, v, n_fixed = cache.sequence(bank)
+        n_cur = k.shape[0] - n_fixed
+        rows = np.arange(n_cur)
+        H = q.shape[1]
+        o = np.zeros((n_cur, H, v.shape[2]))
+        lse = np.zeros((H, n_cur))
+        for h in range(H):
+            if kind == "strict_block":
+                cur = (np.arange(n_cur)[None, :] // causal_block) < (rows[:, None] // causal_block)
+                cur[np.arange(n_cur), np.arange(n_cur)] = True
+            elif kind == "block_off_by_one":
+                cur = (np.arange(n_cur)[None, :] // causal_block) <= ((rows[:, None] + 1) // causal_block)
+            elif kind == "token_causal":
+                cur = np.arange(n_cur)[None, :] <= rows[:, None]
+            else:
+                cur = current_block_mask(rows, n_cur, causal_block)
+            if kind == "history_hidden":
+                fixed = np.zeros((n_cur, n_fixed), bool)
+                fixed[:, :cache.pk[bank].shape[0]] = True
+            else:
+                fixed = np.ones((n_cur, n_fixed), bool)
+            vis = np.concatenate([fixed, cur], axis=1)
+            o[:, h], lse[h] = oracle.masked_attention(widen(q[:, h], dtype), widen(k[:, h], dtype),
+                                                      widen(v[:, h], dtype), vis, scale)
+        return o, lse
+    return chunk_attn
+
+
+@pytest.mark.parametrize("kind", ["bank0", "strict_block", "block_off_by_one", "token_causal", "history_hidden"])
+def test_chunk_attention_mutant_is_caught(kind):
+    ca = _chunk_attention_variant(kind)
+    assert _caught(pins.pin_stream_equals_full_sequence, oracle.StreamingCache, ca,
+                   oracle.full_sequence_attention) or \
+        _caught(pins.pin_stream_brute_force, oracle.StreamingCache, ca), kind
+
+
+class _EvictNewest(oracle.StreamingCache):
+    def evict(self):
+        if not self.history:
+            raise oracle.CacheStateError("empty")
+        return self.history.pop()[0]
+
+
+class _CommitFirstStep(oracle.StreamingCache):
+    def append(self, chunk_id, k, v):
+        if self.current is not None and chunk_id == self.current[0]:
+            return  # keeps the first step's K/V instead of the last
+        super().append(chunk_id, k, v)
+
+
+class _Uncapped(oracle.StreamingCache):
+    def append(self, chunk_id, k, v):
+        if self.current is not None and chunk_id == self.current[0] + 1 and self.window > 0:
+            self.history.append(self.current)
+            self.current = (chunk_id, np.array(k), np.array(v))
+            return
+        super().append(chunk_id, k, v)
+
+
+class _OrderReversed(oracle.StreamingCache):
+    def visible_ids(self):
+        return [c for c, _, _ in reversed(self.history)] + ([self.current[0]] if self.current else [])
+
+
+@pytest.mark.parametrize("cls", [_EvictNewest, _CommitFirstStep, _Uncapped, _OrderReversed],
+                         ids=lambda c: c.__name__)
+def test_cache_model_mutant_is_caught(cls):
+    assert _caught(pins.pin_window_rule, cls) or \
+        _caught(pins.pin_stream_equals_full_sequence, cls, oracle.chunk_attention, oracle.full_sequence_attention) \
+        or _caught(pins.pin_stream_brute_force, cls, oracle.chunk_attention), cls.__name__

@@ -1,0 +1,78 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_ATTENTION_PINS, ids=lambda f: f.__name__)
+def test_attention_definition(pin):
+    pin(oracle.masked_attention)
+
+
+def test_stream_equals_full_sequence():
+    pins.pin_stream_equals_full_sequence(oracle.StreamingCache, oracle.chunk_attention,
+                                         oracle.full_sequence_attention)
+
+
+@pytest.mark.parametrize("window,cb", [(0, 7), (1, 1), (3, 2)])
+def test_stream_equals_full_sequence_shapes(window, cb):
+    pins.pin_stream_equals_full_sequence(oracle.StreamingCache, oracle.chunk_attention,
+                                         oracle.full_sequence_attention, window=window, causal_block=cb,
+                                         n_chunks=7, seed=window * 10 + cb)
+
+
+def test_stream_brute_force():
+    pins.pin_stream_brute_force(oracle.StreamingCache, oracle.chunk_attention)
+
+
+def test_window_rule():
+    pins.pin_window_rule(oracle.StreamingCache)
+
+
+def test_prefix_rows_see_only_prefix():
+    """Prefix rows (building a bank) attend to the prefix alone: equal to masked attention
+    over the prefix and independent of anything appended after it."""
+    from oracle.full_sequence import prefix_self_attention
+    r = np.random.default_rng(5)
+    pk, pv, pq = (r.standard_normal((6, 2, 3)).astype(np.float32) for _ in range(3))
+    o = prefix_self_attention(pk, pv, pq, 0.5, "f32")
+    for h in range(2):
+        ref, _ = oracle.masked_attention(pq[:, h].astype(float), pk[:, h].astype(float), pv[:, h].astype(float),
+                                         np.ones((6, 6), bool), 0.5)
+        assert np.abs(o[:, h] - ref).max() <= 1e-14
+
+
+def test_masked_future_keys_do_not_matter():
+    """Changing keys/values of later causal blocks leaves earlier rows bit-identical."""
+    r = np.random.default_rng(9)
+    pk = r.standard_normal((1, 4, 2, 8)).astype(np.float32)
+    cache = oracle.StreamingCache(pk, pk, 1)
+    k, v, q = (r.standard_normal((12, 2, 8)).astype(np.float32) for _ in range(3))
+    cache.append(0, k, v)
+    o1, l1 = oracle.chunk_attention(cache, 0, q, 0.3, 4, "f32")
+    k2, v2 = k.copy(), v.copy()
+    k2[8:] = 1e3
+    v2[8:] = -7.0
+    cache.append(0, k2, v2)
+    o2, l2 = oracle.chunk_attention(cache, 0, q, 0.3, 4, "f32")
+    assert (o1[:8] == o2[:8]).all() and (l1[:, :8] == l2[:, :8]).all()
+    assert not (o1[8:] == o2[8:]).all()
+
+
+def test_widen_bf16_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0xFF80, 0x0000, 0x8000], dtype=np.uint16)
+    ref = np.array([1.0, -1.0, 2.0 ** -133, 3.3895313892515355e38, -np.inf, 0.0, -0.0])
+    assert (oracle.widen(bits, "bf16") == ref).all()
+
+
+def test_lse_large_logits_finite():
+    """Logits ~1e3 (far past fp32 exp overflow unshifted) stay finite and exact in the max-shift form."""
+    q = np.array([[1.0]])
+    k = np.array([[1000.0], [999.0]])
+    v = np.array([[1.0], [0.0]])
+    o, lse = oracle.masked_attention(q, k, v, np.ones((1, 2), bool), 1.0)
+    e = np.exp(-1.0)
+    assert abs(o[0, 0] - 1.0 / (1.0 + e)) <= 1e-15
+    assert abs(lse[0] - (1000.0 + np.log1p(e))) <= 1e-12
