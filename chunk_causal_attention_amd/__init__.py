@@ -1,0 +1,267 @@
+"""Python binding of libsr: streaming chunk-causal attention over a paged KV cache (gfx950).
+
+Thin ctypes layer over the C ABI declared in include/sr.h: the functions below carry the
+C names and only marshal arguments (tensor pointers, the current HIP stream, status
+codes -> exceptions).  All work runs in the library's HIP kernels; there is no fallback.
+PyTorch provides device memory and streams.  Importing the package does not need a GPU;
+calling into the library does need the built libsr.so (build() or
+`python -m chunk_causal_attention_amd.build`).
+"""
+import ctypes
+import os
+
+__all__ = [
+    "SrError", "sr_kvcache_config", "sr_segment", "load", "build", "config_for",
+    "sr_kvcache_required_bytes", "sr_kvcache_init", "sr_kvcache_append_chunk", "sr_kvcache_evict",
+    "sr_chunk_attention", "sr_kvcache_gather", "sr_kvcache_ring", "sr_kvcache_destroy",
+    "sr_ring_create", "sr_ring_append", "sr_ring_evict", "sr_ring_segments", "sr_ring_destroy",
+    "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "PAGE_TOKENS", "MAX_WINDOW",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsr.so")
+
+SR_OK, SR_E_INVALID, SR_E_STATE, SR_E_NOMEM, SR_E_DEVICE, SR_E_UNSUPPORTED = range(6)
+SR_BF16, SR_F32 = 0, 1
+PAGE_TOKENS = 128
+MAX_WINDOW = 14
+
+
+class SrError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+
+
+_STATUS_NAMES = {0: "SR_OK", 1: "SR_E_INVALID", 2: "SR_E_STATE", 3: "SR_E_NOMEM", 4: "SR_E_DEVICE",
+                 5: "SR_E_UNSUPPORTED"}
+
+
+class sr_kvcache_config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("persistent_tokens", ctypes.c_int32), ("num_banks", ctypes.c_int32),
+                ("chunk_capacity", ctypes.c_int32), ("window_chunks", ctypes.c_int32),
+                ("causal_block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class sr_segment(ctypes.Structure):
+    _fields_ = [("chunk_id", ctypes.c_int64), ("kind", ctypes.c_int32), ("slot", ctypes.c_int32),
+                ("page", ctypes.c_int32), ("length", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def build():
+    from .build import build as _b
+    return _b()
+
+
+def load():
+    """The loaded library.  torch is imported first so libsr binds to torch's HIP runtime."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (HIP runtime shared with torch)
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m chunk_causal_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    cfgp = ctypes.POINTER(sr_kvcache_config)
+    sig = {
+        "sr_kvcache_required_bytes": [cfgp, ctypes.POINTER(SZ)],
+        "sr_kvcache_init": [cfgp, P, SZ, P, P, P, ctypes.POINTER(P)],
+        "sr_kvcache_append_chunk": [P, I64, P, P, I32, P],
+        "sr_kvcache_evict": [P, ctypes.POINTER(I64)],
+        "sr_chunk_attention": [P, I32, P, P, P, F32, P],
+        "sr_kvcache_gather": [P, I32, P, P, I32, ctypes.POINTER(I32), P],
+        "sr_kvcache_destroy": [P],
+        "sr_ring_create": [cfgp, ctypes.POINTER(P)],
+        "sr_ring_append": [P, I64, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)],
+        "sr_ring_evict": [P, ctypes.POINTER(I64)],
+        "sr_ring_segments": [P, I32, ctypes.POINTER(sr_segment), I32, ctypes.POINTER(I32)],
+        "sr_ring_destroy": [P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.sr_kvcache_ring.argtypes = [P]
+    L.sr_kvcache_ring.restype = P
+    L.sr_status_string.argtypes = [ctypes.c_int]
+    L.sr_status_string.restype = ctypes.c_char_p
+    L.sr_last_error.argtypes = []
+    L.sr_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != SR_OK:
+        raise SrError(status, load().sr_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def config_for(num_heads, head_dim, persistent_tokens, chunk_capacity, window_chunks, causal_block=None,
+               num_banks=1, dtype=SR_BF16):
+    return sr_kvcache_config(num_heads, head_dim, persistent_tokens, num_banks, chunk_capacity, window_chunks,
+                             chunk_capacity if causal_block is None else causal_block, dtype)
+
+
+def sr_status_string(status):
+    return load().sr_status_string(status).decode()
+
+
+def sr_last_error():
+    return load().sr_last_error().decode()
+
+
+def sr_kvcache_required_bytes(cfg):
+    n = ctypes.c_size_t()
+    _check(load().sr_kvcache_required_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def sr_kvcache_init(cfg, pool, persistent_k=None, persistent_v=None, stream=None):
+    h = ctypes.c_void_p()
+    _check(load().sr_kvcache_init(ctypes.byref(cfg), _ptr(pool), pool.numel() * pool.element_size(),
+                                  _ptr(persistent_k), _ptr(persistent_v), _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def sr_kvcache_append_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
+    n = k.shape[0] if n_tokens is None else n_tokens
+    _check(load().sr_kvcache_append_chunk(h, chunk_id, _ptr(k), _ptr(v), n, _stream(stream)))
+
+
+def sr_kvcache_evict(h):
+    e = ctypes.c_int64(-1)
+    _check(load().sr_kvcache_evict(h, ctypes.byref(e)))
+    return e.value
+
+
+def sr_chunk_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    _check(load().sr_chunk_attention(h, bank, _ptr(q), _ptr(out), _ptr(lse), float(softmax_scale),
+                                     _stream(stream)))
+
+
+def sr_kvcache_gather(h, bank, k_out, v_out, stream=None):
+    n = ctypes.c_int32()
+    _check(load().sr_kvcache_gather(h, bank, _ptr(k_out), _ptr(v_out), k_out.shape[0], ctypes.byref(n),
+                                    _stream(stream)))
+    return n.value
+
+
+def sr_kvcache_ring(h):
+    return ctypes.c_void_p(load().sr_kvcache_ring(h))
+
+
+def sr_kvcache_destroy(h):
+    _check(load().sr_kvcache_destroy(h))
+
+
+def sr_ring_create(cfg):
+    r = ctypes.c_void_p()
+    _check(load().sr_ring_create(ctypes.byref(cfg), ctypes.byref(r)))
+    return r
+
+
+def sr_ring_append(r, chunk_id, n_tokens):
+    slot, com = ctypes.c_int32(), ctypes.c_int64()
+    _check(load().sr_ring_append(r, chunk_id, n_tokens, ctypes.byref(slot), ctypes.byref(com)))
+    return slot.value, com.value
+
+
+def sr_ring_evict(r):
+    e = ctypes.c_int64()
+    _check(load().sr_ring_evict(r, ctypes.byref(e)))
+    return e.value
+
+
+def sr_ring_segments(r, bank, max_segments=MAX_WINDOW + 2):
+    arr = (sr_segment * max_segments)()
+    n = ctypes.c_int32()
+    _check(load().sr_ring_segments(r, bank, arr, max_segments, ctypes.byref(n)))
+    return [(s.chunk_id, s.kind, s.slot, s.page, s.length) for s in arr[:n.value]]
+
+
+def sr_ring_destroy(r):
+    _check(load().sr_ring_destroy(r))
+
+
+class KVCache:
+    """Owns a pool tensor and a cache handle; methods call the C ABI on the current stream."""
+
+    def __init__(self, cfg, persistent_k=None, persistent_v=None, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.dtype = torch.bfloat16 if cfg.dtype == SR_BF16 else torch.float32
+        self.bytes = sr_kvcache_required_bytes(cfg)
+        self.pool = torch.empty(self.bytes, dtype=torch.uint8, device=device)
+        for t in (persistent_k, persistent_v):
+            if t is not None:
+                self._check_tensor(t, (cfg.num_banks, cfg.persistent_tokens, cfg.num_heads, cfg.head_dim))
+        self.h = sr_kvcache_init(cfg, self.pool, persistent_k, persistent_v, stream)
+
+    def _check_tensor(self, t, shape=None):
+        if t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {self.dtype} device tensor, got {t.dtype} {t.device}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+    def append(self, chunk_id, k, v, stream=None):
+        self._check_tensor(k, (k.shape[0], self.cfg.num_heads, self.cfg.head_dim))
+        self._check_tensor(v, k.shape)
+        sr_kvcache_append_chunk(self.h, chunk_id, k, v, k.shape[0], stream)
+
+    def evict(self):
+        return sr_kvcache_evict(self.h)
+
+    def segments(self, bank=0):
+        return sr_ring_segments(sr_kvcache_ring(self.h), bank)
+
+    def attention(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        import torch
+        self._check_tensor(q, (q.shape[0], self.cfg.num_heads, self.cfg.head_dim))
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_tensor(out, q.shape)
+        if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (self.cfg.num_heads, q.shape[0])):
+            raise ValueError("lse must be float32 [H][n]")
+        sr_chunk_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def gather(self, bank=0, max_tokens=None, stream=None):
+        import torch
+        if max_tokens is None:
+            max_tokens = sum(s[4] for s in self.segments(bank))
+        shape = (max_tokens, self.cfg.num_heads, self.cfg.head_dim)
+        k = torch.empty(shape, dtype=self.dtype, device=self.pool.device)
+        v = torch.empty(shape, dtype=self.dtype, device=self.pool.device)
+        n = sr_kvcache_gather(self.h, bank, k, v, stream)
+        return k[:n], v[:n]
+
+    def close(self):
+        if self.h is not None:
+            sr_kvcache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,145 @@
+// C ABI of the KV cache and the attention call (declared in sr.h).  Host-side validation
+// happens before anything is enqueued; see the conventions at the top of sr.h.
+#include <cmath>
+#include <new>
+
+#include <hip/hip_runtime.h>
+
+#include "core.hpp"
+#include "kernels.hpp"
+
+struct sr_kvcache {
+  sr_ring ring;
+  char* pool = nullptr;
+};
+
+namespace {
+
+sr_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SR_OK;
+  return sr::fail(SR_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Segment table of a call on `bank` (ring must have a current chunk).
+sr::SegTable make_table(const sr_ring& r, int32_t bank, int32_t* total) {
+  sr_segment segs[sr::kMaxSegs];
+  int32_t n = 0;
+  sr_ring_segments(&r, bank, segs, sr::kMaxSegs, &n);
+  sr::SegTable t{};
+  t.n = n;
+  int32_t sum = 0;
+  for (int i = 0; i < n; ++i) {
+    t.s[i] = sr::DevSeg{segs[i].page, segs[i].length};
+    sum += segs[i].length;
+  }
+  if (total) *total = sum;
+  return t;
+}
+
+bool pool_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+sr_status sr_kvcache_init(const sr_kvcache_config* cfg, void* pool, size_t pool_bytes, const void* persistent_k,
+                          const void* persistent_v, void* stream, sr_kvcache** out) {
+  sr::clear_error();
+  if (!out) return sr::fail(SR_E_INVALID, "null output pointer");
+  sr::Layout L;
+  sr_status st = sr::make_layout(cfg, &L);
+  if (st != SR_OK) return st;
+  if (!pool || !pool_aligned(pool)) return sr::fail(SR_E_INVALID, "pool must be non-null and 256-byte aligned");
+  if (pool_bytes < L.bytes)
+    return sr::fail(SR_E_NOMEM, "pool has %zu bytes, the layout needs %zu", pool_bytes, L.bytes);
+  if (L.P > 0 && (!persistent_k || !persistent_v || !sr::aligned16(persistent_k) || !sr::aligned16(persistent_v)))
+    return sr::fail(SR_E_INVALID, "persistent K/V must be non-null and 16-byte aligned when persistent_tokens > 0");
+  sr_kvcache* c = new (std::nothrow) sr_kvcache;
+  if (!c) return sr::fail(SR_E_NOMEM, "host allocation failed");
+  c->ring.L = L;
+  c->pool = static_cast<char*>(pool);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = device_status(sr::launch_zero(pool, L.bytes, s), "pool zero");
+  const size_t bank_elems = size_t(L.P) * L.H * L.D;
+  for (int b = 0; st == SR_OK && b < L.banks && L.P > 0; ++b) {
+    const char* pk = static_cast<const char*>(persistent_k) + b * bank_elems * L.esize;
+    const char* pv = static_cast<const char*>(persistent_v) + b * bank_elems * L.esize;
+    st = device_status(sr::launch_append(L, pool, pk, pv, L.P, L.bank_page(b), L.pages_per_bank, s), "bank copy");
+  }
+  if (st != SR_OK) {
+    delete c;
+    return st;
+  }
+  *out = c;
+  return SR_OK;
+}
+
+sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v, int32_t n_tokens,
+                                  void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
+    return sr::fail(SR_E_INVALID, "chunk K/V must be non-null and 16-byte aligned");
+  int32_t slot;
+  int64_t committed;
+  sr_status st = sr::plan_append(c->ring, chunk_id, n_tokens, &slot, &committed);
+  if (st != SR_OK) return st;
+  const sr::Layout& L = c->ring.L;
+  st = device_status(sr::launch_append(L, c->pool, k, v, n_tokens, L.slot_page(slot), L.pages_per_slot,
+                                       static_cast<hipStream_t>(stream)),
+                     "chunk append");
+  if (st != SR_OK) return st;
+  sr::commit_append(c->ring, chunk_id, n_tokens);
+  return SR_OK;
+}
+
+sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  return sr_ring_evict(&c->ring, evicted_chunk_id);
+}
+
+sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse, float softmax_scale,
+                             void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!q || !out || !sr::aligned16(q) || !sr::aligned16(out))
+    return sr::fail(SR_E_INVALID, "q and out must be non-null and 16-byte aligned");
+  if (q == out) return sr::fail(SR_E_INVALID, "q must not alias out");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return sr::fail(SR_E_INVALID, "lse must be 4-byte aligned");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return sr::fail(SR_E_INVALID, "softmax_scale must be finite and > 0");
+  const sr::Layout& L = c->ring.L;
+  if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
+  const sr::SegTable t = make_table(c->ring, bank, nullptr);
+  return device_status(
+      sr::launch_attention(L, c->pool, t, q, out, lse, softmax_scale, static_cast<hipStream_t>(stream)),
+      "chunk attention");
+}
+
+sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void* v_out, int32_t max_tokens,
+                            int32_t* n_tokens, void* stream) {
+  sr::clear_error();
+  if (!c || !n_tokens) return sr::fail(SR_E_INVALID, "null argument");
+  if (!k_out || !v_out) return sr::fail(SR_E_INVALID, "null output buffers");
+  const sr::Layout& L = c->ring.L;
+  if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk");
+  int32_t total = 0;
+  const sr::SegTable t = make_table(c->ring, bank, &total);
+  if (total > max_tokens) return sr::fail(SR_E_INVALID, "sequence has %d tokens, room for %d", total, max_tokens);
+  *n_tokens = total;
+  return device_status(sr::launch_gather(L, c->pool, t, total, k_out, v_out, static_cast<hipStream_t>(stream)),
+                       "gather");
+}
+
+const sr_ring* sr_kvcache_ring(const sr_kvcache* c) { return c ? &c->ring : nullptr; }
+
+sr_status sr_kvcache_destroy(sr_kvcache* c) {
+  sr::clear_error();
+  delete c;
+  return SR_OK;
+}
+
+}  // extern "C"

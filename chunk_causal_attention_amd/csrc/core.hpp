@@ -1,0 +1,54 @@
+// Host core of the streaming KV cache: argument validation, pool layout, ring state machine.
+// Pure C++ (no HIP calls), so it is exercised on machines without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "sr.h"
+
+namespace sr {
+
+// Pool geometry derived from a validated config (see the pool layout in sr.h).
+struct Layout {
+  int32_t H = 0, D = 0, P = 0, banks = 0, cap = 0, W = 0, cb = 0, dtype = 0, esize = 0;
+  int32_t pages_per_bank = 0, pages_per_slot = 0, total_pages = 0;
+  size_t half_bytes = 0;  // bytes of the K region; the V region follows at this offset
+  size_t bytes = 0;       // whole pool
+
+  int32_t bank_page(int32_t b) const { return b * pages_per_bank; }
+  int32_t slot_page(int32_t s) const { return banks * pages_per_bank + s * pages_per_slot; }
+  int32_t slots() const { return W + 1; }
+};
+
+// Records a thread-local message for sr_last_error() and returns `s`.
+sr_status fail(sr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+sr_status make_layout(const sr_kvcache_config* cfg, Layout* out);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace sr
+
+// Chunk bookkeeping of one cache.  History is a run of consecutive chunk ids ending just
+// before the current id, so ids map to distinct ring slots id mod (W+1).
+struct sr_ring {
+  sr::Layout L;
+  bool has_current = false;
+  int64_t cur_id = -1;
+  int32_t cur_len = 0;
+  int32_t hist_count = 0;
+  int64_t hist_id[SR_MAX_WINDOW];   // oldest first
+  int32_t hist_len[SR_MAX_WINDOW];
+
+  int32_t slot_of(int64_t id) const { return static_cast<int32_t>(id % (L.W + 1)); }
+};
+
+namespace sr {
+// Validates an append without changing the ring.  On success fills the slot written
+// and the id committed (-1 if none).
+sr_status plan_append(const sr_ring& r, int64_t chunk_id, int32_t n_tokens, int32_t* slot, int64_t* committed);
+// Applies a planned append (must follow a successful plan_append with the same arguments).
+void commit_append(sr_ring& r, int64_t chunk_id, int32_t n_tokens);
+}  // namespace sr

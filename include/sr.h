@@ -1,0 +1,183 @@
+/*
+ * sr.h -- streaming chunk-causal attention over a paged KV cache, for AMD MI355X (gfx950).
+ *
+ * What the library computes (StreamRender-H3 project page, "Interactive Coding Worlds
+ * with Real-time Streaming Diffusion Render"):
+ *   - "2.3 A Real-Time Interaction Loop", step 4: the session's conditioning is encoded
+ *     once, then each chunk is generated in a few denoising steps (two in the racing demo)
+ *     conditioned on the session's appearance and on the renderer's own recent output.
+ *   - "3.1.2 Historical Context and Temporal Consistency", prefix cache: every window is a
+ *     fixed prefix (conditioning, reference image, sink) plus a moving part; the moving rows
+ *     attend to the whole window, bidirectionally.
+ *   - "3.3 Inference Acceleration and End-to-End Deployment": the static context's K/V are
+ *     computed once per denoising timestep and each timestep keeps its own bank (static-context
+ *     KV caching); K/V live in persistent per-layer buffers in the layout the attention kernel
+ *     reads, the static part written once and the dynamic region updated in place (persistent
+ *     KV layout); sequence metadata is prepared once, with no host-device synchronisation
+ *     (attention metadata reuse).
+ *   - "3.2 Fast Causal H3 VAE", inference items: a preallocated ring buffer whose slots are
+ *     written in place, never concatenated or repartitioned; empty slots are hidden from the
+ *     kernel rather than masked.
+ *
+ * One attention call: the current chunk's n query tokens attend over
+ *   [ persistent tokens of bank b | history chunks in the window, oldest first | current chunk ]
+ * where current query i sees current key j iff floor(j / causal_block) <= floor(i / causal_block).
+ * With causal_block >= chunk size the whole window is visible (bidirectional).
+ *
+ * Conventions shared by every call
+ *   - Device memory is owned by the caller (e.g. torch tensors).  The library never allocates
+ *     or frees device memory.  Host allocations: the opaque handles only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All device work is
+ *     enqueued on it in call order; no call blocks or synchronises the host.
+ *   - Token-major tensors are contiguous [n][H][D] (the layout a fused qkv projection emits).
+ *     Element type: bf16 (raw 16-bit patterns) for SR_BF16, IEEE fp32 for SR_F32.
+ *   - Device pointers must be 16-byte aligned; the pool 256-byte aligned.
+ *   - Every call validates its arguments on the host before enqueuing anything.  On error it
+ *     returns a status, enqueues nothing and leaves the handle's state unchanged;
+ *     sr_last_error() gives a thread-local message.  A failed kernel launch returns
+ *     SR_E_DEVICE.  Faults inside kernels surface at the caller's next synchronisation.
+ *   - Handles are not thread-safe; distinct handles are independent.
+ */
+#ifndef SR_H
+#define SR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sr_status {
+  SR_OK = 0,
+  SR_E_INVALID = 1,     /* bad argument: null/misaligned pointer, size or index out of range */
+  SR_E_STATE = 2,       /* call not allowed in the current cache state (e.g. window full) */
+  SR_E_NOMEM = 3,       /* pool smaller than sr_kvcache_required_bytes, or host allocation failed */
+  SR_E_DEVICE = 4,      /* HIP runtime error while enqueuing */
+  SR_E_UNSUPPORTED = 5  /* valid request this build does not implement (e.g. head_dim) */
+} sr_status;
+
+typedef enum sr_dtype { SR_BF16 = 0, SR_F32 = 1 } sr_dtype;
+
+/* Tokens per pool page.  Every segment starts on a page boundary. */
+#define SR_PAGE_TOKENS 128
+/* Largest window of history chunks (the segment table is passed to kernels by value). */
+#define SR_MAX_WINDOW 14
+
+typedef struct sr_kvcache_config {
+  int32_t num_heads;         /* H >= 1 (batch folded into heads) */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t persistent_tokens; /* P >= 0: reference-image + prompt (+ sink) tokens per bank */
+  int32_t num_banks;         /* >= 1: one per denoising step */
+  int32_t chunk_capacity;    /* >= 1: most tokens a chunk may have (ring slot size) */
+  int32_t window_chunks;     /* W in [0, SR_MAX_WINDOW]: history chunks kept; the ring has W+1 slots */
+  int32_t causal_block;      /* >= 1: tokens per causal block inside the current chunk */
+  int32_t dtype;             /* sr_dtype */
+} sr_kvcache_config;
+
+/* ------------------------------------------------------------------------------------------
+ * Ring state (host only, no device work).  The chunk bookkeeping of the cache as its own
+ * object, so it can be driven and inspected without a GPU.  sr_kvcache owns one.
+ *
+ * Rules ("3.2 Fast Causal H3 VAE", ring buffer written in place; "2.3 A Real-Time
+ * Interaction Loop", several denoising steps per chunk):
+ *   - the first append may use any chunk_id >= 0;
+ *   - appending the current id again replaces the current chunk (next denoising step);
+ *   - appending current id + 1 commits the current chunk to the history (what was appended
+ *     last stays) and makes the new id current; if the history already holds W chunks this is
+ *     SR_E_STATE ("evict first"); with W == 0 the committed chunk is dropped;
+ *   - any other id is SR_E_INVALID;
+ *   - evict drops the oldest history chunk (SR_E_STATE if there is none);
+ *   - chunk id c lives in ring slot c mod (W+1).
+ * ------------------------------------------------------------------------------------------ */
+typedef struct sr_ring sr_ring;
+
+typedef enum sr_segment_kind { SR_SEG_PERSISTENT = 0, SR_SEG_HISTORY = 1, SR_SEG_CURRENT = 2 } sr_segment_kind;
+
+typedef struct sr_segment {
+  int64_t chunk_id; /* -1 for the persistent bank */
+  int32_t kind;     /* sr_segment_kind */
+  int32_t slot;     /* ring slot, or the bank index for the persistent segment */
+  int32_t page;     /* first pool page of the segment */
+  int32_t length;   /* valid tokens */
+} sr_segment;
+
+/* Validates `cfg` and creates an empty ring.  *out is set on success only. */
+sr_status sr_ring_create(const sr_kvcache_config* cfg, sr_ring** out);
+/* Applies one append.  On success *slot is the ring slot written and *committed_id the
+ * chunk committed to the history by this call, or -1 (either pointer may be NULL).
+ * SR_E_INVALID also for n_tokens outside [1, chunk_capacity]. */
+sr_status sr_ring_append(sr_ring* r, int64_t chunk_id, int32_t n_tokens, int32_t* slot, int64_t* committed_id);
+/* Drops the oldest history chunk; *evicted_id (nullable) receives its id. */
+sr_status sr_ring_evict(sr_ring* r, int64_t* evicted_id);
+/* Logical key segments of an attention call on `bank`, in visiting order:
+ * persistent bank (omitted when P == 0), history oldest first, current.  Writes at most
+ * `max` entries to `out` and the count to *n.  SR_E_STATE if there is no current chunk,
+ * SR_E_INVALID if `max` is too small or `bank` out of range. */
+sr_status sr_ring_segments(const sr_ring* r, int32_t bank, sr_segment* out, int32_t max, int32_t* n);
+sr_status sr_ring_destroy(sr_ring* r);
+
+/* ------------------------------------------------------------------------------------------
+ * KV cache (one handle per attention layer).
+ *
+ * Pool layout in HBM, for each head h, page p (128 tokens), token t, feature d:
+ *   K: pool[((h * total_pages + p) * 128 + t) * D + d]                    (key rows)
+ *   V: pool[V_off + ((h * total_pages + p) * D + d) * 128 + t]            (value columns)
+ * i.e. K pages are token-major and V pages are stored transposed, which is the operand
+ * order the attention kernel's matrix instructions read.  Pages are numbered: banks first
+ * (ceil(P/128) pages each), then the W+1 ring slots (ceil(capacity/128) pages each).
+ * Tokens past a segment's valid length are kept at zero.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct sr_kvcache sr_kvcache;
+
+/* Bytes the pool must have for `cfg`. */
+sr_status sr_kvcache_required_bytes(const sr_kvcache_config* cfg, size_t* bytes);
+
+/* Creates a cache on `pool` (device, caller-owned, >= required bytes, kept alive until
+ * destroy and until its queued work is done).  Enqueues: zero the pool, then copy the
+ * persistent banks persistent_k / persistent_v (device, [num_banks][P][H][D], may be NULL
+ * when P == 0) into their pages.  The caller may reuse those buffers once the stream has
+ * passed this call. */
+sr_status sr_kvcache_init(const sr_kvcache_config* cfg, void* pool, size_t pool_bytes,
+                          const void* persistent_k, const void* persistent_v, void* stream,
+                          sr_kvcache** out);
+
+/* Appends one chunk's K/V (device, [n_tokens][H][D]) under the ring rules above and
+ * enqueues the copy into slot chunk_id mod (W+1), zeroing the slot past n_tokens.
+ * ("3.3 Inference Acceleration", persistent KV layout: only the dynamic region is written.) */
+sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v,
+                                  int32_t n_tokens, void* stream);
+
+/* Drops the oldest history chunk (host metadata only; nothing is enqueued). */
+sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
+
+/* Attention of the current chunk's queries q (device, [n][H][D], n = current chunk length)
+ * over bank `bank` + history + current (see top of file).  out: device [n][H][D] in the
+ * cache dtype.  lse: device fp32 [H][n] natural-log log-sum-exp of the scaled logits, or
+ * NULL.  softmax_scale > 0 multiplies q.k (usually 1/sqrt(D)).  SR_E_STATE without a
+ * current chunk.  q must not alias out. */
+sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
+                             float softmax_scale, void* stream);
+
+/* Copies the logical key/value sequence of a call on `bank` (persistent, history oldest
+ * first, current) into k_out / v_out (device, [max_tokens][H][D]), bit-exact.  *n_tokens
+ * receives the length; SR_E_INVALID if it exceeds max_tokens (nothing enqueued).  For tests
+ * and debugging. */
+sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void* v_out,
+                            int32_t max_tokens, int32_t* n_tokens, void* stream);
+
+/* The handle's ring state, for inspection (owned by the cache). */
+const sr_ring* sr_kvcache_ring(const sr_kvcache* c);
+
+/* Frees the host handle only (the pool stays the caller's). */
+sr_status sr_kvcache_destroy(sr_kvcache* c);
+
+const char* sr_status_string(sr_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* sr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SR_H */

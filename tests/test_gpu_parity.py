@@ -1,0 +1,241 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Element-by-element on reduced workloads that span several query and key tiles with ragged
+tails; on sampled rows (and all-finite checks) at the full workload sizes, with the same
+launch configuration the benchmark times.  Gates: tests/gates.py.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gates
+import harness
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sr():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return harness.lib_module()
+
+
+def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on_step=None):
+    """Streams workload `w` through the library and the oracle model; returns per-step stats."""
+    import torch
+    scale = 1.0 / np.sqrt(w.head_dim)
+    stream = synth.SessionStream(w)
+    pk, pv = stream.persistent()
+    cache = sr.KVCache(harness.cfg_of(sr, w), harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype))
+    model = oracle.StreamingCache(pk, pv, w.window)
+    stats = []
+    for idx, ev in enumerate(stream):
+        cid = ev["chunk"] + phase
+        if ev["evict_before"]:
+            assert cache.evict() == model.evict()
+        cache.append(cid, harness.to_dev(ev["k"], w.dtype), harness.to_dev(ev["v"], w.dtype))
+        model.append(cid, ev["k"], ev["v"])
+        if w.single_step and ev["chunk"] != w.chunks - 1:
+            continue
+        q = harness.to_dev(ev["q"], w.dtype)
+        lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device="cuda")
+        out = cache.attention(ev["bank"], q, lse=lse, softmax_scale=scale)
+        if check_gather:
+            for b in range(w.banks):
+                kg, vg = cache.gather(b)
+                km, vm, _ = model.sequence(b)
+                assert (harness.to_host(kg, w.dtype) == km).all() and (harness.to_host(vg, w.dtype) == vm).all(), \
+                    (w.name, phase, idx, b)
+        out_h = harness.to_host(out, w.dtype)
+        lse_h = lse.cpu().numpy()
+        if on_step:
+            on_step(idx, ev, out_h, lse_h)
+        if idx % oracle_every and not (w.single_step):
+            continue
+        r = np.arange(w.chunk) if rows is None else rows
+        o_ref, l_ref = oracle.chunk_attention(model, ev["bank"], ev["q"], scale, w.causal_block, w.dtype, rows=r)
+        o_dev = harness.widen_host(out_h[r], w.dtype)
+        st = gates.error_stats(o_dev, o_ref)
+        st_l = gates.error_stats(lse_h[:, r], l_ref)
+        assert np.isfinite(harness.widen_host(out_h, w.dtype)).all()
+        stats.append((idx, st, st_l))
+    cache.close()
+    return stats
+
+
+def check_stats(w, stats):
+    g = gates.gates_for(w.dtype)
+    lse_tol = 2e-2 if w.dtype == "bf16" else 1e-4
+    for idx, st, st_l in stats:
+        assert gates.passes(st, g), (w.name, idx, st)
+        assert st_l["max_abs"] <= lse_tol, (w.name, idx, st_l)
+
+
+@pytest.mark.parametrize("name", ["c0", "t_f32", "t_stream", "t_d64", "t_frame"])
+def test_parity_every_element(sr, name):
+    w = synth.get_workload(name)
+    say(f"[parity] {name}: H={w.heads} D={w.head_dim} P={w.persistent} chunk={w.chunk} W={w.window}")
+    stats = run_stream(sr, w, check_gather=True)
+    assert stats
+    check_stats(w, stats)
+    say(f"[parity] {name}: worst", max(s[1]["max_abs"] for s in stats), max(s[1]["rel_fro"] for s in stats))
+
+
+@pytest.mark.parametrize("name", ["c0", "t_stream"])
+def test_ring_phase_bit_identical(sr, name):
+    """Same stream started at chunk id 0, 100 and 1000: same bits (slots differ)."""
+    w = synth.get_workload(name)
+    outs = {}
+    for phase in (0, 100, 1000):
+        say(f"[phase] {name} phase {phase}")
+        got = []
+        run_stream(sr, w, phase=phase, rows=np.arange(2), check_gather=(phase != 0),
+                   on_step=lambda i, ev, o, l: got.append((o.copy(), l.copy())))
+        outs[phase] = got
+    for phase in (100, 1000):
+        for (a, la), (b, lb) in zip(outs[0], outs[phase]):
+            assert (a == b).all() and (la == lb).all()
+
+
+FULL = ["c1", "c3", "c4", "c1s", "c4s"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size_sampled(sr, name):
+    w = synth.get_workload(name)
+    rows = harness.sample_rows(w.chunk, block=w.causal_block if w.causal_block < w.chunk else None)
+    say(f"[full] {name}: {len(rows)} sampled rows x {w.heads} heads, {w.visible_keys} keys")
+    stats = run_stream(sr, w, rows=rows)
+    check_stats(w, stats)
+    say(f"[full] {name}:", stats[-1][1], "lse", stats[-1][2]["max_abs"])
+
+
+def test_session_c2_sampled(sr):
+    """32 chunks x 2 steps with per-step banks and evictions; sampled rows of every step."""
+    w = synth.get_workload("c2")
+    rows = harness.sample_rows(w.chunk, stride=211)
+    say(f"[c2] 64 chunk-steps, {len(rows)} rows each")
+    stats = run_stream(sr, w, rows=rows, check_gather=False)
+    assert len(stats) == 64
+    check_stats(w, stats)
+    errs = [s[1]["rel_fro"] for s in stats]
+    say("[c2] rel_fro first/last/max", errs[0], errs[-1], max(errs))
+    # no drift with the chunk index: the last steps are no worse than twice the first steps
+    assert np.mean(errs[-8:]) <= 2 * np.mean(errs[:8]) + 1e-4
+
+
+def _one_chunk_cache(sr, H, D, P, n, W, cb, dtype, seed, cap=None):
+    import torch
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cfg = sr.config_for(H, D, P, cap or n, W, cb, 1, sr.SR_BF16 if dtype == "bf16" else sr.SR_F32)
+    mk = lambda *s: torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(tdt).cuda()
+    pk, pv = (mk(1, P, H, D), mk(1, P, H, D)) if P else (None, None)
+    cache = sr.KVCache(cfg, pk, pv)
+    return cache, mk, pk, pv
+
+
+def test_single_visible_key_is_exact(sr):
+    """With causal blocks of one token, no prefix and no history, query 0 sees only key 0:
+    its output is V[0] bit for bit, and its lse is its own scaled logit."""
+    import torch
+    for dtype in ("bf16", "f32"):
+        cache, mk, _, _ = _one_chunk_cache(sr, 3, 128, 0, 70, 0, 1, dtype, 1)
+        k, v, q = mk(70, 3, 128), mk(70, 3, 128), mk(70, 3, 128)
+        cache.append(5, k, v)
+        lse = torch.empty((3, 70), dtype=torch.float32, device="cuda")
+        out = cache.attention(0, q, lse=lse, softmax_scale=0.1)
+        assert torch.equal(out[0], v[0]), dtype
+        s0 = (q[0].float() * k[0].float()).sum(-1) * 0.1
+        assert torch.allclose(lse[:, 0], s0, atol=1e-5, rtol=1e-5)
+        cache.close()
+
+
+def test_equal_scores_give_mean(sr):
+    import torch
+    cache, mk, pk, pv = _one_chunk_cache(sr, 2, 128, 100, 300, 1, 300, "bf16", 2)
+    k, v = mk(300, 2, 128), mk(300, 2, 128)
+    cache.append(0, k, v)
+    q = torch.zeros((300, 2, 128), dtype=torch.bfloat16, device="cuda")
+    out = cache.attention(0, q).float()
+    mean = torch.cat([pv[0], v]).float().mean(0)
+    assert (out - mean[None]).abs().max().item() <= 4e-3  # one bf16 rounding of a value < 0.3
+    cache.close()
+
+
+def test_hidden_data_does_not_matter(sr):
+    """Bits of the output do not change when data the kernel must not read changes:
+    an evicted chunk's slot, the zero tail of a short chunk, later causal blocks."""
+    import torch
+    H, D, P, cap, W = 2, 128, 150, 400, 2
+    cache, mk, _, _ = _one_chunk_cache(sr, H, D, P, 0, W, 130, "bf16", 3, cap=cap)
+    n = 333                                    # short current chunk: the tail of its slot is padding
+    cache.append(0, mk(cap, H, D), mk(cap, H, D))
+    cache.append(1, mk(cap, H, D), mk(cap, H, D))
+    k2, v2 = mk(n, H, D), mk(n, H, D)
+    cache.append(2, k2, v2)
+    assert cache.evict() == 0                  # chunk 0's slot (slot 0) is now free
+    q = mk(n, H, D)
+    ref = cache.attention(0, q).clone()
+    pool = cache.pool.view(torch.bfloat16)
+    half = pool.numel() // 2
+    total_pages = cache.bytes // (2 * H * 128 * D * 2)
+    ppb, pps = -(-P // 128), -(-cap // 128)
+    slot_page = lambda s: ppb + s * pps
+    segs = cache.segments(0)
+    assert [sg[0] for sg in segs] == [-1, 1, 2] and segs[-1][3] == slot_page(2)
+    # 1) garbage in the evicted chunk's slot (K rows and V^T pages of every head)
+    for h in range(H):
+        for part in (0, half):
+            p0 = part + (h * total_pages + slot_page(0)) * 128 * D
+            pool[p0:p0 + pps * 128 * D] = 3.0
+    torch.cuda.synchronize()
+    assert torch.equal(cache.attention(0, q), ref)
+    # 2) finite garbage in the padding past the current chunk's 333 tokens
+    for h in range(H):
+        kp = (h * total_pages + slot_page(2) + n // 128) * 128 * D
+        pool[kp + (n % 128) * D: kp + 128 * D] = -5.0
+        vp = half + (h * total_pages + slot_page(2) + n // 128) * 128 * D
+        pool[vp:vp + 128 * D].view(D, 128)[:, n % 128:] = 7.0
+    torch.cuda.synchronize()
+    assert torch.equal(cache.attention(0, q), ref)
+    # 3) later causal blocks: change keys/values of blocks >= 2 (tokens 260..332)
+    k3, v3 = k2.clone(), v2.clone()
+    k3[260:] = 2.0
+    v3[260:] = -1.0
+    cache.append(2, k3, v3)
+    out3 = cache.attention(0, q)
+    assert torch.equal(out3[:260], ref[:260]) and not torch.equal(out3[260:], ref[260:])
+    cache.close()
+
+
+def test_state_errors_on_device_cache(sr):
+    """Rejected calls enqueue nothing and leave the cache usable and unchanged."""
+    import torch
+    w = synth.get_workload("t_stream")
+    cache, mk, _, _ = _one_chunk_cache(sr, 2, 128, 64, 128, 1, 128, "bf16", 4)
+    k, v, q = mk(128, 2, 128), mk(128, 2, 128), mk(128, 2, 128)
+    with pytest.raises(sr.SrError) as e:
+        cache.attention(0, q)
+    assert e.value.status == 2
+    cache.append(0, k, v)
+    cache.append(1, k, v)
+    before = cache.attention(0, q).clone()
+    for args, st in [((2, k, v), 2), ((5, k, v), 1)]:
+        with pytest.raises(sr.SrError) as e:
+            cache.append(*args)
+        assert e.value.status == st
+    with pytest.raises(sr.SrError) as e:
+        cache.attention(1, q)
+    assert e.value.status == 1
+    assert torch.equal(cache.attention(0, q), before)
+    cache.close()

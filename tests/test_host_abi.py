@@ -1,0 +1,185 @@
+"""The C ABI on the host (no GPU): exports, ring state machine, layout, validation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import harness
+import oracle
+
+HEADER = os.path.join(harness.ROOT, "include", "sr.h")
+
+
+@pytest.fixture(scope="module")
+def sr():
+    return harness.lib_module()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sr_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(sr):
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = sr.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(sr):
+    assert sr.sr_status_string(0) == "SR_OK"
+    assert sr.sr_status_string(2) == "SR_E_STATE"
+
+
+def _layout_pages(cfg):
+    ppb = -(-cfg.persistent_tokens // 128)
+    pps = -(-cfg.chunk_capacity // 128)
+    return ppb, pps, cfg.num_banks * ppb + (cfg.window_chunks + 1) * pps
+
+
+@pytest.mark.parametrize("H,D,P,banks,cap,W,dt", [(2, 64, 16, 1, 32, 2, 1), (24, 128, 2072, 1, 4680, 2, 0),
+                                                  (40, 128, 4112, 2, 7200, 3, 0), (3, 128, 0, 1, 1, 0, 0)])
+def test_required_bytes(sr, H, D, P, banks, cap, W, dt):
+    cfg = sr.config_for(H, D, P, cap, W, None, banks, dt)
+    _, _, pages = _layout_pages(cfg)
+    assert sr.sr_kvcache_required_bytes(cfg) == 2 * H * pages * 128 * D * (2 if dt == 0 else 4)
+
+
+@pytest.mark.parametrize("field,value,status", [("head_dim", 96, 5), ("head_dim", 0, 5), ("window_chunks", 15, 1),
+                                                ("window_chunks", -1, 1), ("num_banks", 0, 1), ("num_heads", 0, 1),
+                                                ("chunk_capacity", 0, 1), ("causal_block", 0, 1), ("dtype", 7, 1),
+                                                ("persistent_tokens", -3, 1)])
+def test_config_validation(sr, field, value, status):
+    cfg = sr.config_for(4, 128, 100, 300, 2)
+    setattr(cfg, field, value)
+    with pytest.raises(sr.SrError) as e:
+        sr.sr_ring_create(cfg)
+    assert e.value.status == status
+    assert sr.sr_last_error() != ""
+
+
+def test_init_validation_before_device_work(sr):
+    """Bad arguments to sr_kvcache_init fail on the host, without touching a device."""
+    lib = sr.load()
+    cfg = sr.config_for(2, 64, 16, 32, 2, None, 1, sr.SR_F32)
+    need = sr.sr_kvcache_required_bytes(cfg)
+    h = ctypes.c_void_p()
+    P = ctypes.c_void_p
+    cases = [
+        (None, need, P(4096), P(4096), 1),          # null pool
+        (P(4096 + 16), need, P(4096), P(4096), 1),  # pool not 256-byte aligned
+        (P(4096), need - 1, P(4096), P(4096), 3),   # pool too small
+        (P(4096), need, None, P(4096), 1),          # persistent K missing with P > 0
+        (P(4096), need, P(4100), P(4096), 1),       # persistent K misaligned
+    ]
+    for pool, nbytes, pk, pv, want in cases:
+        st = lib.sr_kvcache_init(ctypes.byref(cfg), pool, nbytes, pk, pv, None, ctypes.byref(h))
+        assert st == want, (pool, nbytes, pk, pv, st, sr.sr_last_error())
+        assert not h.value
+    assert lib.sr_chunk_attention(None, 0, P(4096), P(8192), None, 0.1, None) == 1
+    assert lib.sr_kvcache_append_chunk(None, 0, P(4096), P(4096), 1, None) == 1
+    assert lib.sr_kvcache_evict(None, None) == 1
+    assert lib.sr_kvcache_destroy(None) == 0
+
+
+def _ring_vs_model(sr, W, P, banks, cap, seed, n_ops=600):
+    r = np.random.default_rng(seed)
+    cfg = sr.config_for(1, 64, P, cap, W, None, banks, sr.SR_F32)
+    ppb, pps, _ = _layout_pages(cfg)
+    ring = sr.sr_ring_create(cfg)
+    z = np.zeros((1, 1, 1), np.float32)
+    pk = np.zeros((banks, P, 1, 1), np.float32)
+    model = oracle.StreamingCache(pk, pk, W, capacity=cap)
+    lens = {}
+    cur = None
+    try:
+        for _ in range(n_ops):
+            op = r.integers(0, 5)
+            if op == 0:
+                try:
+                    e_model = model.evict()
+                except oracle.CacheStateError:
+                    e_model = None
+                try:
+                    e_ring = sr.sr_ring_evict(ring)
+                except sr.SrError as ex:
+                    assert ex.status == 2
+                    e_ring = None
+                assert e_model == e_ring
+            else:
+                if cur is None:
+                    cid = int(r.integers(0, 2000))
+                else:
+                    cid = cur + {1: 0, 2: 1, 3: 1, 4: int(r.integers(-2, 3))}[int(op)]
+                n = int(r.integers(0, cap + 2)) if r.random() < 0.1 else int(r.integers(1, cap + 1))
+                try:
+                    model.append(cid, np.zeros((n, 1, 1), np.float32) if n > 0 else z[:0], z[:0] if n == 0 else
+                                 np.zeros((n, 1, 1), np.float32))
+                    m_ok = True
+                except oracle.CacheStateError:
+                    m_ok = False
+                try:
+                    slot, com = sr.sr_ring_append(ring, cid, n)
+                    r_ok = True
+                    assert slot == cid % (W + 1)
+                except sr.SrError as ex:
+                    r_ok = False
+                    assert ex.status in (1, 2)
+                assert m_ok == r_ok, (cid, n, cur, model.visible_ids())
+                if r_ok:
+                    cur = cid
+                    lens[cid] = n
+            ids = model.visible_ids()
+            if ids:
+                for b in range(banks):
+                    segs = sr.sr_ring_segments(ring, b)
+                    expect = ([(-1, 0, b, b * ppb, P)] if P else []) + \
+                             [(i, 1, i % (W + 1), banks * ppb + (i % (W + 1)) * pps, lens[i]) for i in ids[:-1]] + \
+                             [(ids[-1], 2, ids[-1] % (W + 1), banks * ppb + (ids[-1] % (W + 1)) * pps, lens[ids[-1]])]
+                    assert segs == expect
+    finally:
+        sr.sr_ring_destroy(ring)
+
+
+@pytest.mark.parametrize("W,P,banks,cap", [(0, 5, 1, 3), (1, 0, 1, 130), (2, 300, 2, 200), (3, 16, 3, 7),
+                                           (14, 1, 1, 1)])
+def test_ring_matches_oracle_model(sr, W, P, banks, cap):
+    _ring_vs_model(sr, W, P, banks, cap, seed=W * 100 + cap)
+
+
+def test_ring_errors_leave_state(sr):
+    cfg = sr.config_for(1, 128, 10, 50, 2)
+    ring = sr.sr_ring_create(cfg)
+    with pytest.raises(sr.SrError) as e:
+        sr.sr_ring_segments(ring, 0)
+    assert e.value.status == 2                       # no current chunk yet
+    sr.sr_ring_append(ring, 100, 50)
+    sr.sr_ring_append(ring, 101, 20)
+    sr.sr_ring_append(ring, 102, 30)
+    before = sr.sr_ring_segments(ring, 0)
+    for cid, n, st in [(103, 10, 2), (105, 10, 1), (99, 10, 1), (102, 51, 1), (102, 0, 1), (-1, 1, 1)]:
+        with pytest.raises(sr.SrError) as e:
+            sr.sr_ring_append(ring, cid, n)
+        assert e.value.status == st
+        assert sr.sr_ring_segments(ring, 0) == before
+    with pytest.raises(sr.SrError):
+        sr.sr_ring_segments(ring, 1)                 # bank out of range
+    assert sr.sr_ring_evict(ring) == 100
+    sr.sr_ring_append(ring, 103, 10)
+    assert [s[0] for s in sr.sr_ring_segments(ring, 0)] == [-1, 101, 102, 103]
+    sr.sr_ring_destroy(ring)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libsr.so the binding raises instead of falling back to anything else."""
+    import subprocess
+    import sys
+    code = ("import chunk_causal_attention_amd as m; m.LIB_PATH = %r\n"
+            "try:\n    m.load()\nexcept ImportError as e:\n    print('raised', e)\n" % str(tmp_path / "nope.so"))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=harness.ROOT)
+    assert "raised" in out.stdout, out.stderr
