@@ -1,0 +1,218 @@
+"""Benchmark of the streaming chunk-attention hot path on one MI355X.
+
+One step = one streaming chunk-step of one attention layer at full window: evict the
+oldest history chunk, append the next chunk's K/V into its ring slot, run chunk attention
+of its queries over bank + history + current (StreamRender-H3 project page, "2.3 A
+Real-Time Interaction Loop", step 4, and "3.3 Inference Acceleration and End-to-End
+Deployment").  Steps cycle over several independent layer caches, the way a DiT forward
+visits its layers, so each step finds its cache cold in the 256 MB last-level cache
+(the 832x480 workload's K/V are ~200 MB per layer); `--layers 1` gives the warm number.
+
+Prints one JSON line (see --help).  Inputs are seeded synthetic tensors resident in HBM
+before the timed region; timing brackets exactly --steps steps with device syncs, and HIP
+events around each attention launch give the kernel's average duration for the roofline.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload c1] [--layers 4]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def attention_flops(w):
+    """Algorithmic flops of one call: 4 * H * D * sum_i |S(i)| (visible pairs only)."""
+    n, cb = w.chunk, w.causal_block
+    fixed = w.persistent + w.window * w.chunk
+    i = np.arange(n)
+    vis = fixed + np.minimum(n, (i // cb + 1) * cb)
+    return 4.0 * w.heads * w.head_dim * float(vis.sum())
+
+
+def append_bytes(w):
+    """Algorithmic bytes of one append: read K,V [n][H][D] + write them (and the slot's zero tail)."""
+    es = 2 if w.dtype == "bf16" else 4
+    slot_tokens = math.ceil(w.chunk / 128) * 128
+    return es * w.heads * w.head_dim * 2 * (w.chunk + slot_tokens)
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on whole heads of the workload's last chunk-step."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    pk, pv, hist, cur = synth.single_step_inputs(w)
+    m = oracle.StreamingCache(pk, pv, w.window)
+    for i, (k, v) in enumerate(hist):
+        m.append(i, k, v)
+    m.append(len(hist), cur[0], cur[1])
+    scale = 1.0 / math.sqrt(w.head_dim)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        oracle.chunk_attention(m, 0, cur[2], scale, w.causal_block, w.dtype, heads=[heads])
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = attention_flops(w) * heads / w.heads
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads x all {w.chunk} query rows of {w.name} "
+                      f"({w.visible_keys} keys), fp64 numpy oracle, {dt:.1f} s wall"}
+
+
+def make_inputs(sr, w, n_sets, torch):
+    """Device-resident chunk inputs (K, V, Q) and the persistent bank, from the seeded generator."""
+    import synth
+    from synth.torch_io import to_dev
+    stream = synth.SessionStream(w)
+    pk, pv = stream.persistent()
+    sets = []
+    for ev in stream:
+        sets.append(tuple(to_dev(ev[x], w.dtype) for x in ("k", "v", "q")))
+        if len(sets) == n_sets:
+            break
+    return to_dev(pk, w.dtype), to_dev(pv, w.dtype), sets
+
+
+def run(args):
+    import torch
+    import synth
+    import chunk_causal_attention_amd as sr
+
+    sr.load()
+    w = synth.get_workload(args.workload)
+    if not w.single_step:
+        raise SystemExit(f"workload {w.name} is a parity case, not a bench workload")
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    pk, pv, sets = make_inputs(sr, w, w.window + 2, torch)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
+                        sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
+
+    t_init = time.perf_counter()
+    layers = []
+    for _ in range(args.layers):
+        c = sr.KVCache(cfg, pk, pv)
+        for j in range(w.window + 1):
+            k, v, _ = sets[j % len(sets)]
+            c.append(j, k, v)
+        layers.append({"cache": c, "next": w.window + 1})
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t_init
+    out = torch.empty((w.chunk, w.heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
+    lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device=dev)
+
+    ev_pairs = []
+
+    def step(i, timed):
+        L = layers[i % len(layers)]
+        c = L["cache"]
+        cid = L["next"]
+        L["next"] += 1
+        if w.window > 0:
+            c.evict()
+        k, v, q = sets[cid % len(sets)]
+        if timed:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            c.append(cid, k, v)
+            e1.record()
+            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+            e2.record()
+            ev_pairs.append((e0, e1, e2))
+        else:
+            c.append(cid, k, v)
+            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_append = np.array([a.elapsed_time(b) for a, b, _ in ev_pairs])
+    t_attn = np.array([b.elapsed_time(c) for _, b, c in ev_pairs])
+    ms_step = elapsed * 1e3 / args.steps
+    F = attention_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
+    traffic = None
+    if args.traffic_kib is not None:
+        traffic = args.traffic_kib * 1024.0
+    res = {
+        "metric": "ms per chunk-step & attention TFLOP/s (frac of bf16 MFMA peak), 1 MI355X",
+        "value": round(F / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: chunk-step, {w.heads} heads x {w.head_dim}, {w.persistent} persistent + "
+                        f"{w.window}x{w.chunk} history + {w.chunk} current tokens, causal block {w.causal_block}",
+            "heads": w.heads, "head_dim": w.head_dim, "queries": w.chunk, "keys_visible": w.visible_keys,
+            "layers_cycled": args.layers, "step": "evict + append_chunk + chunk_attention",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "ms_attention": round(float(t_attn.mean()), 4),
+        "ms_attention_p10_p50_p90": [round(float(np.percentile(t_attn, p)), 4) for p in (10, 50, 90)],
+        "ms_append": round(float(t_append.mean()), 4),
+        "append_GBps": round(append_bytes(w) / (t_append.mean() * 1e-3) / 1e9, 1),
+        "attention_gflop_per_call": round(F / 1e9, 3),
+        "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
+    }
+    for L in layers:
+        L["cache"].close()
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="c1", help="c1 (default), c3, c4, c1s, c4s or c2")
+    ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (whole heads)")
+    ap.add_argument("--traffic-kib", type=float, default=None,
+                    help="HBM KiB per attention launch from the rocprofv3 FETCH/WRITE runs (scaled)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        raise SystemExit(2)
+    res = run(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,19 +23,7 @@ def cfg_of(sr, w):
                          sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
 
 
-def to_dev(arr, dtype):
-    import torch
-    a = np.ascontiguousarray(arr)
-    if dtype == "bf16":
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(a).cuda()
-
-
-def to_host(t, dtype):
-    import torch
-    if dtype == "bf16":
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.float().cpu().numpy()
+from synth.torch_io import to_dev, to_host  # noqa: E402,F401
 
 
 def widen_host(arr, dtype):
