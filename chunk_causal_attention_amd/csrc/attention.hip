@@ -36,6 +36,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byte piece
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -91,6 +92,8 @@ struct Mma<float> {
   __device__ static void store4(float* dst, f32x4_t v) { *reinterpret_cast<f32x4_t*>(dst) = v; }
 };
 
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 struct AttnArgs {
   const void* q;
   void* o;
@@ -103,8 +106,60 @@ struct AttnArgs {
   SegTable t;
 };
 
+// Registers holding one K/V tile between its global loads and its LDS stores.
+template <int KCH, int VCH>
+struct Stage {
+  u32x4_t k[KCH];
+  u32x4_t v[VCH];
+};
+
+// Issues the global loads of key tile (segment s, first key k0): BN key rows of K (contiguous
+// in the page) and the BN-key slice of each of the D rows of the transposed V page.
+template <typename T, int D, int BN, int NT, int KCH, int VCH>
+__device__ __forceinline__ void load_tile(Stage<KCH, VCH>& st, const AttnArgs& a, size_t head_page, int s, int k0,
+                                          int tid) {
+  constexpr int ES = int(sizeof(T));
+  constexpr int KPR = D * ES / 16;
+  constexpr int VPR = BN * ES / 16;
+  const size_t page = head_page + a.t.s[s].page + k0 / SR_PAGE_TOKENS;
+  const char* kb = a.kpool + (page * SR_PAGE_TOKENS + k0 % SR_PAGE_TOKENS) * (D * ES);
+  const char* vb = a.vpool + page * (D * SR_PAGE_TOKENS * ES) + (k0 % SR_PAGE_TOKENS) * ES;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int ci = j * NT + tid;
+    st.k[j] = *reinterpret_cast<const u32x4_t*>(kb + (ci / KPR) * (D * ES) + (ci % KPR) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int ci = j * NT + tid;
+    st.v[j] = *reinterpret_cast<const u32x4_t*>(vb + (ci / VPR) * (SR_PAGE_TOKENS * ES) + (ci % VPR) * 16);
+  }
+}
+
+// Writes a staged tile into one LDS stage: K rows at their permuted positions (see
+// Mma::row_of_key), V^T rows as they are.
+template <typename M, int D, int BN, int NT, int KCH, int VCH, int KPITCH, int VPITCH>
+__device__ __forceinline__ void store_tile(const Stage<KCH, VCH>& st, char* stage, int tid) {
+  constexpr int ES = int(sizeof(typename M::Op)) / M::EPL;
+  constexpr int KPR = D * ES / 16;
+  constexpr int VPR = BN * ES / 16;
+  char* sv = stage + BN * KPITCH;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int ci = j * NT + tid;
+    const int r = ci / KPR;
+    const int lr = (r & ~31) | M::row_of_key(r & 31);
+    *reinterpret_cast<u32x4_t*>(stage + lr * KPITCH + (ci % KPR) * 16) = st.k[j];
+  }
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) {
+    const int ci = j * NT + tid;
+    *reinterpret_cast<u32x4_t*>(sv + (ci / VPR) * VPITCH + (ci % VPR) * 16) = st.v[j];
+  }
+}
+
 template <typename T, int D, int QB, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, NW / 4) void chunk_attention_kernel(const AttnArgs a) {
   using M = Mma<T>;
   using Op = typename M::Op;
   constexpr int ES = int(sizeof(T));
@@ -136,8 +191,10 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   const int G = a.num_wg, bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3, per = G >> 3, rem = G & 7;
   const int wg = local + xcd * per + (xcd < rem ? xcd : rem);
-  const int h = wg / a.q_tiles;
-  const int q0 = (wg - h * a.q_tiles) * BM;
+  // Integer divisions are expanded on the vector ALU; readfirstlane tells the compiler the
+  // results are wave-uniform so the tile loop stays a scalar loop.
+  const int h = uniform(wg / a.q_tiles);
+  const int q0 = uniform((wg - h * a.q_tiles) * BM);
   const int n_q = a.n_q, H = a.H, cb = a.causal_block;
   const int cur = a.t.n - 1;
   const int cur_len = a.t.s[cur].len;
@@ -161,10 +218,11 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
 
   // Keys of the current chunk visible to every / to some query of this workgroup.
   const int qlast = min(q0 + BM, n_q) - 1;
-  const int cur_all = min(cur_len, (q0 / cb + 1) * cb);
-  const int cur_any = min(cur_len, (qlast / cb + 1) * cb);
+  const int cur_all = uniform(min(cur_len, (q0 / cb + 1) * cb));
+  const int cur_any = uniform(min(cur_len, (qlast / cb + 1) * cb));
   int ntiles = (cur_any + BN - 1) / BN;
   for (int s = 0; s < cur; ++s) ntiles += (a.t.s[s].len + BN - 1) / BN;
+  ntiles = uniform(ntiles);
 
   float m_run[QB], l_run[QB];
   f32x16_t acc[QB][NDB];
@@ -177,38 +235,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   }
 
   const size_t head_page = size_t(h) * a.total_pages;
-  uint4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int s, int k0) {
-    const size_t page = head_page + a.t.s[s].page + k0 / SR_PAGE_TOKENS;
-    const char* kb = a.kpool + (page * SR_PAGE_TOKENS + k0 % SR_PAGE_TOKENS) * (D * ES);
-    const char* vb = a.vpool + page * (D * SR_PAGE_TOKENS * ES) + (k0 % SR_PAGE_TOKENS) * ES;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = j * NT + tid;
-      kreg[j] = *reinterpret_cast<const uint4*>(kb + (ci / KPR) * (D * ES) + (ci % KPR) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int ci = j * NT + tid;
-      vreg[j] = *reinterpret_cast<const uint4*>(vb + (ci / VPR) * (SR_PAGE_TOKENS * ES) + (ci % VPR) * 16);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* sk = smem + buf * STAGE;
-    char* sv = sk + KTILE;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = j * NT + tid;
-      const int r = ci / KPR;
-      const int lr = (r & ~31) | M::row_of_key(r & 31);
-      *reinterpret_cast<uint4*>(sk + lr * KPITCH + (ci % KPR) * 16) = kreg[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int ci = j * NT + tid;
-      *reinterpret_cast<uint4*>(sv + (ci / VPR) * VPITCH + (ci % VPR) * 16) = vreg[j];
-    }
-  };
+  Stage<KCH, VCH> stg;
   auto seg_end = [&](int s) { return s == cur ? cur_any : a.t.s[s].len; };
   auto advance = [&](int& s, int& k0) {
     k0 += BN;
@@ -217,11 +244,10 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
       k0 = 0;
     }
   };
-
   int ls = 0, lk = 0;  // next tile to load
   int cs = 0, ck = 0;  // tile to compute
-  load_tile(ls, lk);
-  store_tile(0);
+  load_tile<T, D, BN, NT, KCH, VCH>(stg, a, head_page, ls, lk, tid);
+  store_tile<M, D, BN, NT, KCH, VCH, KPITCH, VPITCH>(stg, smem, tid);
   advance(ls, lk);
   __syncthreads();
 
@@ -229,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile(ls, lk);
+    if (more) load_tile<T, D, BN, NT, KCH, VCH>(stg, a, head_page, ls, lk, tid);
 
     const bool is_cur = cs == cur;
     const int seg_len = a.t.s[cs].len;
@@ -238,62 +264,73 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
     const char* sk = smem + buf * STAGE;
     const char* sv = sk + KTILE;
 
+    // S^T = K . Q^T for the BN keys of the tile.
+    f32x16_t sc[NKB][QB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      // S^T = K . Q^T for 32 keys of the tile.
-      f32x16_t sc[QB];
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = f32x16_t{};
+      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
         const Op ka = M::load(sk + (kb * 32 + c) * KPITCH + (ks * M::K + hl * M::EPL) * ES);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb] = M::mma(ka, qop[qb][ks], sc[qb]);
+        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = M::mma(ka, qop[qb][ks], sc[kb][qb]);
       }
+    }
 
-      // Keys past the segment's valid length, or in a later causal block than the query's.
-      if (partial) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int lim = (is_cur ? lim_cur[qb] : seg_len) - ck - kb * 32;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (M::key_of_reg(i, hl) >= lim) sc[qb][i] = -INFINITY;
-        }
-      }
-
-      // Online softmax (exp2 domain), lazily rescaled.
+    // Keys past the segment's valid length, or in a later causal block than the query's.
+    if (partial) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+        const int lim = (is_cur ? lim_cur[qb] : seg_len) - ck;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m_run[qb], mx * sl2);
-        if (__any(mnew > m_run[qb] + kRescaleThreshold)) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-          l_run[qb] *= alpha;
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-          m_run[qb] = mnew;
-        }
-        const float mneg = -m_run[qb];
-        float lsum = 0.0f;
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + M::key_of_reg(i, hl) >= lim) sc[kb][qb][i] = -INFINITY;
+      }
+    }
+
+    // Online softmax (exp2 domain), lazily rescaled.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m_run[qb], mx * sl2);
+      if (__any(mnew > m_run[qb] + kRescaleThreshold)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
+        m_run[qb] = mnew;
+      }
+      const float mneg = -m_run[qb];
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][i], sl2, mneg));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][i], sl2, mneg));
           lsum += p;
-          sc[qb][i] = p;
+          sc[kb][qb][i] = p;
         }
-        l_run[qb] += lsum;
-      }
+      l_run[qb] += lsum;
+    }
 
-      // O^T += V^T . P^T
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
       Op pop[QB][PSTEPS];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kq = 0; kq < PSTEPS; ++kq) pop[qb][kq] = M::pack(sc[qb], kq);
+        for (int kq = 0; kq < PSTEPS; ++kq) pop[qb][kq] = M::pack(sc[kb][qb], kq);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -306,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_attention_kernel(const AttnA
     }
 
     if (more) {
-      store_tile(buf ^ 1);
+      store_tile<M, D, BN, NT, KCH, VCH, KPITCH, VPITCH>(stg, smem + (buf ^ 1) * STAGE, tid);
       advance(ls, lk);
     }
     advance(cs, ck);
@@ -363,8 +400,8 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
                             float softmax_scale, hipStream_t st) {
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? launch_t<uint16_t, 128, 2, 4, 64>(L, pool, t, q, o, lse, softmax_scale, st)
-                      : launch_t<uint16_t, 64, 2, 4, 64>(L, pool, t, q, o, lse, softmax_scale, st);
+    return L.D == 128 ? launch_t<uint16_t, 128, 1, 8, 64>(L, pool, t, q, o, lse, softmax_scale, st)
+                      : launch_t<uint16_t, 64, 1, 8, 64>(L, pool, t, q, o, lse, softmax_scale, st);
   return L.D == 128 ? launch_t<float, 128, 1, 4, 32>(L, pool, t, q, o, lse, softmax_scale, st)
                     : launch_t<float, 64, 1, 4, 32>(L, pool, t, q, o, lse, softmax_scale, st);
 }
