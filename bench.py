@@ -189,6 +189,15 @@ def run(args):
     }
     for L in layers:
         L["cache"].close()
+    if args.copy_calibration:
+        # A plain device copy of known size, for scaling the profiler's HBM byte counters.
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     return res
@@ -203,6 +212,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (whole heads)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (reference for the profiler's byte counters)")
     ap.add_argument("--traffic-kib", type=float, default=None,
                     help="HBM KiB per attention launch from the rocprofv3 FETCH/WRITE runs (scaled)")
     args = ap.parse_args()
