@@ -9,21 +9,39 @@
 // Work decomposition.  One workgroup per (head, tile of BM = NW*QB*32 queries); each wave
 // owns QB blocks of 32 queries for the whole key sequence.  The workgroup walks the key
 // tiles of its segments in visiting order; tiles past the last visible causal block are
-// never loaded.  Each tile (BN keys) is staged through LDS, double buffered: the next tile's
-// global loads are issued before the current tile's math.
+// never loaded.  Each tile (BN keys, one cache page for bf16) is copied straight from HBM
+// into LDS by gfx950's global-to-LDS loads (no staging registers), double buffered, into a
+// dense layout whose 16-byte pieces are XOR-swizzled per row so that the operand reads of
+// a 16-lane group hit distinct banks.
+//
+// Schedule.  Iteration i of the key loop works on 64-key sub-tiles of the cache pages:
+//   [mask sub-tile i if partial]
+//   { O^T += V^T P^T for sub-tile i-1  ||  row max of sub-tile i }
+//   [rescale O and l if some row max grew by more than 2^8]
+//   { S^T = K Q^T for sub-tile i+1     ||  exp2, rounding and row sums of sub-tile i }
+// Each {..} block mixes MFMAs, their LDS operand reads and vector-ALU work, and is
+// scheduled to keep several LDS reads in flight and to slot the vector work between the
+// MFMAs; two waves per SIMD run the same stream.  A sub-tile past every query's visible
+// keys is simply fully masked (its probabilities are zero), so the loop has no other
+// branches.  K and V pages have separate double buffers in LDS; the pages of tile t+2 (K)
+// and t+1 (V) are requested at iteration 2t+1, two iterations before their first use,
+// and one barrier ends every iteration.
 //
 // Matrix instructions (32x32 output tile).  Scores are computed transposed, S^T = K . Q^T:
 // the key block is the A operand, the queries are the B operand held in registers for the
 // whole kernel, so lane (c, hl) of a wave owns query column c and row-wise reductions are
-// in-lane plus one exchange with the other lane half.  The output P.V is also computed
-// transposed, O^T += V^T . P^T, so the probabilities never leave the registers: K rows are
-// written to LDS in a permuted row order chosen so that the score registers of a lane come
-// out exactly in the operand order the P.V instruction expects, and V is stored transposed
-// in the cache pages, so its operand is one contiguous LDS read per lane.
+// in-lane plus one exchange with the other lane half (v_permlane32_swap).  The output P.V
+// is also computed transposed, O^T += V^T . P^T, so the probabilities never leave the
+// registers: K rows are written to LDS in a permuted row order chosen so that the score
+// registers of a lane come out exactly in the operand order the P.V instruction expects,
+// and V is stored transposed in the cache pages, so its operand is one contiguous LDS read
+// per lane.
 //
 // Softmax in the exp2 domain with a lazily updated running max: O and l are rescaled only
 // when some row's max grows by more than 2^8, otherwise the stale max is kept (exact in real
-// arithmetic; probabilities stay below 2^8, far from fp32/bf16 overflow).
+// arithmetic; probabilities stay below 2^8, far from fp32/bf16 overflow).  The row sums are
+// taken from the bf16-rounded probabilities that the P.V instruction multiplies, with
+// v_dot2_f32_bf16 against (1, 1).
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -31,8 +49,9 @@
 namespace sr {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -42,6 +61,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kMaxInit = -1.0e30f;       // finite: keeps exp2(x - max) defined on masked rows
+constexpr int kMaxTiles = SR_MAX_VISIBLE_PAGES;  // tile-table capacity (pages of visible keys)
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Lanes l and l^32 each get f(x_l, x_{l^32}).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(r[0])), __builtin_bit_cast(float, unsigned(r[1])));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
+}
 
 // Accumulator layout shared by the 32x32 instructions: lane 32*hl + c holds column c and,
 // in register i, row 8*(i/4) + 4*hl + (i%4).
@@ -54,22 +88,33 @@ template <>
 struct Mma<uint16_t> {
   static constexpr int K = 16;
   static constexpr int EPL = 8;
+  static constexpr int SUB = 64;  // keys per compute sub-tile
   using Op = bf16x8_t;
   __device__ static f32x16_t mma(Op a, Op b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   // Key (inside a 32-key block) whose score lands in register i of lane half hl: the
   // registers 8*kq .. 8*kq+7 of a lane half are then the keys 16*kq + 8*hl + (0..7), which
-  // is the P operand of contraction slice kq.
+  // is the P operand of contraction slice kq.  This holds because the cache stores key r of
+  // each 32-row block at page row r with bits 2 and 3 swapped (row_pos in kv_kernels.hip):
+  // output row 8*(i/4) + 4*hl + (i%4) then holds exactly that key.
   __device__ static constexpr int key_of_reg(int i, int hl) { return 16 * (i / 8) + 8 * hl + (i % 8); }
-  // LDS row that holds key r so that key_of_reg holds: swap bits 2 and 3 of r.
-  __device__ static constexpr int row_of_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
   __device__ static Op load(const char* p) { return *reinterpret_cast<const Op*>(p); }
   __device__ static Op pack(const f32x16_t& s, int kq) {
     f32x8_t t;
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = s[8 * kq + e];
     return __builtin_convertvector(t, bf16x8_t);  // round to nearest even
+  }
+  // acc + sum of the 8 bf16 values of p
+  __device__ static float row_sum(Op p, float acc) {
+    const bf16x2_t one = {__bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2_t pr = {p[2 * e], p[2 * e + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+    return acc;
   }
   __device__ static void store4(uint16_t* dst, f32x4_t v) {
     *reinterpret_cast<bf16x4_t*>(dst) = __builtin_convertvector(v, bf16x4_t);
@@ -82,17 +127,17 @@ template <>
 struct Mma<float> {
   static constexpr int K = 2;
   static constexpr int EPL = 1;
+  static constexpr int SUB = 64;
   using Op = float;
   __device__ static f32x16_t mma(Op a, Op b, f32x16_t c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
-  // Register i of lane half hl holds key 2*i + hl: the P operand of slice kq is register kq.
+  // Register i of lane half hl holds key 2*i + hl, so the P operand of slice kq is register
+  // kq (the cache stores key r at row 8*(r/8) + 4*(r%2) + (r/2)%4 of each 32-row block).
   __device__ static constexpr int key_of_reg(int i, int hl) { return 2 * i + hl; }
-  __device__ static constexpr int row_of_key(int r) { return 8 * (r / 8) + 4 * (r % 2) + (r / 2) % 4; }
   __device__ static Op load(const char* p) { return *reinterpret_cast<const Op*>(p); }
   __device__ static Op pack(const f32x16_t& s, int kq) { return s[kq]; }
+  __device__ static float row_sum(Op p, float acc) { return acc + p; }
   __device__ static void store4(float* dst, f32x4_t v) { *reinterpret_cast<f32x4_t*>(dst) = v; }
 };
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 struct AttnArgs {
   const void* q;
@@ -106,110 +151,319 @@ struct AttnArgs {
   SegTable t;
 };
 
-// Registers holding one K/V tile between its global loads and its LDS stores.
-template <int KCH, int VCH>
-struct Stage {
-  u32x4_t k[KCH];
-  u32x4_t v[VCH];
-};
-
-// Issues the global loads of key tile (segment s, first key k0): BN key rows of K (contiguous
-// in the page) and the BN-key slice of each of the D rows of the transposed V page.
-template <typename T, int D, int BN, int NT, int KCH, int VCH>
-__device__ __forceinline__ void load_tile(Stage<KCH, VCH>& st, const AttnArgs& a, size_t head_page, int s, int k0,
-                                          int tid) {
-  constexpr int ES = int(sizeof(T));
-  constexpr int KPR = D * ES / 16;
-  constexpr int VPR = BN * ES / 16;
-  const size_t page = head_page + a.t.s[s].page + k0 / SR_PAGE_TOKENS;
-  const char* kb = a.kpool + (page * SR_PAGE_TOKENS + k0 % SR_PAGE_TOKENS) * (D * ES);
-  const char* vb = a.vpool + page * (D * SR_PAGE_TOKENS * ES) + (k0 % SR_PAGE_TOKENS) * ES;
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int ci = j * NT + tid;
-    st.k[j] = *reinterpret_cast<const u32x4_t*>(kb + (ci / KPR) * (D * ES) + (ci % KPR) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < VCH; ++j) {
-    const int ci = j * NT + tid;
-    st.v[j] = *reinterpret_cast<const u32x4_t*>(vb + (ci / VPR) * (SR_PAGE_TOKENS * ES) + (ci % VPR) * 16);
-  }
-}
-
-// Writes a staged tile into one LDS stage: K rows at their permuted positions (see
-// Mma::row_of_key), V^T rows as they are.
-template <typename M, int D, int BN, int NT, int KCH, int VCH, int KPITCH, int VPITCH>
-__device__ __forceinline__ void store_tile(const Stage<KCH, VCH>& st, char* stage, int tid) {
-  constexpr int ES = int(sizeof(typename M::Op)) / M::EPL;
-  constexpr int KPR = D * ES / 16;
-  constexpr int VPR = BN * ES / 16;
-  char* sv = stage + BN * KPITCH;
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int ci = j * NT + tid;
-    const int r = ci / KPR;
-    const int lr = (r & ~31) | M::row_of_key(r & 31);
-    *reinterpret_cast<u32x4_t*>(stage + lr * KPITCH + (ci % KPR) * 16) = st.k[j];
-  }
-#pragma unroll
-  for (int j = 0; j < VCH; ++j) {
-    const int ci = j * NT + tid;
-    *reinterpret_cast<u32x4_t*>(sv + (ci / VPR) * VPITCH + (ci % VPR) * 16) = st.v[j];
-  }
-}
-
-template <typename T, int D, int QB, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, NW / 4) void chunk_attention_kernel(const AttnArgs a) {
+// Geometry of one kernel instantiation: one LDS tile = one cache page = 2 sub-tiles.
+template <typename T, int D_, int QB_, int NW_>
+struct Geo {
   using M = Mma<T>;
   using Op = typename M::Op;
-  constexpr int ES = int(sizeof(T));
-  constexpr int BM = NW * QB * 32;
-  constexpr int NKB = BN / 32;          // 32-key blocks per tile
-  constexpr int NDB = D / 32;           // 32-feature blocks of the output
-  constexpr int KSTEPS = D / M::K;      // contraction steps of K.Q^T
-  constexpr int PSTEPS = 32 / M::K;     // contraction steps of V^T.P^T per 32-key block
-  constexpr int KPITCH = D * ES + 16;   // LDS bytes per key row (16-byte pad: bank spread)
-  constexpr int VPITCH = BN * ES + 16;  // LDS bytes per feature row of V^T
-  constexpr int KTILE = BN * KPITCH;
-  constexpr int STAGE = KTILE + D * VPITCH;
-  constexpr int NT = NW * 64;
-  constexpr int KPR = D * ES / 16;      // 16-byte pieces per key row
-  constexpr int VPR = BN * ES / 16;     // 16-byte pieces per V^T row of the tile
-  constexpr int KCH = BN * KPR / NT;
-  constexpr int VCH = D * VPR / NT;
-  static_assert(KCH * NT == BN * KPR && VCH * NT == D * VPR, "tile pieces must split evenly");
-  static_assert(BN % 32 == 0 && SR_PAGE_TOKENS % BN == 0, "tiles must not straddle pages");
-  __shared__ __align__(16) char smem[2 * STAGE];
+  using Elem = T;
+  static constexpr int D = D_, QB = QB_, NW = NW_;
+  static constexpr int ES = int(sizeof(T));
+  static constexpr int SUB = M::SUB;           // keys per compute sub-tile
+  static constexpr int BN = SR_PAGE_TOKENS;    // keys per LDS tile
+  static constexpr int BM = NW * QB * 32;
+  static constexpr int NKB = SUB / 32;         // 32-key blocks per sub-tile
+  static constexpr int NDB = D / 32;           // 32-feature blocks of the output
+  static constexpr int KSTEPS = D / M::K;      // contraction steps of K.Q^T
+  static constexpr int PSTEPS = 32 / M::K;     // contraction steps of V^T.P^T per 32-key block
+  static constexpr int KTILE = BN * D * ES;    // bytes of the K page (and of the V page)
+  static constexpr int VBASE = 2 * KTILE;      // LDS: K page buffers 0, 1, then V page buffers 0, 1
+  static constexpr int TABLE = 4 * KTILE;      // then the tile table (16 bytes per tile)
+  static constexpr int LDS_BYTES = TABLE + kMaxTiles * 16;
+  static constexpr int LOADS = KTILE / 1024 / NW;  // 1 KiB global-to-LDS loads per wave, per page
+  static_assert(LOADS * NW * 1024 == KTILE, "page loads must split evenly");
+  static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One 16-byte global-to-LDS load per lane: lane i's 16 bytes at `g` land at LDS byte
+// lds_base + 16 * i.  Issued as inline asm so the compiler's wait-count insertion does not
+// treat every later LDS read as dependent on it (it cannot tell the page buffers apart);
+// the kernel orders these loads itself with explicit vmcnt waits and barriers.  M0 is
+// written here and used by nothing else in this kernel.
+__device__ __forceinline__ void lds_load16(const void* g, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+
+// Issues the global-to-LDS loads of one page (K or V, `src` = its first byte) into `dst`:
+// a contiguous copy; load j of wave w moves 1 KiB block (j*NW + w), lane i its piece i.
+template <class G>
+__device__ __forceinline__ void issue_page(const char* src, char* dst, int wave, int lane) {
+  const unsigned base = unsigned(size_t((lds_ptr_t)dst));
+#pragma unroll
+  for (int j = 0; j < G::LOADS; ++j) {
+    const int blk = (j * G::NW + wave) * 1024;
+    lds_load16(src + blk + lane * 16, uniform(int(base) + blk));
+  }
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's global(-to-LDS) loads still outstanding.
+// Inline asm as well: the compiler does not see the page loads and would drop a builtin
+// wait that it considers redundant.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Operand addresses in a page buffer (byte offsets).  K: page row lr (rows are stored in
+// operand order), element e of the row; piece x of every row is stored contiguously.
+template <class G>
+__device__ __forceinline__ int k_addr(int lr, int e) {
+  const int bo = e * G::ES;
+  return ((bo >> 4) * G::BN + lr) * 16 + (bo & 15);
+}
+// V: feature row d, key k of the page; piece y (keys 16/ES*y ..) of every feature row is
+// stored contiguously.
+template <class G>
+__device__ __forceinline__ int v_addr(int d, int k) {
+  const int bo = k * G::ES;
+  return ((bo >> 4) * G::D + d) * 16 + (bo & 15);
+}
+
+// Per-lane running state of the online softmax for the wave's QB query blocks.
+template <class G>
+struct RowState {
+  float m[G::QB];               // running max (log2 domain, scaled)
+  float l[G::QB];               // running sum of probabilities (relative to m)
+  f32x16_t acc[G::QB][G::NDB];  // O^T accumulators
+};
+
+template <class G>
+using Scores = f32x16_t[G::NKB][G::QB];
+template <class G>
+using Probs = typename G::Op[G::NKB][G::QB][G::PSTEPS];
+
+// S^T = K . Q^T for sub-tile `sub` of the K page in `kpage`.
+template <class G>
+__device__ __forceinline__ void scores(Scores<G>& sc, const typename G::Op (&qop)[G::QB][G::KSTEPS], const char* kpage,
+                                       int sub, int c, int hl) {
+  using M = typename G::M;
+#pragma unroll
+  for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < G::QB; ++qb) sc[kb][qb] = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < G::KSTEPS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb) {
+      const typename G::Op ka = M::load(kpage + k_addr<G>(sub * G::SUB + kb * 32 + c, ks * M::K + hl * M::EPL));
+#pragma unroll
+      for (int qb = 0; qb < G::QB; ++qb) sc[kb][qb] = M::mma(ka, qop[qb][ks], sc[kb][qb]);
+    }
+}
+
+// Key r of the sub-tile is visible to query block qb iff r < lim[qb]; the others get -inf.
+template <class G>
+__device__ __forceinline__ void mask_sub(Scores<G>& sc, const int (&lim)[G::QB], int hl) {
+  using M = typename G::M;
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + M::key_of_reg(i, hl) >= lim[qb]) sc[kb][qb][i] = -INFINITY;
+}
+
+// Row max of the raw scores (both lane halves hold the same value).
+template <class G>
+__device__ __forceinline__ void row_max(const Scores<G>& sc, float (&rmax)[G::QB]) {
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
+    rmax[qb] = pair_max(mx);
+  }
+}
+
+// Lazy rescale: move the running max only when some row's max grew by more than 2^8.
+template <class G>
+__device__ __forceinline__ void rescale(RowState<G>& st, const float (&rmax)[G::QB], float sl2) {
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) {
+    const float mnew = fmaxf(st.m[qb], rmax[qb] * sl2);
+    if (__any(mnew > st.m[qb] + kRescaleThreshold)) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m[qb] - mnew);
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] *= alpha;
+      st.m[qb] = mnew;
+    }
+  }
+}
+
+// Probabilities exp2(s * scale_log2 - m), rounded to the operand type, and their row sums.
+template <class G>
+__device__ __forceinline__ void softmax_exp(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, float sl2) {
+  using M = typename G::M;
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) {
+    const float mneg = -st.m[qb];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[kb][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][i], sl2, mneg));
+#pragma unroll
+      for (int kq = 0; kq < G::PSTEPS; ++kq) {
+        pop[kb][qb][kq] = M::pack(sc[kb][qb], kq);
+        lsum = M::row_sum(pop[kb][qb][kq], lsum);
+      }
+    }
+    st.l[qb] += lsum;
+  }
+}
+
+// O^T += V^T . P^T for sub-tile `sub` of the V page in `vpage`.
+template <class G>
+__device__ __forceinline__ void accumulate(RowState<G>& st, const Probs<G>& pop, const char* vpage, int sub, int c,
+                                           int hl) {
+  using M = typename G::M;
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int kq = 0; kq < G::PSTEPS; ++kq) {
+        const typename G::Op va =
+            M::load(vpage + v_addr<G>(db * 32 + c, sub * G::SUB + kb * 32 + kq * M::K + hl * M::EPL));
+#pragma unroll
+        for (int qb = 0; qb < G::QB; ++qb) st.acc[qb][db] = M::mma(va, pop[kb][qb][kq], st.acc[qb][db]);
+      }
+}
+
+// ---- bf16 path: explicitly pipelined blocks ------------------------------------------
+// Each MFMA sits in its own scheduling region (sched_barrier), with the LDS read of the
+// operand AH MFMAs ahead and a slice of the vector work, so the order below is the order
+// the hardware sees.  Operands go through a ring of AH registers.
+constexpr int AH = 6;
+
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+// An empty asm "use": the value must be computed before this point.  Keeps the compiler from
+// sinking the exponentials (consumed only in the next iteration) out of the region where they
+// fill the gap between two MFMAs.
+template <typename V>
+__device__ __forceinline__ void pin(const V& v) {
+  asm volatile("" ::"v"(v));
+}
+
+// P.V operand r of sub-tile `sub`: r -> (db = r % NDB, kb, kq), so consecutive MFMAs
+// accumulate into different output blocks.
+template <class G>
+__device__ __forceinline__ typename G::Op pv_operand(const char* vpage, int sub, int r, int c, int hl) {
+  constexpr int NDB = G::NDB;
+  const int db = r % NDB, kk = r / NDB, kb = kk / G::PSTEPS, kq = kk % G::PSTEPS;
+  return G::M::load(vpage + v_addr<G>(db * 32 + c, sub * G::SUB + kb * 32 + kq * 16 + hl * 8));
+}
+// Score operand r of sub-tile `sub`: r -> (ks = r / NKB, kb = r % NKB), alternating the two
+// score chains.
+template <class G>
+__device__ __forceinline__ typename G::Op qk_operand(const char* kpage, int sub, int r, int c, int hl) {
+  const int ks = r / G::NKB, kb = r % G::NKB;
+  return G::M::load(kpage + k_addr<G>(sub * G::SUB + kb * 32 + c, ks * 16 + hl * 8));
+}
+
+// Block A: row max of sub-tile i (scores in sc) alongside O^T += V^T P^T of sub-tile i-1.
+// kq_ring receives the first AH score operands of sub-tile i+1 for block B.
+template <class G>
+__device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, const Probs<G>& pop, float (&rmax)[1],
+                                        const char* vpage, int vsub, const char* kpage, int ksub,
+                                        typename G::Op (&kq_ring)[AH], int c, int hl) {
+  using Op = typename G::Op;
+  constexpr int NP = G::NDB * G::NKB * G::PSTEPS;
+  Op vq[AH];
+#pragma unroll
+  for (int r = 0; r < AH; ++r) kq_ring[r] = qk_operand<G>(kpage, ksub, r, c, hl);
+#pragma unroll
+  for (int r = 0; r < AH; ++r) vq[r] = pv_operand<G>(vpage, vsub, r, c, hl);
+  row_max<G>(sc, rmax);
+  fence();
+#pragma unroll
+  for (int r = 0; r < NP; ++r) {
+    const int db = r % G::NDB, kk = r / G::NDB, kb = kk / G::PSTEPS, kq = kk % G::PSTEPS;
+    st.acc[0][db] = G::M::mma(vq[r % AH], pop[kb][0][kq], st.acc[0][db]);
+    if (r + AH < NP) vq[r % AH] = pv_operand<G>(vpage, vsub, r + AH, c, hl);
+    fence();
+  }
+}
+
+// Block B: S^T = K Q^T of sub-tile i+1 alongside the probabilities of sub-tile i.
+template <class G>
+__device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, Scores<G>& sn,
+                                        const typename G::Op (&qop)[1][G::KSTEPS], const char* kpage, int ksub,
+                                        typename G::Op (&kq_ring)[AH], float sl2, int c, int hl) {
+  using M = typename G::M;
+  constexpr int NS = G::KSTEPS * G::NKB;
+  constexpr int NE = 16 * G::NKB;  // probabilities per lane
+  constexpr int EPR = (NE + NS - 1) / NS;  // per region
+#pragma unroll
+  for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
+  const float mneg = -st.m[0];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int ks = r / G::NKB, kb = r % G::NKB;
+    sn[kb][0] = M::mma(kq_ring[r % AH], qop[0][ks], sn[kb][0]);
+    if (r + AH < NS) kq_ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH, c, hl);
+#pragma unroll
+    for (int e = r * EPR; e < (r + 1) * EPR && e < NE; ++e) {
+      const int ekb = e / 16, ei = e % 16;
+      sc[ekb][0][ei] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ekb][0][ei], sl2, mneg));
+      pin(sc[ekb][0][ei]);
+      if ((e & 7) == 7) {  // a group of 8 probabilities is complete: round and sum them
+        pop[ekb][0][ei / 8] = M::pack(sc[ekb][0], ei / 8);
+        lsum = M::row_sum(pop[ekb][0][ei / 8], lsum);
+        pin(pop[ekb][0][ei / 8]);
+        pin(lsum);
+      }
+    }
+    fence();
+  }
+  st.l[0] += lsum;
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(const AttnArgs a) {
+  using M = typename G::M;
+  using Op = typename G::Op;
+  using T = typename G::Elem;
+  constexpr int BN = G::BN, SUB = G::SUB, D = G::D;
+  __shared__ __align__(1024) char smem[G::LDS_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = uniform(tid >> 6);
   const int c = lane & 31, hl = lane >> 5;
 
   // Workgroups are dispatched round-robin over the 8 XCDs (hardware id i runs on XCD i % 8).
   // Renumber so each XCD gets a contiguous range of (head, query tile): the query tiles of a
   // head then share that XCD's L2 while they stream the same keys.
-  const int G = a.num_wg, bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3, per = G >> 3, rem = G & 7;
+  const int nwg = a.num_wg, bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3, per = nwg >> 3, rem = nwg & 7;
   const int wg = local + xcd * per + (xcd < rem ? xcd : rem);
   // Integer divisions are expanded on the vector ALU; readfirstlane tells the compiler the
   // results are wave-uniform so the tile loop stays a scalar loop.
   const int h = uniform(wg / a.q_tiles);
-  const int q0 = uniform((wg - h * a.q_tiles) * BM);
+  const int q0 = uniform((wg - h * a.q_tiles) * G::BM);
   const int n_q = a.n_q, H = a.H, cb = a.causal_block;
   const int cur = a.t.n - 1;
   const int cur_len = a.t.s[cur].len;
 
   // Query operands (B operand of K.Q^T), resident for the whole kernel.
-  Op qop[QB][KSTEPS];
-  int lim_cur[QB];
+  Op qop[G::QB][G::KSTEPS];
+  int lim_cur[G::QB];
   const T* __restrict__ qg = static_cast<const T*>(a.q);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + (wave * QB + qb) * 32 + c;
+  for (int qb = 0; qb < G::QB; ++qb) {
+    const int qrow = q0 + (wave * G::QB + qb) * 32 + c;
     const bool ok = qrow < n_q;
     const T* src = qg + (size_t(ok ? qrow : 0) * H + h) * D + hl * M::EPL;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < G::KSTEPS; ++ks) {
       Op v = M::load(reinterpret_cast<const char*>(src + ks * M::K));
       qop[qb][ks] = ok ? v : Op{};
     }
@@ -217,166 +471,153 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void chunk_attention_kernel(const 
   }
 
   // Keys of the current chunk visible to every / to some query of this workgroup.
-  const int qlast = min(q0 + BM, n_q) - 1;
+  const int qlast = min(q0 + G::BM, n_q) - 1;
   const int cur_all = uniform(min(cur_len, (q0 / cb + 1) * cb));
   const int cur_any = uniform(min(cur_len, (qlast / cb + 1) * cb));
   int ntiles = (cur_any + BN - 1) / BN;
   for (int s = 0; s < cur; ++s) ntiles += (a.t.s[s].len + BN - 1) / BN;
   ntiles = uniform(ntiles);
 
-  float m_run[QB], l_run[QB];
-  f32x16_t acc[QB][NDB];
+  RowState<G> st;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = kMaxInit;
-    l_run[qb] = 0.0f;
+  for (int qb = 0; qb < G::QB; ++qb) {
+    st.m[qb] = kMaxInit;
+    st.l[qb] = 0.0f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16_t{};
+    for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] = f32x16_t{};
   }
 
   const size_t head_page = size_t(h) * a.total_pages;
-  Stage<KCH, VCH> stg;
-  auto seg_end = [&](int s) { return s == cur ? cur_any : a.t.s[s].len; };
-  auto advance = [&](int& s, int& k0) {
-    k0 += BN;
-    if (k0 >= seg_end(s)) {
-      ++s;
-      k0 = 0;
+
+  // Tile table, built once per workgroup: for tile t (visiting order) the page index
+  // (relative to the head's first page), the key offset inside the current chunk (-1 for
+  // the persistent bank and history), and the keys of the tile visible to some / to every
+  // query of the workgroup (relative to the tile start; <= 0 past them).
+  int4* tab = reinterpret_cast<int4*>(smem + G::TABLE);
+  for (int t = tid; t < ntiles; t += G::NW * 64) {
+    int s = 0, first = 0;
+    for (; s < cur; ++s) {
+      const int nt = (a.t.s[s].len + BN - 1) / BN;
+      if (t < first + nt) break;
+      first += nt;
     }
-  };
-  int ls = 0, lk = 0;  // next tile to load
-  int cs = 0, ck = 0;  // tile to compute
-  load_tile<T, D, BN, NT, KCH, VCH>(stg, a, head_page, ls, lk, tid);
-  store_tile<M, D, BN, NT, KCH, VCH, KPITCH, VPITCH>(stg, smem, tid);
-  advance(ls, lk);
+    const int k0 = (t - first) * BN;
+    const bool is_cur = s == cur;
+    const int len = a.t.s[s].len;
+    tab[t] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
+                       (is_cur ? cur_all : len) - k0);
+  }
+  __syncthreads();
+  auto tile_page = [&](int t) { return (head_page + uniform(tab[t].x)) * G::KTILE; };
+
+  // Prologue: K and V of tile 0, K of tile 1; V buffer 1 zeroed (iteration 0 multiplies it
+  // by all-zero probabilities, so it must not hold NaN bit patterns).
+  {
+    const size_t p0 = tile_page(0);
+    issue_page<G>(a.kpool + p0, smem, wave, lane);
+    issue_page<G>(a.vpool + p0, smem + G::VBASE, wave, lane);
+    if (ntiles > 1) issue_page<G>(a.kpool + tile_page(1), smem + G::KTILE, wave, lane);
+    u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::KTILE);
+    for (int x = tid; x < G::KTILE / 16; x += G::NW * 64) vz[x] = u32x4_t{0, 0, 0, 0};
+  }
+  wait_loads<0>();
   __syncthreads();
 
   const float sl2 = a.scale_log2;
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile<T, D, BN, NT, KCH, VCH>(stg, a, head_page, ls, lk, tid);
+  const int nsub = 2 * ntiles;  // sub-tiles j = 2t, 2t+1 of tile t
+  Scores<G> sc;
+  Probs<G> pop;
+#pragma unroll
+  for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < G::QB; ++qb)
+#pragma unroll
+      for (int kq = 0; kq < G::PSTEPS; ++kq) pop[kb][qb][kq] = Op{};
+  scores<G>(sc, qop, smem, 0, c, hl);
+  int4 ent = tab[0];  // tile of sub-tile i
 
-    const bool is_cur = cs == cur;
-    const int seg_len = a.t.s[cs].len;
-    const bool partial = ck + BN > (is_cur ? cur_all : seg_len);
-
-    const char* sk = smem + buf * STAGE;
-    const char* sv = sk + KTILE;
-
-    // S^T = K . Q^T for the BN keys of the tile.
-    f32x16_t sc[NKB][QB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const Op ka = M::load(sk + (kb * 32 + c) * KPITCH + (ks * M::K + hl * M::EPL) * ES);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = M::mma(ka, qop[qb][ks], sc[kb][qb]);
-      }
+  for (int i = 0; i <= nsub; ++i) {
+    const int t = i >> 1;
+    // Page requests: at iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in
+    // iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read in iteration 2t).
+    if (i & 1) {
+      if (t + 2 < ntiles) issue_page<G>(a.kpool + tile_page(t + 2), smem + (t & 1) * G::KTILE, wave, lane);
+      if (t + 1 < ntiles)
+        issue_page<G>(a.vpool + tile_page(t + 1), smem + G::VBASE + ((t + 1) & 1) * G::KTILE, wave, lane);
     }
+    // Table entry of the next iteration's tile (read now, used next iteration).
+    const int4 ent_next = tab[min((i + 1) >> 1, ntiles - 1)];
 
-    // Keys past the segment's valid length, or in a later causal block than the query's.
-    if (partial) {
+    // Sub-tile i: keys visible to some / every query (relative to the sub-tile), per-lane
+    // limit; all zero past the sequence, which masks the whole sub-tile.
+    const int sub0 = (i & 1) * SUB;
+    const bool in_seq = i < nsub;
+    const int any_rel = in_seq ? uniform(ent.z) - sub0 : 0;
+    const int all_rel = in_seq ? uniform(ent.w) - sub0 : 0;
+    const int cur_k0 = uniform(ent.y);
+    int lim[G::QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int lim = (is_cur ? lim_cur[qb] : seg_len) - ck;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + M::key_of_reg(i, hl) >= lim) sc[kb][qb][i] = -INFINITY;
-      }
-    }
+    for (int qb = 0; qb < G::QB; ++qb)
+      lim[qb] = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[qb] - cur_k0 - sub0 : all_rel);
+    const bool partial = all_rel < SUB;
 
-    // Online softmax (exp2 domain), lazily rescaled.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run[qb], mx * sl2);
-      if (__any(mnew > m_run[qb] + kRescaleThreshold)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-        m_run[qb] = mnew;
-      }
-      const float mneg = -m_run[qb];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][qb][i], sl2, mneg));
-          lsum += p;
-          sc[kb][qb][i] = p;
-        }
-      l_run[qb] += lsum;
+    if (partial) mask_sub<G>(sc, lim, hl);
+    const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::KTILE;  // sub-tile i-1
+    const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
+    Scores<G> sn;
+    float rmax[G::QB];
+    if constexpr (G::ES == 2 && G::QB == 1) {
+      Op kq_ring[AH];
+      // P.V of sub-tile i-1 alongside the row max of sub-tile i, then the rescale, then the
+      // scores of sub-tile i+1 alongside the probabilities of sub-tile i.
+      block_a<G>(st, sc, pop, rmax, vpage, (i - 1) & 1, kpage, (i + 1) & 1, kq_ring, c, hl);
+      rescale<G>(st, rmax, sl2);
+      block_b<G>(st, sc, pop, sn, qop, kpage, (i + 1) & 1, kq_ring, sl2, c, hl);
+    } else {
+      accumulate<G>(st, pop, vpage, (i - 1) & 1, c, hl);
+      row_max<G>(sc, rmax);
+      rescale<G>(st, rmax, sl2);
+      scores<G>(sn, qop, kpage, (i + 1) & 1, c, hl);
+      softmax_exp<G>(st, sc, pop, sl2);
     }
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < G::QB; ++qb) sc[kb][qb] = sn[kb][qb];
+    ent = ent_next;
 
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      Op pop[QB][PSTEPS];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kq = 0; kq < PSTEPS; ++kq) pop[qb][kq] = M::pack(sc[kb][qb], kq);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kq = 0; kq < PSTEPS; ++kq) {
-          const Op va = M::load(sv + (db * 32 + c) * VPITCH + (kb * 32 + kq * M::K + hl * M::EPL) * ES);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = M::mma(va, pop[qb][kq], acc[qb][db]);
-        }
-      }
-    }
-
-    if (more) {
-      store_tile<M, D, BN, NT, KCH, VCH, KPITCH, VPITCH>(stg, smem + (buf ^ 1) * STAGE, tid);
-      advance(ls, lk);
-    }
-    advance(cs, ck);
+    // V of tile t+1 and K of tile t+2 are first read in iteration 2t+3: wait at the end of
+    // the even iteration 2t+2 (they were requested at 2t+1, nothing later).
+    if ((i & 1) == 0 && i >= 2) wait_loads<0>();
     __syncthreads();
   }
 
   // Epilogue: O = O^T / l, written token-major; lse = (max + log2 l) * ln 2.
   T* __restrict__ og = static_cast<T*>(a.o);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = q0 + (wave * QB + qb) * 32 + c;
-    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  for (int qb = 0; qb < G::QB; ++qb) {
+    const int qrow = q0 + (wave * G::QB + qb) * 32 + c;
+    const float l = pair_sum(st.l[qb]);
     const float inv = 1.0f / l;
     if (qrow < n_q) {
       T* orow = og + (size_t(qrow) * H + h) * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           f32x4_t v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[qb][db][4 * ig + e] * inv;
+          for (int e = 0; e < 4; ++e) v[e] = st.acc[qb][db][4 * ig + e] * inv;
           M::store4(orow + db * 32 + 8 * ig + 4 * hl, v);
         }
-      if (a.lse && hl == 0) a.lse[size_t(h) * n_q + qrow] = (m_run[qb] + __log2f(l)) * kLn2;
+      if (a.lse && hl == 0) a.lse[size_t(h) * n_q + qrow] = (st.m[qb] + __log2f(l)) * kLn2;
     }
   }
 }
 
-template <typename T, int D, int QB, int NW, int BN>
+template <class G>
 hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
                     float scale, hipStream_t st) {
-  constexpr int BM = NW * QB * 32;
   AttnArgs a;
   a.q = q;
   a.o = o;
@@ -387,11 +628,11 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
   a.H = L.H;
   a.total_pages = L.total_pages;
   a.causal_block = L.cb;
-  a.q_tiles = (a.n_q + BM - 1) / BM;
+  a.q_tiles = (a.n_q + G::BM - 1) / G::BM;
   a.num_wg = a.q_tiles * L.H;
   a.scale_log2 = scale * kLog2e;
   a.t = t;
-  hipLaunchKernelGGL((chunk_attention_kernel<T, D, QB, NW, BN>), dim3(a.num_wg), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((chunk_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -400,10 +641,11 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
                             float softmax_scale, hipStream_t st) {
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? launch_t<uint16_t, 128, 1, 8, 64>(L, pool, t, q, o, lse, softmax_scale, st)
-                      : launch_t<uint16_t, 64, 1, 8, 64>(L, pool, t, q, o, lse, softmax_scale, st);
-  return L.D == 128 ? launch_t<float, 128, 1, 4, 32>(L, pool, t, q, o, lse, softmax_scale, st)
-                    : launch_t<float, 64, 1, 4, 32>(L, pool, t, q, o, lse, softmax_scale, st);
+    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st)
+                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st);
+  // fp32 caches are head_dim 64 only (validated on the host): a double-buffered 128-key
+  // fp32 tile at head_dim 128 would need 256 KiB of LDS.
+  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st);
 }
 
 }  // namespace sr

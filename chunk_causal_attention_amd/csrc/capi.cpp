@@ -113,6 +113,10 @@ sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* o
   if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
   if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
   const sr::SegTable t = make_table(c->ring, bank, nullptr);
+  int32_t pages = 0;
+  for (int i = 0; i < t.n; ++i) pages += (t.s[i].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+  if (pages > SR_MAX_VISIBLE_PAGES)
+    return sr::fail(SR_E_UNSUPPORTED, "the call visits %d pages of keys, more than %d", pages, SR_MAX_VISIBLE_PAGES);
   return device_status(
       sr::launch_attention(L, c->pool, t, q, out, lse, softmax_scale, static_cast<hipStream_t>(stream)),
       "chunk attention");

@@ -29,6 +29,7 @@ sr_status make_layout(const sr_kvcache_config* cfg, Layout* out) {
   if (c.dtype != SR_BF16 && c.dtype != SR_F32) return fail(SR_E_INVALID, "dtype %d is not SR_BF16 or SR_F32", c.dtype);
   if (c.num_heads < 1 || c.num_heads > 4096) return fail(SR_E_INVALID, "num_heads %d outside [1, 4096]", c.num_heads);
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SR_E_UNSUPPORTED, "head_dim %d: only 64 and 128", c.head_dim);
+  if (c.dtype == SR_F32 && c.head_dim != 64) return fail(SR_E_UNSUPPORTED, "SR_F32 supports head_dim 64 only");
   if (c.persistent_tokens < 0 || c.persistent_tokens > (1 << 24))
     return fail(SR_E_INVALID, "persistent_tokens %d outside [0, 2^24]", c.persistent_tokens);
   if (c.num_banks < 1 || c.num_banks > 64) return fail(SR_E_INVALID, "num_banks %d outside [1, 64]", c.num_banks);

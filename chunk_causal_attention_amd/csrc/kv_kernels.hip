@@ -9,61 +9,93 @@
 namespace sr {
 namespace {
 
-__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, size_t n16) {
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byte piece
+
+__global__ __launch_bounds__(256) void zero_kernel(u32x4_t* __restrict__ p, size_t n16) {
   const size_t stride = size_t(gridDim.x) * blockDim.x;
-  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = u32x4_t{0, 0, 0, 0};
 }
 
 constexpr int kAppendTokens = 64;  // tokens per workgroup (half a page)
 
-// Workgroup (token tile of 64, head).  K rows are copied straight through in 16-byte
-// pieces; V goes through LDS and is written transposed: for each feature d, the tile's
-// 64 tokens are contiguous in the page.
+// Page layout (one head, one page of 128 tokens), with E = 16 / sizeof(T) elements per
+// 16-byte piece:
+//   K  element (token t, feature d) at ((d / E) * 128 + row_pos(t)) * E + d % E
+//   V  element (token t, feature d) at ((t / E) * D + d) * E + t % E
+// i.e. K is stored piece-column by piece-column with its 128 rows in the order the
+// attention kernel's matrix operands want them (row_pos permutes rows inside each block of
+// 32), and V is stored transposed, E consecutive tokens of one feature per piece.  A page
+// is then copied into LDS as is, and every operand read is one 16-byte piece per lane with
+// 32 lanes reading 512 contiguous bytes.
+template <typename T>
+__device__ __forceinline__ int row_pos(int t) {
+  const int r = t & 31;
+  if constexpr (sizeof(T) == 2) return (t & ~31) | (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+  return (t & ~31) | (8 * (r / 8) + 4 * (r % 2) + (r / 2) % 4);
+}
+
+// The 16-byte piece made of E elements of one LDS column (stride `pitch` elements).
+__device__ __forceinline__ u32x4_t column_piece(const uint16_t* p, int pitch) {
+  u32x4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = unsigned(p[(2 * i) * pitch]) | (unsigned(p[(2 * i + 1) * pitch]) << 16);
+  return w;
+}
+__device__ __forceinline__ u32x4_t column_piece(const float* p, int pitch) {
+  return u32x4_t{__float_as_uint(p[0]), __float_as_uint(p[pitch]), __float_as_uint(p[2 * pitch]),
+                 __float_as_uint(p[3 * pitch])};
+}
+
+// Workgroup (64-token half page, head).  Both K and V rows go through LDS (coalesced
+// 16-byte reads along the features), then are written piece by piece in page order
+// (coalesced 16-byte writes).  Tokens >= n are written as zeros.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v, int n, int H,
                                                      T* __restrict__ kpool, T* __restrict__ vpool, int total_pages,
                                                      int page0) {
-  constexpr int EPC = 16 / int(sizeof(T));  // elements per 16-byte piece
-  constexpr int CPR = D / EPC;              // pieces per token row
-  constexpr int PITCH = D + EPC;            // LDS row pitch (elements), padded by 16 bytes
-  __shared__ __align__(16) T tile[kAppendTokens * PITCH];
+  constexpr int E = 16 / int(sizeof(T));  // elements per 16-byte piece
+  constexpr int CPR = D / E;              // pieces per token row
+  constexpr int PITCH = D + E;            // LDS row pitch (elements), padded by one piece
+  __shared__ __align__(16) T ktile[kAppendTokens * PITCH];
+  __shared__ __align__(16) T vtile[kAppendTokens * PITCH];
 
   const int h = blockIdx.y;
-  const int t0 = blockIdx.x * kAppendTokens;
+  const int t0 = blockIdx.x * kAppendTokens;  // first token of this half page (slot-relative)
+  const int tp = t0 % SR_PAGE_TOKENS;         // its position inside the page
   const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
-  T* kdst = kpool + (page * SR_PAGE_TOKENS + t0 % SR_PAGE_TOKENS) * D;
-  const uint4 z = make_uint4(0, 0, 0, 0);
+  const u32x4_t z = {0, 0, 0, 0};
 
   for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
-    const int r = ci / CPR, c = ci % CPR, t = t0 + r;
-    const size_t src = (size_t(t) * H + h) * D + c * EPC;
-    const uint4 kv = t < n ? *reinterpret_cast<const uint4*>(k + src) : z;
-    const uint4 vv = t < n ? *reinterpret_cast<const uint4*>(v + src) : z;
-    *reinterpret_cast<uint4*>(kdst + r * D + c * EPC) = kv;
-    *reinterpret_cast<uint4*>(tile + r * PITCH + c * EPC) = vv;
+    const int r = ci / CPR, x = ci % CPR, t = t0 + r;
+    const size_t src = (size_t(t) * H + h) * D + x * E;
+    *reinterpret_cast<u32x4_t*>(ktile + r * PITCH + x * E) = t < n ? *reinterpret_cast<const u32x4_t*>(k + src) : z;
+    *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = t < n ? *reinterpret_cast<const u32x4_t*>(v + src) : z;
   }
   __syncthreads();
 
-  T* vdst = vpool + page * D * SR_PAGE_TOKENS + t0 % SR_PAGE_TOKENS;
-  constexpr int CPD = kAppendTokens / EPC;  // pieces per feature row of the tile
-  for (int ci = threadIdx.x; ci < D * CPD; ci += blockDim.x) {
-    const int d = ci / CPD, c = ci % CPD;
-    union {
-      T e[EPC];
-      uint4 u;
-    } pk;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) pk.e[e] = tile[(c * EPC + e) * PITCH + d];
-    *reinterpret_cast<uint4*>(vdst + size_t(d) * SR_PAGE_TOKENS + c * EPC) = pk.u;
+  // K: piece x of row r goes to ((x * 128 + row_pos(tp + r)) * E); consecutive threads take
+  // consecutive rows of one piece column.
+  T* kpage = kpool + page * SR_PAGE_TOKENS * D;
+  for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
+    const int x = ci / kAppendTokens, r = ci % kAppendTokens;
+    *reinterpret_cast<u32x4_t*>(kpage + (size_t(x) * SR_PAGE_TOKENS + row_pos<T>(tp + r)) * E) =
+        *reinterpret_cast<const u32x4_t*>(ktile + r * PITCH + x * E);
+  }
+  // V: piece (token group g, feature d) holds tokens E*g .. E*g+E-1 of feature d.
+  T* vpage = vpool + page * SR_PAGE_TOKENS * D;
+  constexpr int GROUPS = kAppendTokens / E;
+  for (int ci = threadIdx.x; ci < GROUPS * D; ci += blockDim.x) {
+    const int g = ci / D, d = ci % D;
+    *reinterpret_cast<u32x4_t*>(vpage + (size_t(tp / E + g) * D + d) * E) = column_piece(vtile + g * E * PITCH + d, PITCH);
   }
 }
 
-// Thread per (token, feature) with the token index fastest, so the transposed V pages are
-// read along their contiguous direction.  Test/debug path; not tuned.
+// Thread per (token, feature).  Test/debug path; not tuned.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool, const T* __restrict__ vpool,
                                                      SegTable tab, int total_pages, int H, int ntok,
                                                      T* __restrict__ kout, T* __restrict__ vout) {
+  constexpr int E = 16 / int(sizeof(T));
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * 64;
   for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
@@ -75,9 +107,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool
       ++s;
     }
     const size_t page = size_t(h) * total_pages + tab.s[s].page + off / SR_PAGE_TOKENS;
-    const int row = off % SR_PAGE_TOKENS;
-    kout[(size_t(t) * H + h) * D + d] = kpool[(page * SR_PAGE_TOKENS + row) * D + d];
-    vout[(size_t(t) * H + h) * D + d] = vpool[(page * D + d) * SR_PAGE_TOKENS + row];
+    const int tp = off % SR_PAGE_TOKENS;
+    const T* kpage = kpool + page * SR_PAGE_TOKENS * D;
+    const T* vpage = vpool + page * SR_PAGE_TOKENS * D;
+    kout[(size_t(t) * H + h) * D + d] = kpage[(size_t(d / E) * SR_PAGE_TOKENS + row_pos<T>(tp)) * E + d % E];
+    vout[(size_t(t) * H + h) * D + d] = vpage[(size_t(tp / E) * D + d) * E + tp % E];
   }
 }
 
@@ -110,7 +144,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
   if (n16 == 0) return hipSuccess;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<uint4*>(p), n16);
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<u32x4_t*>(p), n16);
   return hipGetLastError();
 }
 
@@ -120,8 +154,7 @@ hipError_t launch_append(const Layout& L, void* pool, const void* k, const void*
   if (L.dtype == SR_BF16)
     return L.D == 128 ? append_t<uint16_t, 128>(L, pool, k, v, n, page0, npages, st)
                       : append_t<uint16_t, 64>(L, pool, k, v, n, page0, npages, st);
-  return L.D == 128 ? append_t<float, 128>(L, pool, k, v, n, page0, npages, st)
-                    : append_t<float, 64>(L, pool, k, v, n, page0, npages, st);
+  return append_t<float, 64>(L, pool, k, v, n, page0, npages, st);
 }
 
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
@@ -130,8 +163,7 @@ hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, i
   if (L.dtype == SR_BF16)
     return L.D == 128 ? gather_t<uint16_t, 128>(L, pool, t, ntok, kout, vout, st)
                       : gather_t<uint16_t, 64>(L, pool, t, ntok, kout, vout, st);
-  return L.D == 128 ? gather_t<float, 128>(L, pool, t, ntok, kout, vout, st)
-                    : gather_t<float, 64>(L, pool, t, ntok, kout, vout, st);
+  return gather_t<float, 64>(L, pool, t, ntok, kout, vout, st);
 }
 
 }  // namespace sr

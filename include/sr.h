@@ -63,10 +63,14 @@ typedef enum sr_dtype { SR_BF16 = 0, SR_F32 = 1 } sr_dtype;
 #define SR_PAGE_TOKENS 128
 /* Largest window of history chunks (the segment table is passed to kernels by value). */
 #define SR_MAX_WINDOW 14
+/* Most pages of keys one attention call may visit: sum over the visited segments
+ * (persistent bank, history chunks, current chunk) of ceil(length / SR_PAGE_TOKENS).
+ * sr_chunk_attention returns SR_E_UNSUPPORTED beyond it. */
+#define SR_MAX_VISIBLE_PAGES 1024
 
 typedef struct sr_kvcache_config {
   int32_t num_heads;         /* H >= 1 (batch folded into heads) */
-  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t head_dim;          /* D: 64 or 128 for SR_BF16; 64 for SR_F32 */
   int32_t persistent_tokens; /* P >= 0: reference-image + prompt (+ sink) tokens per bank */
   int32_t num_banks;         /* >= 1: one per denoising step */
   int32_t chunk_capacity;    /* >= 1: most tokens a chunk may have (ring slot size) */
@@ -120,13 +124,17 @@ sr_status sr_ring_destroy(sr_ring* r);
 /* ------------------------------------------------------------------------------------------
  * KV cache (one handle per attention layer).
  *
- * Pool layout in HBM, for each head h, page p (128 tokens), token t, feature d:
- *   K: pool[((h * total_pages + p) * 128 + t) * D + d]                    (key rows)
- *   V: pool[V_off + ((h * total_pages + p) * D + d) * 128 + t]            (value columns)
- * i.e. K pages are token-major and V pages are stored transposed, which is the operand
- * order the attention kernel's matrix instructions read.  Pages are numbered: banks first
- * (ceil(P/128) pages each), then the W+1 ring slots (ceil(capacity/128) pages each).
- * Tokens past a segment's valid length are kept at zero.
+ * Pool layout in HBM.  The K region (half_bytes = bytes / 2) is followed by the V region.
+ * Each region holds, for head h and page p (128 tokens), one page of 128 * D elements at
+ * element offset (h * total_pages + p) * 128 * D.  Inside a page, with E = 16 / element
+ * size (8 for bf16, 4 for fp32), token t (0..127) and feature d:
+ *   K: ((d / E) * 128 + row(t)) * E + d % E
+ *   V: ((t / E) * D + d) * E + t % E
+ * row(t) permutes t inside its block of 32 (bf16: swap bits 2 and 3; fp32: 32-block row
+ * 8*(r/8) + 4*(r%2) + (r/2)%4 for r = t % 32).  This is the order in which the attention
+ * kernel's matrix instructions consume the page, so a page is copied into LDS unchanged.
+ * Pages are numbered: banks first (ceil(P/128) pages each), then the W+1 ring slots
+ * (ceil(capacity/128) pages each).  Tokens past a segment's valid length are kept at zero.
  * ------------------------------------------------------------------------------------------ */
 typedef struct sr_kvcache sr_kvcache;
 
@@ -155,7 +163,8 @@ sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
  * over bank `bank` + history + current (see top of file).  out: device [n][H][D] in the
  * cache dtype.  lse: device fp32 [H][n] natural-log log-sum-exp of the scaled logits, or
  * NULL.  softmax_scale > 0 multiplies q.k (usually 1/sqrt(D)).  SR_E_STATE without a
- * current chunk.  q must not alias out. */
+ * current chunk; SR_E_UNSUPPORTED if the call would visit more than SR_MAX_VISIBLE_PAGES
+ * pages.  q must not alias out. */
 sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
                              float softmax_scale, void* stream);
 

@@ -81,7 +81,7 @@ WORKLOADS = {
     "t_frame": Workload("t_frame", 22, "bf16", 2, 128, 200, 780, 2, 390, 1, 3, 1, 1.0, _SIGMA,
                         boost_fraction=0.01),
     "t_d64": Workload("t_d64", 23, "bf16", 3, 64, 130, 333, 1, 111, 1, 3, 1, 1.0, 1.0),
-    "t_f32": Workload("t_f32", 24, "f32", 2, 128, 70, 200, 2, 200, 1, 4, 1, 1.0, 1.0, single_step=False),
+    "t_f32": Workload("t_f32", 24, "f32", 3, 64, 70, 300, 2, 100, 2, 5, 2, 1.0, 1.0, single_step=False),
 }
 
 

@@ -148,9 +148,9 @@ def test_single_visible_key_is_exact(sr):
     """With causal blocks of one token, no prefix and no history, query 0 sees only key 0:
     its output is V[0] bit for bit, and its lse is its own scaled logit."""
     import torch
-    for dtype in ("bf16", "f32"):
-        cache, mk, _, _ = _one_chunk_cache(sr, 3, 128, 0, 70, 0, 1, dtype, 1)
-        k, v, q = mk(70, 3, 128), mk(70, 3, 128), mk(70, 3, 128)
+    for dtype, D in (("bf16", 128), ("bf16", 64), ("f32", 64)):
+        cache, mk, _, _ = _one_chunk_cache(sr, 3, D, 0, 70, 0, 1, dtype, 1)
+        k, v, q = mk(70, 3, D), mk(70, 3, D), mk(70, 3, D)
         cache.append(5, k, v)
         lse = torch.empty((3, 70), dtype=torch.float32, device="cuda")
         out = cache.attention(0, q, lse=lse, softmax_scale=0.1)
@@ -200,12 +200,19 @@ def test_hidden_data_does_not_matter(sr):
             pool[p0:p0 + pps * 128 * D] = 3.0
     torch.cuda.synchronize()
     assert torch.equal(cache.attention(0, q), ref)
-    # 2) finite garbage in the padding past the current chunk's 333 tokens
+    # 2) finite garbage in the padding past the current chunk's 333 tokens.  Page layout:
+    #    K [D/8][128 rows, permuted in blocks of 32][8], V [128/8][D][8 tokens].
+    def row(t):
+        r = t & 31
+        return (t & ~31) | (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
+    pad = list(range(n % 128, 128))
     for h in range(H):
         kp = (h * total_pages + slot_page(2) + n // 128) * 128 * D
-        pool[kp + (n % 128) * D: kp + 128 * D] = -5.0
-        vp = half + (h * total_pages + slot_page(2) + n // 128) * 128 * D
-        pool[vp:vp + 128 * D].view(D, 128)[:, n % 128:] = 7.0
+        kpage = pool[kp:kp + 128 * D].view(D // 8, 128, 8)
+        kpage[:, [row(t) for t in pad], :] = -5.0
+        vpage = pool[half + kp:half + kp + 128 * D].view(128 // 8, D, 8)
+        for t in pad:
+            vpage[t // 8, :, t % 8] = 7.0
     torch.cuda.synchronize()
     assert torch.equal(cache.attention(0, q), ref)
     # 3) later causal blocks: change keys/values of blocks >= 2 (tokens 260..332)

@@ -51,12 +51,16 @@ def test_required_bytes(sr, H, D, P, banks, cap, W, dt):
 
 
 @pytest.mark.parametrize("field,value,status", [("head_dim", 96, 5), ("head_dim", 0, 5), ("window_chunks", 15, 1),
+                                                ("dtype_f32_d128", None, 5),
                                                 ("window_chunks", -1, 1), ("num_banks", 0, 1), ("num_heads", 0, 1),
                                                 ("chunk_capacity", 0, 1), ("causal_block", 0, 1), ("dtype", 7, 1),
                                                 ("persistent_tokens", -3, 1)])
 def test_config_validation(sr, field, value, status):
     cfg = sr.config_for(4, 128, 100, 300, 2)
-    setattr(cfg, field, value)
+    if field == "dtype_f32_d128":
+        cfg.dtype = sr.SR_F32          # fp32 caches support head_dim 64 only
+    else:
+        setattr(cfg, field, value)
     with pytest.raises(sr.SrError) as e:
         sr.sr_ring_create(cfg)
     assert e.value.status == status
