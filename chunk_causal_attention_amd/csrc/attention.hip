@@ -9,10 +9,11 @@
 // Work decomposition.  One workgroup per (head, tile of BM = NW*QB*32 queries); each wave
 // owns QB blocks of 32 queries for the whole key sequence.  The workgroup walks the key
 // tiles of its segments in visiting order; tiles past the last visible causal block are
-// never loaded.  Each tile (BN keys, one cache page for bf16) is copied straight from HBM
-// into LDS by gfx950's global-to-LDS loads (no staging registers), double buffered, into a
-// dense layout whose 16-byte pieces are XOR-swizzled per row so that the operand reads of
-// a 16-lane group hit distinct banks.
+// never loaded.  Each tile (BN = 128 keys, one cache page) is copied unchanged from HBM
+// into LDS by gfx950's global-to-LDS loads (no staging registers), double buffered.  The
+// cache pages are stored in the order the matrix instructions consume them, so every
+// operand read is one 16-byte piece per lane at a lane base plus a constant offset, and
+// 32 lanes read 512 contiguous bytes (no bank conflicts).
 //
 // Schedule.  Iteration i of the key loop works on 64-key sub-tiles of the cache pages:
 //   [mask sub-tile i if partial]
@@ -25,7 +26,7 @@
 // keys is simply fully masked (its probabilities are zero), so the loop has no other
 // branches.  K and V pages have separate double buffers in LDS; the pages of tile t+2 (K)
 // and t+1 (V) are requested at iteration 2t+1, two iterations before their first use,
-// and one barrier ends every iteration.
+// and a barrier ends every even iteration (one per page).
 //
 // Matrix instructions (32x32 output tile).  Scores are computed transposed, S^T = K . Q^T:
 // the key block is the A operand, the queries are the B operand held in registers for the
@@ -538,6 +539,8 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
 
   for (int i = 0; i <= nsub; ++i) {
     const int t = i >> 1;
+    // The SIMD favours the older of its two waves (w and w+4); swapping their priorities
+    // every iteration lets them reach each barrier together.
     // Page requests: at iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in
     // iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read in iteration 2t).
     if (i & 1) {
@@ -587,9 +590,13 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     ent = ent_next;
 
     // V of tile t+1 and K of tile t+2 are first read in iteration 2t+3: wait at the end of
-    // the even iteration 2t+2 (they were requested at 2t+1, nothing later).
-    if ((i & 1) == 0 && i >= 2) wait_loads<0>();
-    __syncthreads();
+    // the even iteration 2t+2 (they were requested at 2t+1, nothing later).  Only even
+    // iterations end with a barrier: it publishes those pages and releases the buffers that
+    // iteration 2t+3 overwrites (last read in 2t+2).
+    if ((i & 1) == 0) {
+      if (i >= 2) wait_loads<0>();
+      __syncthreads();
+    }
   }
 
   // Epilogue: O = O^T / l, written token-major; lse = (max + log2 l) * ln 2.
