@@ -127,8 +127,10 @@ def run(args):
 
     t_init = time.perf_counter()
     layers = []
+    # One attention workspace serves every layer cache: their calls are ordered on one stream.
+    ws = None if args.no_split else sr.workspace_for(cfg)
     for _ in range(args.layers):
-        c = sr.KVCache(cfg, pk, pv)
+        c = sr.KVCache(cfg, pk, pv, workspace=ws)
         for j in range(w.window + 1):
             k, v, _ = sets[j % len(sets)]
             c.append(j, k, v)
@@ -195,6 +197,7 @@ def run(args):
                         f"{w.window}x{w.chunk} history + {w.chunk} current tokens, causal block {w.causal_block}",
             "heads": w.heads, "head_dim": w.head_dim, "queries": w.chunk, "keys_visible": w.visible_keys,
             "layers_cycled": args.layers, "step": "evict + append_chunk + chunk_attention",
+            "schedule": "whole items" if args.no_split else "key tiles split evenly over the CUs",
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -236,6 +239,8 @@ def main():
     ap.add_argument("--workload", default="c1", help="c1 (default), c3, c4, c1s, c4s or c2")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-split", action="store_true",
+                    help="run attention without a workspace (one workgroup per head and query tile)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (whole heads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference for the profiler's byte counters)")

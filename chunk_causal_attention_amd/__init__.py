@@ -14,6 +14,7 @@ __all__ = [
     "SrError", "sr_kvcache_config", "sr_segment", "load", "build", "config_for",
     "sr_kvcache_required_bytes", "sr_kvcache_init", "sr_kvcache_append_chunk", "sr_kvcache_evict",
     "sr_chunk_attention", "sr_kvcache_gather", "sr_kvcache_ring", "sr_kvcache_destroy",
+    "sr_attention_workspace_bytes", "sr_kvcache_set_workspace", "workspace_for",
     "sr_ring_create", "sr_ring_append", "sr_ring_evict", "sr_ring_segments", "sr_ring_destroy",
     "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "PAGE_TOKENS", "MAX_WINDOW",
 ]
@@ -76,6 +77,8 @@ def load():
         "sr_chunk_attention": [P, I32, P, P, P, F32, P],
         "sr_kvcache_gather": [P, I32, P, P, I32, ctypes.POINTER(I32), P],
         "sr_kvcache_destroy": [P],
+        "sr_attention_workspace_bytes": [cfgp, I32, ctypes.POINTER(SZ)],
+        "sr_kvcache_set_workspace": [P, P, SZ, P],
         "sr_ring_create": [cfgp, ctypes.POINTER(P)],
         "sr_ring_append": [P, I64, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)],
         "sr_ring_evict": [P, ctypes.POINTER(I64)],
@@ -166,6 +169,26 @@ def sr_kvcache_gather(h, bank, k_out, v_out, stream=None):
     return n.value
 
 
+def sr_attention_workspace_bytes(cfg, num_workgroups=0):
+    n = ctypes.c_size_t()
+    _check(load().sr_attention_workspace_bytes(ctypes.byref(cfg), num_workgroups, ctypes.byref(n)))
+    return n.value
+
+
+def sr_kvcache_set_workspace(h, ws, stream=None):
+    """Attach device tensor `ws` (uint8, 256-byte aligned) as the attention workspace; None detaches."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().sr_kvcache_set_workspace(h, _ptr(ws), nbytes, _stream(stream)))
+
+
+def workspace_for(*cfgs, device="cuda"):
+    """A workspace tensor large enough for caches of every config in `cfgs` (shareable by
+    caches whose attention calls are ordered on one stream)."""
+    import torch
+    n = max(sr_attention_workspace_bytes(c) for c in cfgs)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def sr_kvcache_ring(h):
     return ctypes.c_void_p(load().sr_kvcache_ring(h))
 
@@ -204,11 +227,17 @@ def sr_ring_destroy(r):
 
 
 class KVCache:
-    """Owns a pool tensor and a cache handle; methods call the C ABI on the current stream."""
+    """Owns a pool tensor and a cache handle; methods call the C ABI on the current stream.
 
-    def __init__(self, cfg, persistent_k=None, persistent_v=None, device="cuda", stream=None):
+    workspace: "own" (default) allocates and attaches a workspace for this cache, so the
+    attention call splits its key tiles evenly over the device; a uint8 device tensor
+    (e.g. from workspace_for) attaches a shared one; None runs without a workspace.
+    """
+
+    def __init__(self, cfg, persistent_k=None, persistent_v=None, device="cuda", stream=None, workspace="own"):
         import torch
         self.cfg = cfg
+        self.h = None
         self.dtype = torch.bfloat16 if cfg.dtype == SR_BF16 else torch.float32
         self.bytes = sr_kvcache_required_bytes(cfg)
         self.pool = torch.empty(self.bytes, dtype=torch.uint8, device=device)
@@ -216,6 +245,16 @@ class KVCache:
             if t is not None:
                 self._check_tensor(t, (cfg.num_banks, cfg.persistent_tokens, cfg.num_heads, cfg.head_dim))
         self.h = sr_kvcache_init(cfg, self.pool, persistent_k, persistent_v, stream)
+        self.workspace = None
+        if isinstance(workspace, str):
+            if workspace != "own":
+                raise ValueError('workspace must be "own", None or a device tensor')
+            workspace = workspace_for(cfg, device=device)
+        self.set_workspace(workspace, stream)
+
+    def set_workspace(self, workspace, stream=None):
+        sr_kvcache_set_workspace(self.h, workspace, stream)
+        self.workspace = workspace
 
     def _check_tensor(self, t, shape=None):
         if t.dtype != self.dtype or not t.is_cuda or not t.is_contiguous():

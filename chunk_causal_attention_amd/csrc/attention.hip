@@ -149,8 +149,17 @@ struct AttnArgs {
   int32_t n_q, H, total_pages, causal_block;
   int32_t q_tiles, num_wg;
   float scale_log2;
+  int32_t split;           // 0: one workgroup per item; 1: the split schedule (xcd_plan)
+  int32_t fixed_tiles;     // pages of the bank and history segments
+  int32_t n_items;         // H * q_tiles (head, query tile) items, head-major
+  int32_t cus_per_xcd;     // split: C, compute units per XCD
+  float* rec;              // split: 4C partial records per XCD
+  int32_t* cnt;            // split: C arrival counters per XCD (zero between calls)
   SegTable t;
+  XcdPlan plan[8];                          // split: xcd_plan of each XCD
+  int16_t left_tiles[8][kMaxCusPerXcd];     // split: key tiles of each XCD's split items
 };
+static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Geometry of one kernel instantiation: one LDS tile = one cache page = 2 sub-tiles.
 template <typename T, int D_, int QB_, int NW_>
@@ -174,6 +183,9 @@ struct Geo {
   static constexpr int LOADS = KTILE / 1024 / NW;  // 1 KiB global-to-LDS loads per wave, per page
   static_assert(LOADS * NW * 1024 == KTILE, "page loads must split evenly");
   static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
+  static constexpr int RPL = QB * (NDB * 16 + 2);  // record floats per lane: O^T, max, sum
+  static constexpr int REC = NW * 64 * RPL;        // record floats per workgroup
+  static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -199,7 +211,8 @@ __device__ __forceinline__ void issue_page(const char* src, char* dst, int wave,
   }
 }
 
-// s_waitcnt vmcnt(N): at most N of this wave's global(-to-LDS) loads still outstanding.
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations (global loads,
+// global-to-LDS loads, stores) still outstanding.
 // Inline asm as well: the compiler does not see the page loads and would drop a builtin
 // wait that it considers redundant.
 template <int N>
@@ -428,31 +441,125 @@ __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>
   st.l[0] += lsum;
 }
 
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = uint64_t(x);
+  return int64_t((uint64_t(uint32_t(uniform(int(u >> 32)))) << 32) | uint32_t(uniform(int(uint32_t(u)))));
+}
+
+// A split item as the merge sees it: XCD x, index r among the XCD's split items, its tile
+// count, and the XCD's plan (xcd_plan in kernels.hpp).
+struct SplitItem {
+  int x, r, tiles;
+  XcdPlan plan;
+};
+
+// Key tiles of split item r of XCD x (item_tiles of its query tile, computed on the host).
+__device__ __forceinline__ int split_item_tiles(const AttnArgs& a, int x, int r) { return a.left_tiles[x][r]; }
+
+// Calls f(slot) for every piece of split item `it` in slot order; returns their count (0: the
+// item runs whole on its band-0 workgroup).
+template <class F>
+__device__ __forceinline__ int for_each_subpiece(const AttnArgs& a, const SplitItem& it, int C, F&& f) {
+  const XcdPlan& p = it.plan;
+  if (it.tiles <= p.b) return 0;
+  const int base = it.x * 4 * C;
+  f(base + 2 * it.r);  // band 0
+  int start = 0;       // band-1 layout offset of the item
+  for (int rr = 0; rr < it.r; ++rr) start += band1_len(split_item_tiles(a, it.x, rr), p.b);
+  const int len = it.tiles - p.b;
+  f(base + 2 * C + 2 * it.r);
+  if (start / p.s != (start + len - 1) / p.s) {  // cut by a workgroup boundary
+    f(base + 2 * C + 2 * it.r + 1);
+    return 3;
+  }
+  return 2;
+}
+
+// Records are written and read with device-scope (agent) relaxed atomic stores and loads,
+// which gfx950 performs at the device's coherence point without touching other data in the
+// XCD's L2.  Ordering: every wave waits for its record stores to complete (vmcnt 0) before
+// the workgroup barrier that precedes the arrival counter update, and the merging workgroup
+// loads records only after its counter update returned.  Release/acquire fences at device
+// scope would instead write back and invalidate the whole L2 of the XCD, dropping the key
+// pages every other workgroup there is streaming.
+__device__ __forceinline__ void rec_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float rec_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Record layout: lane-major, float j of lane (wave, lane) at (wave * RPL + j) * 64 + lane,
+// so every store and load of a record is a coalesced 256-byte row per wave.
 template <class G>
-__global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(const AttnArgs a) {
+__device__ __forceinline__ void store_record(float* rec, const RowState<G>& st, int wave, int lane) {
+  float* p = rec + size_t(wave) * G::RPL * 64 + lane;
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) {
+    float* q = p + qb * (G::NDB * 16 + 2) * 64;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rec_store(q + (db * 16 + e) * 64, st.acc[qb][db][e]);
+    rec_store(q + (G::NDB * 16) * 64, st.m[qb]);
+    rec_store(q + (G::NDB * 16 + 1) * 64, st.l[qb]);
+  }
+}
+
+// Merges the records of a split item's sub-pieces: O^T and l of each rescaled to the common
+// max, summed in (band, sub) order.
+template <class G>
+__device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int wave,
+                                              int lane) {
+  const int C = a.cus_per_xcd;
+  const size_t lane_off = size_t(wave) * G::RPL * 64 + lane;
+  float mx[G::QB];
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) mx[qb] = kMaxInit;
+  for_each_subpiece(a, it, C, [&](int slot) {
+    const float* p = a.rec + size_t(slot) * G::REC + lane_off;
+#pragma unroll
+    for (int qb = 0; qb < G::QB; ++qb) mx[qb] = fmaxf(mx[qb], rec_load(p + (qb * (G::NDB * 16 + 2) + G::NDB * 16) * 64));
+  });
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb) {
+    st.m[qb] = mx[qb];
+    st.l[qb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] = f32x16_t{};
+  }
+  for_each_subpiece(a, it, C, [&](int slot) {
+    const float* p = a.rec + size_t(slot) * G::REC + lane_off;
+#pragma unroll
+    for (int qb = 0; qb < G::QB; ++qb) {
+      const float* q = p + qb * (G::NDB * 16 + 2) * 64;
+      const float alpha = __builtin_amdgcn_exp2f(rec_load(q + (G::NDB * 16) * 64) - mx[qb]);
+      st.l[qb] += alpha * rec_load(q + (G::NDB * 16 + 1) * 64);
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.acc[qb][db][e] += alpha * rec_load(q + (db * 16 + e) * 64);
+    }
+  });
+}
+
+// One piece of work: query tile qt of head h over tiles [tb, te) of its tile list.  slot < 0:
+// the whole list (write the output); else a sub-piece of split item `it` (record `slot`).
+template <class G>
+__device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* flag, int h, int qt, int tb, int te,
+                                          int slot, const SplitItem& it) {
   using M = typename G::M;
   using Op = typename G::Op;
   using T = typename G::Elem;
   constexpr int BN = G::BN, SUB = G::SUB, D = G::D;
-  __shared__ __align__(1024) char smem[G::LDS_BYTES];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);
   const int c = lane & 31, hl = lane >> 5;
-
-  // Workgroups are dispatched round-robin over the 8 XCDs (hardware id i runs on XCD i % 8).
-  // Renumber so each XCD gets a contiguous range of (head, query tile): the query tiles of a
-  // head then share that XCD's L2 while they stream the same keys.
-  const int nwg = a.num_wg, bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3, per = nwg >> 3, rem = nwg & 7;
-  const int wg = local + xcd * per + (xcd < rem ? xcd : rem);
-  // Integer divisions are expanded on the vector ALU; readfirstlane tells the compiler the
-  // results are wave-uniform so the tile loop stays a scalar loop.
-  const int h = uniform(wg / a.q_tiles);
-  const int q0 = uniform((wg - h * a.q_tiles) * G::BM);
+  const int q0 = qt * G::BM;
   const int n_q = a.n_q, H = a.H, cb = a.causal_block;
   const int cur = a.t.n - 1;
   const int cur_len = a.t.s[cur].len;
+  __syncthreads();  // the previous piece of this workgroup is done with LDS
 
   // Query operands (B operand of K.Q^T), resident for the whole kernel.
   Op qop[G::QB][G::KSTEPS];
@@ -475,9 +582,7 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   const int qlast = min(q0 + G::BM, n_q) - 1;
   const int cur_all = uniform(min(cur_len, (q0 / cb + 1) * cb));
   const int cur_any = uniform(min(cur_len, (qlast / cb + 1) * cb));
-  int ntiles = (cur_any + BN - 1) / BN;
-  for (int s = 0; s < cur; ++s) ntiles += (a.t.s[s].len + BN - 1) / BN;
-  ntiles = uniform(ntiles);
+  const int ntiles = te - tb;  // tiles [tb, te) of the item's tile list
 
   RowState<G> st;
 #pragma unroll
@@ -490,12 +595,12 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
 
   const size_t head_page = size_t(h) * a.total_pages;
 
-  // Tile table, built once per workgroup: for tile t (visiting order) the page index
-  // (relative to the head's first page), the key offset inside the current chunk (-1 for
-  // the persistent bank and history), and the keys of the tile visible to some / to every
-  // query of the workgroup (relative to the tile start; <= 0 past them).
+  // Tile table of the piece: for tile t (visiting order) the page index (relative to the
+  // head's first page), the key offset inside the current chunk (-1 for the persistent bank
+  // and history), and the keys of the tile visible to some / to every query of the
+  // workgroup (relative to the tile start; <= 0 past them).  Entry t - tb holds tile t.
   int4* tab = reinterpret_cast<int4*>(smem + G::TABLE);
-  for (int t = tid; t < ntiles; t += G::NW * 64) {
+  for (int t = tb + tid; t < te; t += G::NW * 64) {
     int s = 0, first = 0;
     for (; s < cur; ++s) {
       const int nt = (a.t.s[s].len + BN - 1) / BN;
@@ -505,8 +610,8 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     const int k0 = (t - first) * BN;
     const bool is_cur = s == cur;
     const int len = a.t.s[s].len;
-    tab[t] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
-                       (is_cur ? cur_all : len) - k0);
+    tab[t - tb] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
+                            (is_cur ? cur_all : len) - k0);
   }
   __syncthreads();
   auto tile_page = [&](int t) { return (head_page + uniform(tab[t].x)) * G::KTILE; };
@@ -539,8 +644,6 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
 
   for (int i = 0; i <= nsub; ++i) {
     const int t = i >> 1;
-    // The SIMD favours the older of its two waves (w and w+4); swapping their priorities
-    // every iteration lets them reach each barrier together.
     // Page requests: at iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in
     // iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read in iteration 2t).
     if (i & 1) {
@@ -599,6 +702,26 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     }
   }
 
+  // A piece of a split item leaves its partial result in its record; the last of the item's
+  // pieces to arrive merges all of them (in piece order, so the result does not depend on
+  // which piece came last) and writes the output.  Nobody waits for anybody.
+  if (slot >= 0) {
+    store_record<G>(a.rec + size_t(slot) * G::REC, st, wave, lane);
+    wait_loads<0>();  // this wave's record stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      int32_t* cnt = a.cnt + it.x * a.cus_per_xcd + it.r;
+      const int pieces = for_each_subpiece(a, it, a.cus_per_xcd, [](int) {});
+      const int arrived = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = arrived == pieces - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (*flag == 0) return;
+    merge_records<G>(a, st, it, wave, lane);
+  }
+
   // Epilogue: O = O^T / l, written token-major; lse = (max + log2 l) * ln 2.
   T* __restrict__ og = static_cast<T*>(a.o);
 #pragma unroll
@@ -622,10 +745,111 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   }
 }
 
+__device__ __forceinline__ XcdPlan uniform_plan(const XcdPlan& p) {
+  XcdPlan q;
+  q.first = uniform(p.first);
+  q.whole = uniform(p.whole);
+  q.left = uniform(p.left);
+  q.b = uniform(p.b);
+  q.s = uniform(p.s);
+  q.u1 = uniform(p.u1);
+  q.wgs = uniform(p.wgs);
+  return q;
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(const AttnArgs a) {
+  __shared__ __align__(1024) char smem[G::LDS_BYTES];
+  __shared__ int flag;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs: hardware id i runs on XCD i % 8
+  // as the (i / 8)-th workgroup of that XCD.  Integer divisions are expanded on the vector
+  // ALU; readfirstlane keeps every loop bound and branch scalar.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+
+  // The workgroup's first piece; band-1 workgroups then walk further pieces.
+  int h = 0, qt = 0, tb = 0, te = 0, slot = -1;
+  SplitItem it{};
+  bool band1 = false;
+  XcdPlan p{};
+  int r = 0, pos = 0, end = 0, base = 0;  // band-1 walk; base: layout offset of item r's piece
+  if (!a.split) {
+    // One workgroup per item, renumbered so each XCD gets a contiguous range of items: the
+    // query tiles of a head then share that XCD's L2 while they stream the same keys.
+    const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
+    const int g = local + xcd * per + (xcd < rem ? xcd : rem);
+    h = uniform(g / a.q_tiles);
+    qt = uniform(g - h * a.q_tiles);
+    te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block));
+  } else {
+    p = uniform_plan(a.plan[xcd]);
+    if (local < p.whole) {
+      const int item = p.first + local;
+      h = uniform(item / a.q_tiles);
+      qt = uniform(item - h * a.q_tiles);
+      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block));
+    } else {
+      const int j = local - p.whole;
+      if (j >= p.wgs) return;
+      if (j < p.left) {
+        // Band 0 of split item j: tiles [0, min(b, T)); the whole item if T <= b.
+        r = j;
+        const int tiles = split_item_tiles(a, xcd, r);
+        const int item = p.first + p.whole + r;
+        h = uniform(item / a.q_tiles);
+        qt = uniform(item - h * a.q_tiles);
+        te = tiles < p.b ? tiles : p.b;
+        if (tiles > p.b) {
+          slot = xcd * 4 * a.cus_per_xcd + 2 * r;
+          it = SplitItem{xcd, r, tiles, p};
+        }
+      } else {
+        // Band-1 workgroup q: units [q s, (q+1) s) of the band-1 layout.
+        band1 = true;
+        const int q = j - p.left;
+        pos = q * p.s;
+        end = pos + p.s < p.u1 ? pos + p.s : p.u1;
+        for (; r < p.left; ++r) {
+          const int len = band1_len(split_item_tiles(a, xcd, r), p.b);
+          if (pos < base + len) break;
+          base += len;
+        }
+      }
+    }
+  }
+
+  // The bound on r only guards against a malformed plan; a valid one never reaches it.
+  for (;;) {
+    int e = 0, len = 0;
+    if (band1) {
+      if (r >= p.left) break;
+      const int tiles = split_item_tiles(a, xcd, r);
+      len = band1_len(tiles, p.b);
+      e = end < base + len ? end : base + len;
+      tb = p.b + (pos - base);
+      te = tb + (e - pos);
+      const int sub = pos > base ? 1 : 0;  // only a workgroup's first piece can start mid-piece
+      const int item = p.first + p.whole + r;
+      h = uniform(item / a.q_tiles);
+      qt = uniform(item - h * a.q_tiles);
+      slot = xcd * 4 * a.cus_per_xcd + 2 * a.cus_per_xcd + 2 * r + sub;
+      it = SplitItem{xcd, r, tiles, p};
+    }
+    run_piece<G>(a, smem, &flag, h, qt, tb, te, slot, it);
+    if (!band1) break;
+    pos = e;
+    if (pos >= end) break;
+    base += len;
+    for (++r; r < p.left && band1_len(split_item_tiles(a, xcd, r), p.b) == 0;) ++r;
+  }
+}
+
 template <class G>
 hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                    float scale, hipStream_t st) {
-  AttnArgs a;
+                    float scale, const SplitWorkspace& ws, hipStream_t st) {
+  static_assert(SR_MAX_VISIBLE_PAGES <= 32767, "tile counts are stored as int16");
+  AttnArgs a{};
   a.q = q;
   a.o = o;
   a.lse = lse;
@@ -636,8 +860,27 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
   a.total_pages = L.total_pages;
   a.causal_block = L.cb;
   a.q_tiles = (a.n_q + G::BM - 1) / G::BM;
-  a.num_wg = a.q_tiles * L.H;
   a.scale_log2 = scale * kLog2e;
+  a.fixed_tiles = 0;
+  for (int s = 0; s + 1 < t.n; ++s) a.fixed_tiles += (t.s[s].len + G::BN - 1) / G::BN;
+  a.n_items = a.q_tiles * L.H;
+  a.split = ws.cus_per_xcd > 0 ? 1 : 0;
+  a.cus_per_xcd = ws.cus_per_xcd;
+  a.rec = ws.records;
+  a.cnt = ws.counters;
+  if (a.split) {
+    // Per-XCD plans and split items' tile counts; 8 XCDs x the largest per-XCD count of
+    // whole items + split workgroups.
+    int32_t per = 0;
+    for (int x = 0; x < 8; ++x) {
+      const XcdPlan p = xcd_plan(x, a.n_items, a.q_tiles, a.fixed_tiles, a.n_q, L.cb, ws.cus_per_xcd, a.left_tiles[x]);
+      a.plan[x] = p;
+      per = p.whole + p.wgs > per ? p.whole + p.wgs : per;
+    }
+    a.num_wg = 8 * per;
+  } else {
+    a.num_wg = a.n_items;
+  }
   a.t = t;
   hipLaunchKernelGGL((chunk_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
   return hipGetLastError();
@@ -646,13 +889,13 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
 }  // namespace
 
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                            float softmax_scale, hipStream_t st) {
+                            float softmax_scale, const SplitWorkspace& ws, hipStream_t st) {
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st)
-                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st);
+    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st)
+                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st);
   // fp32 caches are head_dim 64 only (validated on the host): a double-buffered 128-key
   // fp32 tile at head_dim 128 would need 256 KiB of LDS.
-  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, st);
+  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st);
 }
 
 }  // namespace sr

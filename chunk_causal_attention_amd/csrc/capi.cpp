@@ -11,6 +11,9 @@
 struct sr_kvcache {
   sr_ring ring;
   char* pool = nullptr;
+  int32_t num_cus = 0;        // compute units of the device the cache was created on
+  sr::SplitWorkspace split;   // grid 0: no workspace attached
+  size_t ws_bytes = 0;
 };
 
 namespace {
@@ -38,6 +41,16 @@ sr::SegTable make_table(const sr_ring& r, int32_t bank, int32_t* total) {
 
 bool pool_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+sr_status device_cus(int32_t* n) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_status(e, "device query");
+  if (cus <= 0) return sr::fail(SR_E_DEVICE, "device reports %d compute units", cus);
+  *n = cus;
+  return SR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,10 +67,14 @@ sr_status sr_kvcache_init(const sr_kvcache_config* cfg, void* pool, size_t pool_
     return sr::fail(SR_E_NOMEM, "pool has %zu bytes, the layout needs %zu", pool_bytes, L.bytes);
   if (L.P > 0 && (!persistent_k || !persistent_v || !sr::aligned16(persistent_k) || !sr::aligned16(persistent_v)))
     return sr::fail(SR_E_INVALID, "persistent K/V must be non-null and 16-byte aligned when persistent_tokens > 0");
+  int32_t cus = 0;
+  st = device_cus(&cus);
+  if (st != SR_OK) return st;
   sr_kvcache* c = new (std::nothrow) sr_kvcache;
   if (!c) return sr::fail(SR_E_NOMEM, "host allocation failed");
   c->ring.L = L;
   c->pool = static_cast<char*>(pool);
+  c->num_cus = cus;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = device_status(sr::launch_zero(pool, L.bytes, s), "pool zero");
   const size_t bank_elems = size_t(L.P) * L.H * L.D;
@@ -118,8 +135,48 @@ sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* o
   if (pages > SR_MAX_VISIBLE_PAGES)
     return sr::fail(SR_E_UNSUPPORTED, "the call visits %d pages of keys, more than %d", pages, SR_MAX_VISIBLE_PAGES);
   return device_status(
-      sr::launch_attention(L, c->pool, t, q, out, lse, softmax_scale, static_cast<hipStream_t>(stream)),
+      sr::launch_attention(L, c->pool, t, q, out, lse, softmax_scale, c->split, static_cast<hipStream_t>(stream)),
       "chunk attention");
+}
+
+sr_status sr_attention_workspace_bytes(const sr_kvcache_config* cfg, int32_t num_workgroups, size_t* bytes) {
+  sr::clear_error();
+  if (!bytes) return sr::fail(SR_E_INVALID, "null output pointer");
+  sr::Layout L;
+  sr_status st = sr::make_layout(cfg, &L);
+  if (st != SR_OK) return st;
+  if (num_workgroups < 0) return sr::fail(SR_E_INVALID, "num_workgroups must be >= 0");
+  if (num_workgroups == 0) {
+    st = device_cus(&num_workgroups);
+    if (st != SR_OK) return st;
+  }
+  *bytes = sr::attn_records_bytes(L.D, num_workgroups) + sr::attn_counters_bytes(num_workgroups);
+  return SR_OK;
+}
+
+sr_status sr_kvcache_set_workspace(sr_kvcache* c, void* ws, size_t ws_bytes, void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!ws) {
+    c->split = sr::SplitWorkspace{};
+    c->ws_bytes = 0;
+    return SR_OK;
+  }
+  if (!pool_aligned(ws)) return sr::fail(SR_E_INVALID, "workspace must be 256-byte aligned");
+  const sr::Layout& L = c->ring.L;
+  const size_t rec = sr::attn_records_bytes(L.D, c->num_cus);
+  const size_t need = rec + sr::attn_counters_bytes(c->num_cus);
+  if (ws_bytes < need) return sr::fail(SR_E_NOMEM, "workspace has %zu bytes, the cache needs %zu", ws_bytes, need);
+  char* base = static_cast<char*>(ws);
+  // Counters start at zero; every attention call leaves them at zero again.
+  sr_status st = device_status(sr::launch_zero(base + rec, need - rec, static_cast<hipStream_t>(stream)),
+                               "workspace zero");
+  if (st != SR_OK) return st;
+  c->split.cus_per_xcd = sr::split_cus_per_xcd(c->num_cus);
+  c->split.records = reinterpret_cast<float*>(base);
+  c->split.counters = reinterpret_cast<int32_t*>(base + rec);
+  c->ws_bytes = ws_bytes;
+  return SR_OK;
 }
 
 sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void* v_out, int32_t max_tokens,

@@ -24,6 +24,141 @@ struct SegTable {
   DevSeg s[kMaxSegs];
 };
 
+// Queries per workgroup of the attention kernel (8 waves x 32 queries).
+constexpr int kQueryTile = 256;
+
+// Key tiles (cache pages) that query tile `qt` visits: every page of the bank and history
+// segments (`fixed_tiles`) plus the current chunk's pages up to the last causal block that
+// one of the tile's queries can see.  n_q is the current chunk's length.
+__host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, int32_t n_q, int32_t cb) {
+  const int32_t end = (qt + 1) * kQueryTile < n_q ? (qt + 1) * kQueryTile : n_q;
+  const int32_t blocks_end = ((end - 1) / cb + 1) * cb;
+  const int32_t any = blocks_end < n_q ? blocks_end : n_q;
+  return fixed_tiles + (any + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+}
+
+// Floats of one workgroup's partial result in the split schedule: per lane of the 8 waves,
+// the head_dim/2 output accumulators it holds plus its running max and sum.
+__host__ __device__ constexpr int32_t attn_record_floats(int32_t head_dim) { return 8 * 64 * (head_dim / 2 + 2); }
+
+// Split schedule.  Workgroup i of a launch runs on XCD i % 8 as that XCD's (i / 8)-th
+// workgroup, and each XCD (own L2, C compute units) gets a contiguous range of the head-major
+// (head, query tile) items.  An XCD runs its items whole, C at a time: the query tiles of a
+// head then stream the same pages at the same time, so each page is fetched past L2 about
+// once per XCD.  The last `left` < C items of an XCD would leave units idle in a final round;
+// instead, split workgroup r < left runs tiles [0, min(b, T_r)) of split item r ("band 0"),
+// and the remaining tiles [b, T_r) of all split items, laid out one item after the other
+// ("band 1"), are dealt in runs of s tiles to the other split workgroups.  Band-0 workgroups
+// stream the same pages together, and so do band-1 workgroups.  A band-1 piece is at most s
+// long (the plan guarantees it), so it is cut by at most one workgroup boundary: sub-piece 0
+// and possibly 1.  Every piece of a split item leaves a partial record, in slot
+// x * 4C + 2r (band 0) or x * 4C + 2C + 2r + sub (band 1); the last piece of an item to
+// finish merges the item's records in slot order and writes its output.
+constexpr int32_t kPieceOverheadTiles = 4;  // measured cost of starting and ending a piece
+constexpr int32_t kMaxCusPerXcd = 64;       // largest C (split items per XCD are fewer)
+
+struct XcdPlan {
+  int32_t first;  // first item of the XCD
+  int32_t whole;  // items run whole (a multiple of C, or 0)
+  int32_t left;   // split items (< C), items first + whole ...
+  int32_t b;      // band-0 width
+  int32_t s;      // band-1 tiles per workgroup (0: no band 1)
+  int32_t u1;     // band-1 tiles in all
+  int32_t wgs;    // split workgroups: left band-0 + ceil(u1 / s) band-1
+};
+
+__host__ __device__ inline int32_t band1_len(int32_t t, int32_t b) { return t > b ? t - b : 0; }
+
+// Estimated duration (tiles, plus kPieceOverheadTiles per piece) of the split round of an
+// XCD for band-0 width b; -1 if band 1 would need a run shorter than one of its pieces.
+inline int32_t split_estimate(const int16_t* T, int32_t left, int32_t C, int32_t b, int32_t* s_out, int32_t* u1_out) {
+  int32_t u1 = 0, maxlen = 0, band0 = 0;
+  for (int32_t r = 0; r < left; ++r) {
+    const int32_t l1 = band1_len(T[r], b);
+    u1 += l1;
+    maxlen = l1 > maxlen ? l1 : maxlen;
+    const int32_t l0 = T[r] < b ? T[r] : b;
+    band0 = l0 > band0 ? l0 : band0;
+  }
+  *u1_out = u1;
+  *s_out = 0;
+  int32_t worst = band0 + kPieceOverheadTiles;
+  if (u1 == 0) return worst;
+  const int32_t s = (u1 + (C - left) - 1) / (C - left);
+  if (s < maxlen) return -1;
+  *s_out = s;
+  // Pieces overlapping each run [q s, (q+1) s): two pointers over the band-1 pieces.
+  int32_t i = 0, start = 0;  // piece i starts at unit `start`
+  for (int32_t lo = 0; lo < u1; lo += s) {
+    const int32_t hi = lo + s < u1 ? lo + s : u1;
+    while (i < left && start + band1_len(T[i], b) <= lo) start += band1_len(T[i++], b);
+    int32_t n = 0;
+    for (int32_t k = i, a = start; k < left && a < hi; a += band1_len(T[k++], b)) n += band1_len(T[k], b) > 0;
+    const int32_t w = (hi - lo) + n * kPieceOverheadTiles;
+    worst = w > worst ? w : worst;
+  }
+  return worst;
+}
+
+// Plan of XCD x; T receives the tile counts of its split items.
+inline XcdPlan xcd_plan(int32_t x, int32_t n_items, int32_t q_tiles, int32_t fixed_tiles, int32_t n_q, int32_t cb,
+                        int32_t C, int16_t* T) {
+  XcdPlan p{};
+  p.first = int32_t(int64_t(x) * n_items / 8);
+  const int32_t n = int32_t(int64_t(x + 1) * n_items / 8) - p.first;
+  p.left = n % C;
+  p.whole = n - p.left;
+  if (p.left == 0) return p;
+  int32_t tmax = 0;
+  for (int32_t r = 0; r < p.left; ++r) {
+    T[r] = int16_t(item_tiles((p.first + p.whole + r) % q_tiles, fixed_tiles, n_q, cb));
+    tmax = T[r] > tmax ? T[r] : tmax;
+  }
+  // Best b: every stride-th candidate, then the neighbours of the best one.
+  int32_t best = -1, best_b = tmax;
+  auto consider = [&](int32_t b) {
+    if (b < 1 || b > tmax) return;
+    int32_t s, u1;
+    const int32_t e = split_estimate(T, p.left, C, b, &s, &u1);
+    if (e >= 0 && (best < 0 || e < best || (e == best && b > best_b))) {
+      best = e;
+      best_b = b;
+    }
+  };
+  const int32_t stride = tmax / 64 > 1 ? tmax / 64 : 1;
+  for (int32_t b = 1; b <= tmax; b += stride) consider(b);
+  consider(tmax);
+  for (int32_t d = -stride; d <= stride; ++d) consider(best_b + d);
+  // Split only if it saves at least 1/16 of running the items whole.
+  const int32_t whole_cost = tmax + kPieceOverheadTiles / 2;
+  if (best < 0 || best > whole_cost - (whole_cost >> 4)) best_b = tmax;
+  p.b = best_b;
+  split_estimate(T, p.left, C, p.b, &p.s, &p.u1);
+  p.wgs = p.left + (p.u1 > 0 ? (p.u1 + p.s - 1) / p.s : 0);
+  return p;
+}
+
+// C of the split schedule for a device with num_cus compute units.
+inline int32_t split_cus_per_xcd(int32_t num_cus) {
+  const int32_t C = num_cus / 8;
+  return C < 1 ? 1 : (C > kMaxCusPerXcd ? kMaxCusPerXcd : C);
+}
+
+// Attention workspace: 8 XCDs x 4C records, then 8C arrival counters (256-byte aligned).
+inline size_t attn_records_bytes(int32_t head_dim, int32_t num_cus) {
+  return size_t(8) * 4 * split_cus_per_xcd(num_cus) * attn_record_floats(head_dim) * sizeof(float);
+}
+inline size_t attn_counters_bytes(int32_t num_cus) {
+  return (size_t(8) * split_cus_per_xcd(num_cus) * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+// Split schedule of one call (see launch_attention): the XCD width and where partial results go.
+struct SplitWorkspace {
+  int32_t cus_per_xcd = 0;      // 0 = one workgroup per (head, query tile), no workspace
+  float* records = nullptr;
+  int32_t* counters = nullptr;  // zero between calls
+};
+
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 // Copies n tokens of K/V ([n][H][D], token-major) into pages [page0, page0 + npages) of
@@ -35,8 +170,9 @@ hipError_t launch_append(const Layout& L, void* pool, const void* k, const void*
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
                          hipStream_t st);
 
-// Chunk attention of the current chunk's queries over the segments of `t`.
+// Chunk attention of the current chunk's queries over the segments of `t`.  With
+// ws.cus_per_xcd > 0 the split schedule (xcd_plan) is used.
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                            float softmax_scale, hipStream_t st);
+                            float softmax_scale, const SplitWorkspace& ws, hipStream_t st);
 
 }  // namespace sr

@@ -25,8 +25,9 @@
  * With causal_block >= chunk size the whole window is visible (bidirectional).
  *
  * Conventions shared by every call
- *   - Device memory is owned by the caller (e.g. torch tensors).  The library never allocates
- *     or frees device memory.  Host allocations: the opaque handles only.
+ *   - Device memory is owned by the caller (e.g. torch tensors): pools, inputs, outputs and
+ *     the optional attention workspace.  The library never allocates or frees device
+ *     memory.  Host allocations: the opaque handles only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All device work is
  *     enqueued on it in call order; no call blocks or synchronises the host.
  *   - Token-major tensors are contiguous [n][H][D] (the layout a fused qkv projection emits).
@@ -164,9 +165,41 @@ sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
  * cache dtype.  lse: device fp32 [H][n] natural-log log-sum-exp of the scaled logits, or
  * NULL.  softmax_scale > 0 multiplies q.k (usually 1/sqrt(D)).  SR_E_STATE without a
  * current chunk; SR_E_UNSUPPORTED if the call would visit more than SR_MAX_VISIBLE_PAGES
- * pages.  q must not alias out. */
+ * pages.  q must not alias out.  Uses the cache's workspace, if one is attached (below). */
 sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
                              float softmax_scale, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Attention workspace (optional, caller-owned device memory).
+ *
+ * Without a workspace, sr_chunk_attention runs one workgroup per (head, 256-query tile),
+ * each over that tile's whole key list, and the last round of workgroups can leave compute
+ * units idle.  With a workspace attached, each of the device's 8 XCDs (C = compute units / 8,
+ * at most 64) runs its share of the (head, query tile) items whole, C at a time, and the key
+ * tiles of its last (< C) items are cut into pieces spread over all C units.  A piece of a
+ * split item leaves fp32 partial results (output, running max and sum per query) in the
+ * workspace, and the last of the item's pieces to finish merges them in a fixed order and
+ * writes out / lse.  No workgroup waits for another.  The kernel shape is tuned per device
+ * ("3.3 Inference Acceleration and End-to-End Deployment", attention kernel tuning); this
+ * split is the MI355X choice.
+ *
+ * Layout: 32 C records of 8 x 64 x (head_dim / 2 + 2) floats, then 8 C int32 arrival
+ * counters (rounded up to 256 bytes).  The counters must be zero when a call starts;
+ * sr_kvcache_set_workspace zeroes them and every call leaves them zero.  Results with and
+ * without a workspace agree within rounding (different summation order); with a workspace
+ * they are bit-reproducible from call to call.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Workspace bytes for caches of `cfg` on a device with `num_workgroups` compute units
+ * (0: the current device's count, which is what sr_kvcache_set_workspace uses). */
+sr_status sr_attention_workspace_bytes(const sr_kvcache_config* cfg, int32_t num_workgroups, size_t* bytes);
+
+/* Attaches workspace `ws` (device, 256-byte aligned, >= sr_attention_workspace_bytes(cfg, 0)
+ * bytes, else SR_E_NOMEM) to the cache and enqueues the zeroing of its counters on `stream`;
+ * ws == NULL detaches it.  One workspace may serve several caches whose attention calls are
+ * ordered (one stream); calls that may overlap need separate workspaces.  The caller keeps
+ * it alive while calls that use it are queued. */
+sr_status sr_kvcache_set_workspace(sr_kvcache* c, void* ws, size_t ws_bytes, void* stream);
 
 /* Copies the logical key/value sequence of a call on `bank` (persistent, history oldest
  * first, current) into k_out / v_out (device, [max_tokens][H][D]), bit-exact.  *n_tokens

@@ -29,13 +29,15 @@ def sr():
     return harness.lib_module()
 
 
-def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on_step=None):
-    """Streams workload `w` through the library and the oracle model; returns per-step stats."""
+def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on_step=None, workspace="own"):
+    """Streams workload `w` through the library and the oracle model; returns per-step stats.
+    workspace "own": the split schedule (the default a KVCache runs); None: one workgroup per item."""
     import torch
     scale = 1.0 / np.sqrt(w.head_dim)
     stream = synth.SessionStream(w)
     pk, pv = stream.persistent()
-    cache = sr.KVCache(harness.cfg_of(sr, w), harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype))
+    cache = sr.KVCache(harness.cfg_of(sr, w), harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype),
+                       workspace=workspace)
     model = oracle.StreamingCache(pk, pv, w.window)
     stats = []
     for idx, ev in enumerate(stream):
@@ -80,11 +82,15 @@ def check_stats(w, stats):
         assert st_l["max_abs"] <= lse_tol, (w.name, idx, st_l)
 
 
+SCHEDULES = {"split": "own", "whole": None}
+
+
+@pytest.mark.parametrize("schedule", ["split", "whole"])
 @pytest.mark.parametrize("name", ["c0", "t_f32", "t_stream", "t_d64", "t_frame"])
-def test_parity_every_element(sr, name):
+def test_parity_every_element(sr, name, schedule):
     w = synth.get_workload(name)
-    say(f"[parity] {name}: H={w.heads} D={w.head_dim} P={w.persistent} chunk={w.chunk} W={w.window}")
-    stats = run_stream(sr, w, check_gather=True)
+    say(f"[parity] {name} ({schedule}): H={w.heads} D={w.head_dim} P={w.persistent} chunk={w.chunk} W={w.window}")
+    stats = run_stream(sr, w, check_gather=True, workspace=SCHEDULES[schedule])
     assert stats
     check_stats(w, stats)
     say(f"[parity] {name}: worst", max(s[1]["max_abs"] for s in stats), max(s[1]["rel_fro"] for s in stats))
@@ -109,14 +115,58 @@ def test_ring_phase_bit_identical(sr, name):
 FULL = ["c1", "c3", "c4", "c1s", "c4s"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_parity_full_size_sampled(sr, name):
+@pytest.mark.parametrize("name,schedule", [(n, "split") for n in FULL] + [("c1", "whole"), ("c4", "whole")])
+def test_parity_full_size_sampled(sr, name, schedule):
     w = synth.get_workload(name)
     rows = harness.sample_rows(w.chunk, block=w.causal_block if w.causal_block < w.chunk else None)
-    say(f"[full] {name}: {len(rows)} sampled rows x {w.heads} heads, {w.visible_keys} keys")
-    stats = run_stream(sr, w, rows=rows)
+    say(f"[full] {name} ({schedule}): {len(rows)} sampled rows x {w.heads} heads, {w.visible_keys} keys")
+    stats = run_stream(sr, w, rows=rows, workspace=SCHEDULES[schedule])
     check_stats(w, stats)
     say(f"[full] {name}:", stats[-1][1], "lse", stats[-1][2]["max_abs"])
+
+
+def test_one_gpu_share_of_sharded_run(sr):
+    """c1 shapes with 3 heads (one GPU's share when 24 heads are sharded over 8): the split
+    schedule cuts each query tile's key list into about five pieces merged by the last one."""
+    w = synth.get_workload("c1").scaled(heads=3)
+    rows = harness.sample_rows(w.chunk)
+    say(f"[share] c1 x 3 heads: {len(rows)} sampled rows")
+    stats = run_stream(sr, w, rows=rows)
+    check_stats(w, stats)
+
+
+def test_split_schedule_is_deterministic_and_leaves_counters_zero(sr):
+    """Repeated calls give the same bits whichever piece merges; a workspace shared by two
+    caches works; the arrival counters are zero after every call; split and whole schedules
+    agree within rounding."""
+    import torch
+    w = synth.get_workload("t_stream")
+    cfg = harness.cfg_of(sr, w)
+    ws = sr.workspace_for(cfg)
+    pk, pv, hist, cur = synth.single_step_inputs(w)
+    caches = []
+    for workspace in (ws, ws, None):
+        c = sr.KVCache(cfg, harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype), workspace=workspace)
+        for i, (k, v) in enumerate(hist):
+            c.append(i, harness.to_dev(k, w.dtype), harness.to_dev(v, w.dtype))
+        c.append(len(hist), harness.to_dev(cur[0], w.dtype), harness.to_dev(cur[1], w.dtype))
+        caches.append(c)
+    q = harness.to_dev(cur[2], w.dtype)
+    outs = [caches[i % 2].attention(0, q) for i in range(6)]
+    whole = caches[2].attention(0, q)
+    torch.cuda.synchronize()
+    first = harness.to_host(outs[0], w.dtype)
+    for o in outs[1:]:
+        assert (harness.to_host(o, w.dtype) == first).all()
+    # the counters (C = CUs / 8 per XCD, int32, padded to 256 bytes) end the workspace
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    counters = ws[ws.numel() - (8 * max(cus // 8, 1) * 4 + 255) // 256 * 256:].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+    st = gates.error_stats(harness.widen_host(first, w.dtype),
+                           harness.widen_host(harness.to_host(whole, w.dtype), w.dtype))
+    assert st["max_abs"] <= 2e-2 and st["rel_fro"] <= 1e-2, st
+    for c in caches:
+        c.close()
 
 
 def test_session_c2_sampled(sr):

@@ -50,6 +50,29 @@ def test_required_bytes(sr, H, D, P, banks, cap, W, dt):
     assert sr.sr_kvcache_required_bytes(cfg) == 2 * H * pages * 128 * D * (2 if dt == 0 else 4)
 
 
+@pytest.mark.parametrize("H,D,cap,cus", [(24, 128, 4680, 256), (2, 64, 32, 8), (40, 128, 7200, 304), (3, 64, 1, 1)])
+def test_attention_workspace_bytes(sr, H, D, cap, cus):
+    """Per XCD (C = cus / 8 compute units, at least 1): 4C records of 8 waves x 64 lanes x
+    (D/2 output floats + max + sum), then C int32 arrival counters, padded to 256 bytes."""
+    cfg = sr.config_for(H, D, 0, cap, 1)
+    C = max(cus // 8, 1)
+    assert sr.sr_attention_workspace_bytes(cfg, cus) == 8 * 4 * C * 512 * (D // 2 + 2) * 4 + -(-8 * C * 4 // 256) * 256
+
+
+def test_attention_workspace_bytes_validation(sr):
+    cfg = sr.config_for(24, 128, 0, 4680, 1)
+    with pytest.raises(sr.SrError) as e:
+        sr.sr_attention_workspace_bytes(cfg, -1)
+    assert e.value.status == 1
+    cfg.head_dim = 96
+    with pytest.raises(sr.SrError) as e:
+        sr.sr_attention_workspace_bytes(cfg, 256)
+    assert e.value.status == 5
+    lib = sr.load()
+    assert lib.sr_attention_workspace_bytes(ctypes.byref(cfg), 256, None) == 1
+    assert lib.sr_kvcache_set_workspace(None, None, 0, None) == 1
+
+
 @pytest.mark.parametrize("field,value,status", [("head_dim", 96, 5), ("head_dim", 0, 5), ("window_chunks", 15, 1),
                                                 ("dtype_f32_d128", None, 5),
                                                 ("window_chunks", -1, 1), ("num_banks", 0, 1), ("num_heads", 0, 1),
