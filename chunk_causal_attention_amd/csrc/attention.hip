@@ -506,41 +506,56 @@ __device__ __forceinline__ void store_record(float* rec, const RowState<G>& st, 
   }
 }
 
-// Merges the records of a split item's sub-pieces: O^T and l of each rescaled to the common
-// max, summed in (band, sub) order.
+// Merges the pieces of a split item in slot order, rescaling to the running max as it goes
+// (O^T and l of each piece times 2^(m_piece - m)).  The merging workgroup's own piece, slot
+// `own`, is taken from its registers (the same values its record holds), the others from
+// their records.
 template <class G>
-__device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int wave,
-                                              int lane) {
-  const int C = a.cus_per_xcd;
+__device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int own,
+                                              int wave, int lane) {
   const size_t lane_off = size_t(wave) * G::RPL * 64 + lane;
-  float mx[G::QB];
-#pragma unroll
-  for (int qb = 0; qb < G::QB; ++qb) mx[qb] = kMaxInit;
-  for_each_subpiece(a, it, C, [&](int slot) {
-    const float* p = a.rec + size_t(slot) * G::REC + lane_off;
-#pragma unroll
-    for (int qb = 0; qb < G::QB; ++qb) mx[qb] = fmaxf(mx[qb], rec_load(p + (qb * (G::NDB * 16 + 2) + G::NDB * 16) * 64));
-  });
+  RowState<G> mg;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
-    st.m[qb] = mx[qb];
-    st.l[qb] = 0.0f;
+    mg.m[qb] = kMaxInit;
+    mg.l[qb] = 0.0f;
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] = f32x16_t{};
+    for (int db = 0; db < G::NDB; ++db) mg.acc[qb][db] = f32x16_t{};
   }
-  for_each_subpiece(a, it, C, [&](int slot) {
+  for_each_subpiece(a, it, a.cus_per_xcd, [&](int slot) {
     const float* p = a.rec + size_t(slot) * G::REC + lane_off;
+    const bool mine = slot == own;
 #pragma unroll
     for (int qb = 0; qb < G::QB; ++qb) {
       const float* q = p + qb * (G::NDB * 16 + 2) * 64;
-      const float alpha = __builtin_amdgcn_exp2f(rec_load(q + (G::NDB * 16) * 64) - mx[qb]);
-      st.l[qb] += alpha * rec_load(q + (G::NDB * 16 + 1) * 64);
+      const float mk = mine ? st.m[qb] : rec_load(q + (G::NDB * 16) * 64);
+      const float lk = mine ? st.l[qb] : rec_load(q + (G::NDB * 16 + 1) * 64);
+      const float mn = fmaxf(mg.m[qb], mk);
+      const float a0 = __builtin_amdgcn_exp2f(mg.m[qb] - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
+      mg.m[qb] = mn;
+      mg.l[qb] = mg.l[qb] * a0 + lk * a1;
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st.acc[qb][db][e] += alpha * rec_load(q + (db * 16 + e) * 64);
+        for (int e = 0; e < 16; ++e) {
+          const float x = mine ? st.acc[qb][db][e] : rec_load(q + (db * 16 + e) * 64);
+          mg.acc[qb][db][e] = mg.acc[qb][db][e] * a0 + x * a1;
+        }
     }
   });
+  st = mg;
+}
+
+// Pool page (relative to the head's first page) of tile t of the call's tile list: the
+// pages of the segments in visiting order.
+__device__ __forceinline__ int tile_page_index(const AttnArgs& a, int t) {
+  int s = 0, first = 0;
+  for (; s < a.t.n - 1; ++s) {
+    const int nt = (a.t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+    if (t < first + nt) break;
+    first += nt;
+  }
+  return uniform(a.t.s[s].page + (t - first));
 }
 
 // One piece of work: query tile qt of head h over tiles [tb, te) of its tile list.  slot < 0:
@@ -559,9 +574,18 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   const int n_q = a.n_q, H = a.H, cb = a.causal_block;
   const int cur = a.t.n - 1;
   const int cur_len = a.t.s[cur].len;
+  const int ntiles = te - tb;  // tiles [tb, te) of the item's tile list
+  const size_t head_page = size_t(h) * a.total_pages;
   __syncthreads();  // the previous piece of this workgroup is done with LDS
 
-  // Query operands (B operand of K.Q^T), resident for the whole kernel.
+  // The first pages (K and V of tile tb, K of tile tb+1) are requested first, their page
+  // indices walked from the segment table in scalar code, so that their latency overlaps
+  // the query loads and the tile-table build below.
+  issue_page<G>(a.kpool + (head_page + tile_page_index(a, tb)) * G::KTILE, smem, wave, lane);
+  issue_page<G>(a.vpool + (head_page + tile_page_index(a, tb)) * G::KTILE, smem + G::VBASE, wave, lane);
+  if (ntiles > 1) issue_page<G>(a.kpool + (head_page + tile_page_index(a, tb + 1)) * G::KTILE, smem + G::KTILE, wave, lane);
+
+  // Query operands (B operand of K.Q^T), resident for the whole piece.
   Op qop[G::QB][G::KSTEPS];
   int lim_cur[G::QB];
   const T* __restrict__ qg = static_cast<const T*>(a.q);
@@ -582,7 +606,6 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   const int qlast = min(q0 + G::BM, n_q) - 1;
   const int cur_all = uniform(min(cur_len, (q0 / cb + 1) * cb));
   const int cur_any = uniform(min(cur_len, (qlast / cb + 1) * cb));
-  const int ntiles = te - tb;  // tiles [tb, te) of the item's tile list
 
   RowState<G> st;
 #pragma unroll
@@ -592,8 +615,6 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] = f32x16_t{};
   }
-
-  const size_t head_page = size_t(h) * a.total_pages;
 
   // Tile table of the piece: for tile t (visiting order) the page index (relative to the
   // head's first page), the key offset inside the current chunk (-1 for the persistent bank
@@ -613,20 +634,12 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     tab[t - tb] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
                             (is_cur ? cur_all : len) - k0);
   }
-  __syncthreads();
   auto tile_page = [&](int t) { return (head_page + uniform(tab[t].x)) * G::KTILE; };
-
-  // Prologue: K and V of tile 0, K of tile 1; V buffer 1 zeroed (iteration 0 multiplies it
-  // by all-zero probabilities, so it must not hold NaN bit patterns).
-  {
-    const size_t p0 = tile_page(0);
-    issue_page<G>(a.kpool + p0, smem, wave, lane);
-    issue_page<G>(a.vpool + p0, smem + G::VBASE, wave, lane);
-    if (ntiles > 1) issue_page<G>(a.kpool + tile_page(1), smem + G::KTILE, wave, lane);
-    u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::KTILE);
-    for (int x = tid; x < G::KTILE / 16; x += G::NW * 64) vz[x] = u32x4_t{0, 0, 0, 0};
-  }
-  wait_loads<0>();
+  // V buffer 1 zeroed: iteration 0 multiplies it by all-zero probabilities, so it must not
+  // hold NaN bit patterns.
+  u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::KTILE);
+  for (int x = tid; x < G::KTILE / 16; x += G::NW * 64) vz[x] = u32x4_t{0, 0, 0, 0};
+  wait_loads<0>();  // first pages and query operands
   __syncthreads();
 
   const float sl2 = a.scale_log2;
@@ -719,7 +732,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     }
     __syncthreads();
     if (*flag == 0) return;
-    merge_records<G>(a, st, it, wave, lane);
+    merge_records<G>(a, st, it, slot, wave, lane);
   }
 
   // Epilogue: O = O^T / l, written token-major; lse = (max + log2 l) * ln 2.
