@@ -546,6 +546,43 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
   st = mg;
 }
 
+// Iteration i of the key loop (ODD: i odd): mask sub-tile i if partial; P.V of sub-tile i-1
+// alongside the row max of sub-tile i; the lazy rescale; scores of sub-tile i+1 (into sn)
+// alongside the probabilities of sub-tile i.  `ent` is the table entry of tile i / 2; a
+// sub-tile past the sequence (i == nsub) is fully masked.
+template <class G, int ODD>
+__device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[G::QB], char* smem,
+                                         RowState<G>& st, Scores<G>& sc, Scores<G>& sn, Probs<G>& pop,
+                                         const typename G::Op (&qop)[G::QB][G::KSTEPS], float sl2, int c, int hl) {
+  constexpr int SUB = G::SUB;
+  constexpr int NEXT = ODD ? 0 : 1;  // half of the page holding sub-tiles i-1 and i+1
+  const int sub0 = ODD * SUB;
+  const bool in_seq = i < nsub;
+  const int any_rel = in_seq ? uniform(ent.z) - sub0 : 0;
+  const int all_rel = in_seq ? uniform(ent.w) - sub0 : 0;
+  const int cur_k0 = uniform(ent.y);
+  int lim[G::QB];
+#pragma unroll
+  for (int qb = 0; qb < G::QB; ++qb)
+    lim[qb] = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[qb] - cur_k0 - sub0 : all_rel);
+  if (all_rel < SUB) mask_sub<G>(sc, lim, hl);
+  const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::KTILE;  // sub-tile i-1
+  const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
+  float rmax[G::QB];
+  if constexpr (G::ES == 2 && G::QB == 1) {
+    typename G::Op kq_ring[AH];
+    block_a<G>(st, sc, pop, rmax, vpage, NEXT, kpage, NEXT, kq_ring, c, hl);
+    rescale<G>(st, rmax, sl2);
+    block_b<G>(st, sc, pop, sn, qop, kpage, NEXT, kq_ring, sl2, c, hl);
+  } else {
+    accumulate<G>(st, pop, vpage, NEXT, c, hl);
+    row_max<G>(sc, rmax);
+    rescale<G>(st, rmax, sl2);
+    scores<G>(sn, qop, kpage, NEXT, c, hl);
+    softmax_exp<G>(st, sc, pop, sl2);
+  }
+}
+
 // Pool page (relative to the head's first page) of tile t of the call's tile list: the
 // pages of the segments in visiting order.
 __device__ __forceinline__ int tile_page_index(const AttnArgs& a, int t) {
@@ -634,7 +671,6 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     tab[t - tb] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
                             (is_cur ? cur_all : len) - k0);
   }
-  auto tile_page = [&](int t) { return (head_page + uniform(tab[t].x)) * G::KTILE; };
   // V buffer 1 zeroed: iteration 0 multiplies it by all-zero probabilities, so it must not
   // hold NaN bit patterns.
   u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::KTILE);
@@ -653,67 +689,34 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
 #pragma unroll
       for (int kq = 0; kq < G::PSTEPS; ++kq) pop[kb][qb][kq] = Op{};
   scores<G>(sc, qop, smem, 0, c, hl);
-  int4 ent = tab[0];  // tile of sub-tile i
+  Scores<G> sc_odd;  // scores of the odd sub-tile of the current pair (ping-pong with sc)
 
-  for (int i = 0; i <= nsub; ++i) {
-    const int t = i >> 1;
-    // Page requests: at iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in
-    // iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read in iteration 2t).
-    if (i & 1) {
-      if (t + 2 < ntiles) issue_page<G>(a.kpool + tile_page(t + 2), smem + (t & 1) * G::KTILE, wave, lane);
-      if (t + 1 < ntiles)
-        issue_page<G>(a.vpool + tile_page(t + 1), smem + G::VBASE + ((t + 1) & 1) * G::KTILE, wave, lane);
-    }
-    // Table entry of the next iteration's tile (read now, used next iteration).
-    const int4 ent_next = tab[min((i + 1) >> 1, ntiles - 1)];
-
-    // Sub-tile i: keys visible to some / every query (relative to the sub-tile), per-lane
-    // limit; all zero past the sequence, which masks the whole sub-tile.
-    const int sub0 = (i & 1) * SUB;
-    const bool in_seq = i < nsub;
-    const int any_rel = in_seq ? uniform(ent.z) - sub0 : 0;
-    const int all_rel = in_seq ? uniform(ent.w) - sub0 : 0;
-    const int cur_k0 = uniform(ent.y);
-    int lim[G::QB];
-#pragma unroll
-    for (int qb = 0; qb < G::QB; ++qb)
-      lim[qb] = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[qb] - cur_k0 - sub0 : all_rel);
-    const bool partial = all_rel < SUB;
-
-    if (partial) mask_sub<G>(sc, lim, hl);
-    const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::KTILE;  // sub-tile i-1
-    const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
-    Scores<G> sn;
-    float rmax[G::QB];
-    if constexpr (G::ES == 2 && G::QB == 1) {
-      Op kq_ring[AH];
-      // P.V of sub-tile i-1 alongside the row max of sub-tile i, then the rescale, then the
-      // scores of sub-tile i+1 alongside the probabilities of sub-tile i.
-      block_a<G>(st, sc, pop, rmax, vpage, (i - 1) & 1, kpage, (i + 1) & 1, kq_ring, c, hl);
-      rescale<G>(st, rmax, sl2);
-      block_b<G>(st, sc, pop, sn, qop, kpage, (i + 1) & 1, kq_ring, sl2, c, hl);
-    } else {
-      accumulate<G>(st, pop, vpage, (i - 1) & 1, c, hl);
-      row_max<G>(sc, rmax);
-      rescale<G>(st, rmax, sl2);
-      scores<G>(sn, qop, kpage, (i + 1) & 1, c, hl);
-      softmax_exp<G>(st, sc, pop, sl2);
-    }
-#pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < G::QB; ++qb) sc[kb][qb] = sn[kb][qb];
+  // Pair t = iterations 2t (even, first half of tile t) and 2t+1 (odd, second half), then
+  // the closing iteration nsub, whose sub-tile lies past the sequence (fully masked) and
+  // which adds the last P.V.  Page requests: at iteration 2t+1, K of tile t+2 (its buffer held
+  // tile t, last read in iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read
+  // in iteration 2t); their page indices are read from the tile table during iteration 2t.
+  // V of tile t+1 and K of tile t+2 are first read in iteration 2t+3: each wave waits for
+  // its requests at the end of iteration 2t+2, and the barrier that ends every even
+  // iteration publishes those pages and releases the buffers that iteration 2t+3 overwrites.
+  int4 ent = tab[0];  // table entry of tile t
+  for (int t = 0; t < ntiles; ++t) {
+    const int4 ent_next = tab[min(t + 1, ntiles - 1)];
+    const int kpage_next = tab[min(t + 2, ntiles - 1)].x;  // K of tile t+2, requested at 2t+1
+    const int vpage_next = tab[min(t + 1, ntiles - 1)].x;  // V of tile t+1, requested at 2t+1
+    key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
+    if (t >= 1) wait_loads<0>();
+    __syncthreads();
+    if (t + 2 < ntiles)
+      issue_page<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KTILE, smem + (t & 1) * G::KTILE, wave, lane);
+    if (t + 1 < ntiles)
+      issue_page<G>(a.vpool + (head_page + uniform(vpage_next)) * G::KTILE, smem + G::VBASE + ((t + 1) & 1) * G::KTILE,
+                    wave, lane);
+    key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, sl2, c, hl);
     ent = ent_next;
-
-    // V of tile t+1 and K of tile t+2 are first read in iteration 2t+3: wait at the end of
-    // the even iteration 2t+2 (they were requested at 2t+1, nothing later).  Only even
-    // iterations end with a barrier: it publishes those pages and releases the buffers that
-    // iteration 2t+3 overwrites (last read in 2t+2).
-    if ((i & 1) == 0) {
-      if (i >= 2) wait_loads<0>();
-      __syncthreads();
-    }
   }
+  key_step<G, 0>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
+  __syncthreads();
 
   // A piece of a split item leaves its partial result in its record; the last of the item's
   // pieces to arrive merges all of them (in piece order, so the result does not depend on
