@@ -550,7 +550,7 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
 // alongside the row max of sub-tile i; the lazy rescale; scores of sub-tile i+1 (into sn)
 // alongside the probabilities of sub-tile i.  `ent` is the table entry of tile i / 2; a
 // sub-tile past the sequence (i == nsub) is fully masked.
-template <class G, int ODD>
+template <class G, int ODD, bool CLOSING = false>
 __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[G::QB], char* smem,
                                          RowState<G>& st, Scores<G>& sc, Scores<G>& sn, Probs<G>& pop,
                                          const typename G::Op (&qop)[G::QB][G::KSTEPS], float sl2, int c, int hl) {
@@ -565,17 +565,19 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb)
     lim[qb] = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[qb] - cur_k0 - sub0 : all_rel);
-  if (all_rel < SUB) mask_sub<G>(sc, lim, hl);
+  if (!CLOSING && all_rel < SUB) mask_sub<G>(sc, lim, hl);
   const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::KTILE;  // sub-tile i-1
   const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
   float rmax[G::QB];
   if constexpr (G::ES == 2 && G::QB == 1) {
     typename G::Op kq_ring[AH];
     block_a<G>(st, sc, pop, rmax, vpage, NEXT, kpage, NEXT, kq_ring, c, hl);
+    if (CLOSING) return;  // nothing follows the last sub-tile's P.V
     rescale<G>(st, rmax, sl2);
     block_b<G>(st, sc, pop, sn, qop, kpage, NEXT, kq_ring, sl2, c, hl);
   } else {
     accumulate<G>(st, pop, vpage, NEXT, c, hl);
+    if (CLOSING) return;
     row_max<G>(sc, rmax);
     rescale<G>(st, rmax, sl2);
     scores<G>(sn, qop, kpage, NEXT, c, hl);
@@ -603,7 +605,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   using M = typename G::M;
   using Op = typename G::Op;
   using T = typename G::Elem;
-  constexpr int BN = G::BN, SUB = G::SUB, D = G::D;
+  constexpr int BN = G::BN, D = G::D;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);
   const int c = lane & 31, hl = lane >> 5;
@@ -692,13 +694,13 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   Scores<G> sc_odd;  // scores of the odd sub-tile of the current pair (ping-pong with sc)
 
   // Pair t = iterations 2t (even, first half of tile t) and 2t+1 (odd, second half), then
-  // the closing iteration nsub, whose sub-tile lies past the sequence (fully masked) and
-  // which adds the last P.V.  Page requests: at iteration 2t+1, K of tile t+2 (its buffer held
-  // tile t, last read in iteration 2t) and V of tile t+1 (its buffer held tile t-1, last read
-  // in iteration 2t); their page indices are read from the tile table during iteration 2t.
-  // V of tile t+1 and K of tile t+2 are first read in iteration 2t+3: each wave waits for
-  // its requests at the end of iteration 2t+2, and the barrier that ends every even
-  // iteration publishes those pages and releases the buffers that iteration 2t+3 overwrites.
+  // the closing iteration nsub, which only adds the last sub-tile's P.V.  Page requests: at
+  // iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in iteration 2t) and V
+  // of tile t+1 (its buffer held tile t-1, last read in iteration 2t); their page indices are
+  // read from the tile table during iteration 2t.  V of tile t+1 and K of tile t+2 are first
+  // read in iteration 2t+3: each wave waits for its requests at the end of iteration 2t+2,
+  // and the barrier that ends every even iteration publishes those pages and releases the
+  // buffers that iteration 2t+3 overwrites.
   int4 ent = tab[0];  // table entry of tile t
   for (int t = 0; t < ntiles; ++t) {
     const int4 ent_next = tab[min(t + 1, ntiles - 1)];
@@ -715,7 +717,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, sl2, c, hl);
     ent = ent_next;
   }
-  key_step<G, 0>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
+  key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
   __syncthreads();
 
   // A piece of a split item leaves its partial result in its record; the last of the item's
