@@ -17,6 +17,7 @@ __all__ = [
     "sr_attention_workspace_bytes", "sr_kvcache_set_workspace", "workspace_for",
     "sr_ring_create", "sr_ring_append", "sr_ring_evict", "sr_ring_segments", "sr_ring_destroy",
     "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "PAGE_TOKENS", "MAX_WINDOW",
+    "MAX_VISIBLE_PAGES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,8 +25,9 @@ LIB_PATH = os.path.join(HERE, "libsr.so")
 
 SR_OK, SR_E_INVALID, SR_E_STATE, SR_E_NOMEM, SR_E_DEVICE, SR_E_UNSUPPORTED = range(6)
 SR_BF16, SR_F32 = 0, 1
-PAGE_TOKENS = 128
-MAX_WINDOW = 14
+PAGE_TOKENS = 128         # SR_PAGE_TOKENS
+MAX_WINDOW = 14           # SR_MAX_WINDOW
+MAX_VISIBLE_PAGES = 1024  # SR_MAX_VISIBLE_PAGES
 
 
 class SrError(RuntimeError):

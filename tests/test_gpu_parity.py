@@ -275,6 +275,81 @@ def test_hidden_data_does_not_matter(sr):
     cache.close()
 
 
+def _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, seed, chunks, workspace, rows=None):
+    """Streams chunks of the given lengths (evicting when the window is full) through a device
+    cache and the oracle's cache model, then checks the last chunk's attention element by
+    element (or on `rows`) against the oracle."""
+    import torch
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def draw(*shape):
+        t = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(tdt)
+        return t, harness.to_host(t.cuda(), dtype)
+
+    cfg = sr.config_for(H, D, P, cap, W, cb, 1, sr.SR_BF16 if dtype == "bf16" else sr.SR_F32)
+    pk_t, pk = draw(1, P, H, D)
+    pv_t, pv = draw(1, P, H, D)
+    cache = sr.KVCache(cfg, pk_t.cuda() if P else None, pv_t.cuda() if P else None, workspace=workspace)
+    model = oracle.StreamingCache(pk, pv, W)
+    for cid, n in enumerate(chunks):
+        if W > 0 and cid >= W + 1:
+            assert cache.evict() == model.evict()
+        (k_t, k), (v_t, v) = draw(n, H, D), draw(n, H, D)
+        cache.append(cid, k_t.cuda(), v_t.cuda())
+        model.append(cid, k, v)
+    q_t, q = draw(chunks[-1], H, D)
+    scale = 1.0 / np.sqrt(D)
+    lse = torch.empty((H, chunks[-1]), dtype=torch.float32, device="cuda")
+    out = cache.attention(0, q_t.cuda(), lse=lse, softmax_scale=scale)
+    r = np.arange(chunks[-1]) if rows is None else rows
+    o_ref, l_ref = oracle.chunk_attention(model, 0, q, scale, cb, dtype, rows=r)
+    st = gates.error_stats(harness.widen_host(harness.to_host(out, dtype)[r], dtype), o_ref)
+    assert gates.passes(st, gates.gates_for(dtype)), st
+    assert np.abs(lse.cpu().numpy()[:, r] - l_ref).max() <= (2e-2 if dtype == "bf16" else 1e-4)
+    cache.close()
+    return st
+
+
+EDGE = [  # H, D, P, cap, W, cb, dtype, chunks
+    ("one key, no prefix or history", 2, 128, 0, 1, 0, 1, "bf16", [1]),
+    ("fully causal blocks", 2, 128, 0, 300, 0, 1, "bf16", [300]),
+    ("fully causal, fp32", 2, 64, 0, 200, 0, 1, "f32", [200]),
+    ("one head, ragged pages", 1, 64, 5, 129, 1, 129, "bf16", [129, 129, 129]),
+    ("short chunk in a large slot", 2, 128, 300, 1000, 2, 1000, "bf16", [1000, 1000, 3]),
+    ("one-token history chunks", 3, 128, 7, 40, 3, 17, "bf16", [1, 1, 1, 40]),
+    ("no prefix, full window", 2, 64, 0, 256, 3, 64, "bf16", [256] * 6),
+]
+
+
+@pytest.mark.parametrize("schedule", ["split", "whole"])
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_degenerate_and_ragged_shapes(sr, case, schedule):
+    name, H, D, P, cap, W, cb, dtype, chunks = case
+    say(f"[edge] {name} ({schedule})")
+    _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, 31, chunks, SCHEDULES[schedule])
+
+
+@pytest.mark.parametrize("schedule", ["split", "whole"])
+def test_most_visible_pages(sr, schedule):
+    """A call visiting exactly SR_MAX_VISIBLE_PAGES pages (1023 persistent + 1 current) runs and
+    matches the oracle on sampled rows; one page more is refused before anything is enqueued."""
+    import torch
+    P = (sr.MAX_VISIBLE_PAGES - 1) * 128
+    say(f"[max pages] P={P} ({schedule})")
+    _stream_vs_oracle(sr, 1, 64, P, 256, 0, 256, "bf16", 32, [128], SCHEDULES[schedule],
+                      rows=np.array([0, 1, 63, 64, 127]))
+    cfg = sr.config_for(1, 64, P, 256, 0, 256, 1, sr.SR_BF16)
+    pk = torch.zeros((1, P, 1, 64), dtype=torch.bfloat16, device="cuda")
+    cache = sr.KVCache(cfg, pk, pk, workspace=SCHEDULES[schedule])
+    x = torch.zeros((129, 1, 64), dtype=torch.bfloat16, device="cuda")
+    cache.append(0, x, x)
+    with pytest.raises(sr.SrError) as e:
+        cache.attention(0, x)
+    assert e.value.status == 5  # SR_E_UNSUPPORTED
+    cache.close()
+
+
 def test_state_errors_on_device_cache(sr):
     """Rejected calls enqueue nothing and leave the cache usable and unchanged."""
     import torch

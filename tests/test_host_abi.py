@@ -31,6 +31,15 @@ def test_exports_every_declared_symbol(sr):
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_header(sr):
+    """The binding's constants are the header's #defines."""
+    text = open(os.path.join(harness.ROOT, "include", "sr.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (SR_\w+) (\d+)", text)}
+    assert defs["SR_PAGE_TOKENS"] == sr.PAGE_TOKENS
+    assert defs["SR_MAX_WINDOW"] == sr.MAX_WINDOW
+    assert defs["SR_MAX_VISIBLE_PAGES"] == sr.MAX_VISIBLE_PAGES
+
+
 def test_status_strings(sr):
     assert sr.sr_status_string(0) == "SR_OK"
     assert sr.sr_status_string(2) == "SR_E_STATE"
