@@ -6,8 +6,10 @@
 // prefix cache; "3.3 Inference Acceleration and End-to-End Deployment", static-context KV
 // caching and persistent KV layout).
 //
-// Work decomposition.  One workgroup per (head, tile of BM = NW*QB*32 queries); each wave
-// owns QB blocks of 32 queries for the whole key sequence.  The workgroup walks the key
+// Work decomposition.  An item is (head, tile of BM = NW*QB*32 = 256 queries); each wave
+// owns QB blocks of 32 queries.  A piece of work is an item's query tile over a range of
+// its key tiles: the whole range, or, in the split schedule (kernels.hpp, xcd_plan), part
+// of it, with the partial results merged by the item's last piece.  A piece walks the key
 // tiles of its segments in visiting order; tiles past the last visible causal block are
 // never loaded.  Each tile (BN = 128 keys, one cache page) is copied unchanged from HBM
 // into LDS by gfx950's global-to-LDS loads (no staging registers), double buffered.  The
@@ -24,19 +26,20 @@
 // scheduled to keep several LDS reads in flight and to slot the vector work between the
 // MFMAs; two waves per SIMD run the same stream.  A sub-tile past every query's visible
 // keys is simply fully masked (its probabilities are zero), so the loop has no other
-// branches.  K and V pages have separate double buffers in LDS; the pages of tile t+2 (K)
-// and t+1 (V) are requested at iteration 2t+1, two iterations before their first use,
-// and a barrier ends every even iteration (one per page).
+// branches.  The loop runs one page (two iterations) per trip, the two sub-tiles' score
+// registers alternating; a closing step adds the last sub-tile's P.V.  K and V pages have
+// separate double buffers in LDS; the pages of tile t+2 (K) and t+1 (V) are requested at
+// iteration 2t+1, two iterations before their first use, and a barrier ends every even
+// iteration (one per page).
 //
 // Matrix instructions (32x32 output tile).  Scores are computed transposed, S^T = K . Q^T:
 // the key block is the A operand, the queries are the B operand held in registers for the
 // whole kernel, so lane (c, hl) of a wave owns query column c and row-wise reductions are
 // in-lane plus one exchange with the other lane half (v_permlane32_swap).  The output P.V
 // is also computed transposed, O^T += V^T . P^T, so the probabilities never leave the
-// registers: K rows are written to LDS in a permuted row order chosen so that the score
+// registers: the cache pages hold K rows in a permuted order chosen so that the score
 // registers of a lane come out exactly in the operand order the P.V instruction expects,
-// and V is stored transposed in the cache pages, so its operand is one contiguous LDS read
-// per lane.
+// and V transposed, so its operand is one contiguous LDS read per lane.
 //
 // Softmax in the exp2 domain with a lazily updated running max: O and l are rescaled only
 // when some row's max grows by more than 2^8, otherwise the stale max is kept (exact in real
@@ -548,8 +551,8 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
 
 // Iteration i of the key loop (ODD: i odd): mask sub-tile i if partial; P.V of sub-tile i-1
 // alongside the row max of sub-tile i; the lazy rescale; scores of sub-tile i+1 (into sn)
-// alongside the probabilities of sub-tile i.  `ent` is the table entry of tile i / 2; a
-// sub-tile past the sequence (i == nsub) is fully masked.
+// alongside the probabilities of sub-tile i.  `ent` is the table entry of tile i / 2.  The
+// closing step (CLOSING, i == nsub) only adds the P.V of sub-tile nsub-1.
 template <class G, int ODD, bool CLOSING = false>
 __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[G::QB], char* smem,
                                          RowState<G>& st, Scores<G>& sc, Scores<G>& sn, Probs<G>& pop,

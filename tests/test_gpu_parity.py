@@ -126,8 +126,8 @@ def test_parity_full_size_sampled(sr, name, schedule):
 
 
 def test_one_gpu_share_of_sharded_run(sr):
-    """c1 shapes with 3 heads (one GPU's share when 24 heads are sharded over 8): the split
-    schedule cuts each query tile's key list into about five pieces merged by the last one."""
+    """c1 shapes with 3 heads (one GPU's share when 24 heads are sharded over 8): about 7
+    items per XCD, for which the split plan runs the items whole on the split workgroups."""
     w = synth.get_workload("c1").scaled(heads=3)
     rows = harness.sample_rows(w.chunk)
     say(f"[share] c1 x 3 heads: {len(rows)} sampled rows")
