@@ -197,9 +197,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // lds_base + 16 * i.  Issued as inline asm so the compiler's wait-count insertion does not
 // treat every later LDS read as dependent on it (it cannot tell the page buffers apart);
 // the kernel orders these loads itself with explicit vmcnt waits and barriers.  M0 is
-// written here and used by nothing else in this kernel.
+// written here and used by nothing else in this kernel (it is a reserved register that the
+// compiler only sets right before instructions that read it).  The LDS-DMA load reads M0, and a
+// scalar write of M0 needs one wait state before such a read (the compiler cannot insert it
+// inside the asm block), hence the s_nop.
 __device__ __forceinline__ void lds_load16(const void* g, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
 }
 
 // Issues the global-to-LDS loads of one page (K or V, `src` = its first byte) into `dst`:
