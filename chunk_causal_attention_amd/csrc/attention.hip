@@ -360,8 +360,12 @@ __device__ __forceinline__ void accumulate(RowState<G>& st, const Probs<G>& pop,
 // ---- bf16 path: explicitly pipelined blocks ------------------------------------------
 // Each MFMA sits in its own scheduling region (sched_barrier), with the LDS read of the
 // operand AH MFMAs ahead and a slice of the vector work, so the order below is the order
-// the hardware sees.  Operands go through a ring of AH registers.
-constexpr int AH = 6;
+// the hardware sees.  The A operands of all MFMAs (V^T rows in block A, K rows in block B)
+// stream through one ring of AH registers: MFMA j of a block reads slot j % AH and refills it
+// with the operand AH MFMAs later, which near the end of a block is an operand of the next
+// block.  So the reads run AH ahead across block boundaries too, except where the next
+// block's page is published by the barrier in between.
+constexpr int AH = 8;
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 // An empty asm "use": the value must be computed before this point.  Keeps the compiler from
@@ -388,39 +392,92 @@ __device__ __forceinline__ typename G::Op qk_operand(const char* kpage, int sub,
   return G::M::load(kpage + k_addr<G>(sub * G::SUB + kb * 32 + c, ks * 16 + hl * 8));
 }
 
-// Block A: row max of sub-tile i (scores in sc) alongside O^T += V^T P^T of sub-tile i-1.
-// kq_ring receives the first AH score operands of sub-tile i+1 for block B.
-template <class G>
-__device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, const Probs<G>& pop, float (&rmax)[1],
-                                        const char* vpage, int vsub, const char* kpage, int ksub,
-                                        typename G::Op (&kq_ring)[AH], int c, int hl) {
-  using Op = typename G::Op;
+// Probabilities of sub-tile i computed in block A (one operand group of 8); block B computes
+// the others.
+constexpr int kEarlyProbs = 8;
+
+// Block A: O^T += V^T P^T of sub-tile i-1, with, in the shadow of its MFMAs, the row max of
+// sub-tile i and the lazy-rescale decision (first half of the regions) and the first
+// kEarlyProbs probabilities of sub-tile i with their row sum (second half), so that the
+// vector work is spread over both blocks.  Outputs: `grow` (uniform) tells whether the
+// running max moves to `mnew`; the caller rescales the accumulators after the block, once
+// its MFMAs are issued.  The probabilities here already use the new max.
+// LOADED: the ring already holds the first AH V operands (read during the previous block B);
+// else they are read here.  SOFTMAX: false for the closing step (no sub-tile i).  With
+// SOFTMAX, the last AH regions also read the first AH score operands of sub-tile i+1
+// (block B) into the ring.
+template <class G, bool LOADED, bool SOFTMAX>
+__device__ __forceinline__ void block_a(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, float& lsum, bool& grow,
+                                        float& mnew, float sl2, const char* vpage, int vsub, const char* kpage,
+                                        int ksub, typename G::Op (&ring)[AH], int c, int hl) {
+  using M = typename G::M;
   constexpr int NP = G::NDB * G::NKB * G::PSTEPS;
-  Op vq[AH];
+  static_assert(NP % AH == 0, "ring slots must line up across blocks");
+  constexpr int H1 = NP / 2;                        // regions of the row max
+  constexpr int NE = 16 * G::NKB;                   // scores per lane
+  constexpr int MPR = NE / H1;                      // scores per region of the max
+  constexpr int EPR = (kEarlyProbs + (NP - H1) - 1) / (NP - H1);
+  static_assert(MPR % 2 == 0 && kEarlyProbs % 8 == 0, "max pairs, whole operand groups");
+  if constexpr (!LOADED) {
 #pragma unroll
-  for (int r = 0; r < AH; ++r) kq_ring[r] = qk_operand<G>(kpage, ksub, r, c, hl);
-#pragma unroll
-  for (int r = 0; r < AH; ++r) vq[r] = pv_operand<G>(vpage, vsub, r, c, hl);
-  row_max<G>(sc, rmax);
+    for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(vpage, vsub, r, c, hl);
+  }
+  float mx = -INFINITY, mneg = 0.0f;
   fence();
 #pragma unroll
   for (int r = 0; r < NP; ++r) {
     const int db = r % G::NDB, kk = r / G::NDB, kb = kk / G::PSTEPS, kq = kk % G::PSTEPS;
-    st.acc[0][db] = G::M::mma(vq[r % AH], pop[kb][0][kq], st.acc[0][db]);
-    if (r + AH < NP) vq[r % AH] = pv_operand<G>(vpage, vsub, r + AH, c, hl);
+    st.acc[0][db] = M::mma(ring[r % AH], pop[kb][0][kq], st.acc[0][db]);
+    if (r + AH < NP)
+      ring[r % AH] = pv_operand<G>(vpage, vsub, r + AH, c, hl);
+    else if (SOFTMAX)
+      ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH - NP, c, hl);
+    if constexpr (SOFTMAX) {
+      if (r < H1) {
+#pragma unroll
+        for (int e = r * MPR; e < (r + 1) * MPR; e += 2) {
+          mx = fmaxf(mx, fmaxf(sc[e / 16][0][e % 16], sc[(e + 1) / 16][0][(e + 1) % 16]));
+          pin(mx);
+        }
+      }
+      if (r == H1 - 1) {
+        const float m_old = st.m[0];
+        mnew = fmaxf(m_old, pair_max(mx) * sl2);
+        grow = __any(mnew > m_old + kRescaleThreshold);
+        mneg = -(grow ? mnew : m_old);
+      }
+      if (r >= H1) {
+#pragma unroll
+        for (int e = (r - H1) * EPR; e < (r - H1 + 1) * EPR && e < kEarlyProbs; ++e) {
+          sc[e / 16][0][e % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][0][e % 16], sl2, mneg));
+          pin(sc[e / 16][0][e % 16]);
+          if ((e & 7) == 7) {
+            pop[e / 16][0][(e % 16) / 8] = M::pack(sc[e / 16][0], (e % 16) / 8);
+            lsum = M::row_sum(pop[e / 16][0][(e % 16) / 8], lsum);
+            pin(pop[e / 16][0][(e % 16) / 8]);
+            pin(lsum);
+          }
+        }
+      }
+    }
     fence();
   }
 }
 
-// Block B: S^T = K Q^T of sub-tile i+1 alongside the probabilities of sub-tile i.
-template <class G>
+// Block B: S^T = K Q^T of sub-tile i+1 alongside the probabilities of sub-tile i that block A
+// left (from kEarlyProbs on), spread evenly over the regions.  The ring holds the first AH
+// score operands on entry.  NEXT_V: the last AH regions read the first AH
+// V operands of the next block A (half `vsub_next` of the V page at `vnext`) into the ring.
+template <class G, bool NEXT_V>
 __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, Scores<G>& sn,
                                         const typename G::Op (&qop)[1][G::KSTEPS], const char* kpage, int ksub,
-                                        typename G::Op (&kq_ring)[AH], float sl2, int c, int hl) {
+                                        const char* vnext, int vsub_next, typename G::Op (&ring)[AH], float sl2,
+                                        int c, int hl) {
   using M = typename G::M;
   constexpr int NS = G::KSTEPS * G::NKB;
+  static_assert(NS % AH == 0, "ring slots must line up across blocks");
   constexpr int NE = 16 * G::NKB;  // probabilities per lane
-  constexpr int EPR = (NE + NS - 1) / NS;  // per region
+  constexpr int NB = NE - kEarlyProbs;
 #pragma unroll
   for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
   const float mneg = -st.m[0];
@@ -428,10 +485,13 @@ __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
     const int ks = r / G::NKB, kb = r % G::NKB;
-    sn[kb][0] = M::mma(kq_ring[r % AH], qop[0][ks], sn[kb][0]);
-    if (r + AH < NS) kq_ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH, c, hl);
+    sn[kb][0] = M::mma(ring[r % AH], qop[0][ks], sn[kb][0]);
+    if (r + AH < NS)
+      ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH, c, hl);
+    else if (NEXT_V)
+      ring[r % AH] = pv_operand<G>(vnext, vsub_next, r + AH - NS, c, hl);
 #pragma unroll
-    for (int e = r * EPR; e < (r + 1) * EPR && e < NE; ++e) {
+    for (int e = kEarlyProbs + r * NB / NS; e < kEarlyProbs + (r + 1) * NB / NS; ++e) {
       const int ekb = e / 16, ei = e % 16;
       sc[ekb][0][ei] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ekb][0][ei], sl2, mneg));
       pin(sc[ekb][0][ei]);
@@ -555,11 +615,19 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
 // Iteration i of the key loop (ODD: i odd): mask sub-tile i if partial; P.V of sub-tile i-1
 // alongside the row max of sub-tile i; the lazy rescale; scores of sub-tile i+1 (into sn)
 // alongside the probabilities of sub-tile i.  `ent` is the table entry of tile i / 2.  The
-// closing step (CLOSING, i == nsub) only adds the P.V of sub-tile nsub-1.
-template <class G, int ODD, bool CLOSING = false>
+// closing step (CLOSING, i == nsub) only adds the P.V of sub-tile nsub-1.  `mid` runs
+// between the P.V and the scores (the page requests placed there).  `ring` carries
+// operands between the blocks: an odd iteration leaves in it the first V operands of the
+// even iteration that follows (the even iteration's V page was published before the odd
+// one began); an odd iteration reads its own after the barrier that precedes it.
+struct NoWork {
+  __device__ void operator()() const {}
+};
+template <class G, int ODD, bool CLOSING = false, class Mid = NoWork>
 __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[G::QB], char* smem,
                                          RowState<G>& st, Scores<G>& sc, Scores<G>& sn, Probs<G>& pop,
-                                         const typename G::Op (&qop)[G::QB][G::KSTEPS], float sl2, int c, int hl) {
+                                         const typename G::Op (&qop)[G::QB][G::KSTEPS], typename G::Op (&ring)[AH],
+                                         float sl2, int c, int hl, Mid mid = Mid{}) {
   constexpr int SUB = G::SUB;
   constexpr int NEXT = ODD ? 0 : 1;  // half of the page holding sub-tiles i-1 and i+1
   const int sub0 = ODD * SUB;
@@ -576,16 +644,28 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
   const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
   float rmax[G::QB];
   if constexpr (G::ES == 2 && G::QB == 1) {
-    typename G::Op kq_ring[AH];
-    block_a<G>(st, sc, pop, rmax, vpage, NEXT, kpage, NEXT, kq_ring, c, hl);
+    float lsum = 0.0f, mnew = 0.0f;
+    bool grow = false;
+    block_a<G, !ODD, !CLOSING>(st, sc, pop, lsum, grow, mnew, sl2, vpage, NEXT, kpage, NEXT, ring, c, hl);
     if (CLOSING) return;  // nothing follows the last sub-tile's P.V
-    rescale<G>(st, rmax, sl2);
-    block_b<G>(st, sc, pop, sn, qop, kpage, NEXT, kq_ring, sl2, c, hl);
+    if (grow) {  // lazy rescale: the running max grew by more than 2^8 in some row
+      const float alpha = __builtin_amdgcn_exp2f(st.m[0] - mnew);
+      st.l[0] *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) st.acc[0][db] *= alpha;
+      st.m[0] = mnew;
+    }
+    st.l[0] += lsum;
+    mid();
+    // Odd i: the next iteration's P.V reads sub-tile i, the second half of V page i / 2.
+    const char* vnext = smem + G::VBASE + ((i >> 1) & 1) * G::KTILE;
+    block_b<G, ODD == 1>(st, sc, pop, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, c, hl);
   } else {
     accumulate<G>(st, pop, vpage, NEXT, c, hl);
     if (CLOSING) return;
     row_max<G>(sc, rmax);
     rescale<G>(st, rmax, sl2);
+    mid();
     scores<G>(sn, qop, kpage, NEXT, c, hl);
     softmax_exp<G>(st, sc, pop, sl2);
   }
@@ -696,34 +776,50 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     for (int qb = 0; qb < G::QB; ++qb)
 #pragma unroll
       for (int kq = 0; kq < G::PSTEPS; ++kq) pop[kb][qb][kq] = Op{};
+  // Table entry of tile 0, read (and waited for) before the LDS operand reads below: the wait
+  // at the loop head serves every iteration, so it must not find this read queued behind them.
+  int4 ent = tab[0];
+  asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w) : "memory");
   scores<G>(sc, qop, smem, 0, c, hl);
   Scores<G> sc_odd;  // scores of the odd sub-tile of the current pair (ping-pong with sc)
+  // Operand ring: iteration 0 starts with its V operands loaded, from the zeroed buffer that
+  // stands for sub-tile -1.
+  Op ring[AH];
+  if constexpr (G::ES == 2 && G::QB == 1) {
+#pragma unroll
+    for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(smem + G::VBASE + G::KTILE, 1, r, c, hl);
+  }
 
   // Pair t = iterations 2t (even, first half of tile t) and 2t+1 (odd, second half), then
-  // the closing iteration nsub, which only adds the last sub-tile's P.V.  Page requests: at
-  // iteration 2t+1, K of tile t+2 (its buffer held tile t, last read in iteration 2t) and V
-  // of tile t+1 (its buffer held tile t-1, last read in iteration 2t); their page indices are
-  // read from the tile table during iteration 2t.  V of tile t+1 and K of tile t+2 are first
-  // read in iteration 2t+3: each wave waits for its requests at the end of iteration 2t+2,
-  // and the barrier that ends every even iteration publishes those pages and releases the
-  // buffers that iteration 2t+3 overwrites.
-  int4 ent = tab[0];  // table entry of tile t
-  for (int t = 0; t < ntiles; ++t) {
+  // the closing iteration nsub, which only adds the last sub-tile's P.V.  Page requests, in
+  // iteration 2t+1: V of tile t+1 at its start (its buffer held tile t-1, last read in
+  // iteration 2t) and K of tile t+2 halfway, between its P.V and its scores (its buffer held
+  // tile t, last read in iteration 2t); splitting the requests in two halves the burst that
+  // the memory pipeline queues at once.  V of tile t+1 and K of tile t+2 are first read in iteration 2t+3:
+  // each wave waits for its requests at the end of iteration 2t+2, and the barrier that ends
+  // every even iteration publishes those pages and releases the buffers that iteration 2t+3
+  // overwrites.
+  // The table entries for tile t+1 and the page index of tile t+2 are read at the end of
+  // iteration 2t, where the barrier waits for all LDS reads anyway (read earlier, they would
+  // make the wave wait for the operand reads queued behind them).
+  for (int t = 0; t < ntiles; ++t) {  // ent: table entry of tile t
+    key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
     const int4 ent_next = tab[min(t + 1, ntiles - 1)];
     const int kpage_next = tab[min(t + 2, ntiles - 1)].x;  // K of tile t+2, requested at 2t+1
-    const int vpage_next = tab[min(t + 1, ntiles - 1)].x;  // V of tile t+1, requested at 2t+1
-    key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
+    const int vpage_next = ent_next.x;                     // V of tile t+1, requested at 2t+1
     if (t >= 1) wait_loads<0>();
     __syncthreads();
-    if (t + 2 < ntiles)
-      issue_page<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KTILE, smem + (t & 1) * G::KTILE, wave, lane);
     if (t + 1 < ntiles)
       issue_page<G>(a.vpool + (head_page + uniform(vpage_next)) * G::KTILE, smem + G::VBASE + ((t + 1) & 1) * G::KTILE,
                     wave, lane);
-    key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, sl2, c, hl);
+    const auto request_k = [&] {
+      if (t + 2 < ntiles)
+        issue_page<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KTILE, smem + (t & 1) * G::KTILE, wave, lane);
+    };
+    key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, ring, sl2, c, hl, request_k);
     ent = ent_next;
   }
-  key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, sl2, c, hl);
+  key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
   __syncthreads();
 
   // A piece of a split item leaves its partial result in its record; the last of the item's
