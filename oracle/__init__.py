@@ -20,6 +20,9 @@ Modules
   cache_model    the streaming cache: persistent banks, rolling window, current chunk
   chunk_attention  one attention call of the current chunk over the cache model
   full_sequence  an independent dense path over the whole stream with an explicit mask
+                 (also over one window with the prefix cache's asymmetric mask)
+  window_attention  page-literal variant: moving rows over the whole window, prefix rows
+                 over their bank
   brute          arbitrary-precision (decimal) brute force for tiny inputs
 
 Every function has at least one pin in tests/test_oracle_pins.py that does not
@@ -30,8 +33,10 @@ independent path).  Parity status: pinned, except where a docstring says
 from .attention import masked_attention, widen
 from .cache_model import StreamingCache, CacheStateError
 from .chunk_attention import chunk_attention, current_block_mask
-from .full_sequence import full_sequence_attention
+from .full_sequence import full_sequence_attention, window_full_attention
+from .window_attention import window_attention, prefix_attention
 from .brute import brute_attention
 
 __all__ = ["masked_attention", "widen", "StreamingCache", "CacheStateError", "chunk_attention",
-           "current_block_mask", "full_sequence_attention", "brute_attention"]
+           "current_block_mask", "full_sequence_attention", "window_full_attention", "window_attention",
+           "prefix_attention", "brute_attention"]

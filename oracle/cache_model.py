@@ -71,6 +71,32 @@ class StreamingCache:
         else:
             raise CacheStateError("chunk ids must repeat the current id or advance by one")
 
+    def update(self, chunk_id, k, v):
+        """Replace, in place, the K/V of a chunk in the window: a history chunk or the current one.
+
+        Page-literal reading of the window (project page "3.1.2 Historical Context and
+        Temporal Consistency", prefix cache): only the fixed prefix is cached; the recent
+        history and the current chunk are recomputed every step, so the keys/values of a
+        history chunk change while it stays in the window.  Same shape rules as append; an
+        id outside the window is an error and changes nothing."""
+        k, v = np.array(k), np.array(v)
+        if k.shape != v.shape or k.shape[0] == 0:
+            raise CacheStateError("bad chunk shape")
+        if self.capacity is not None and k.shape[0] > self.capacity:
+            raise CacheStateError("chunk larger than the slot capacity")
+        if self.current is not None and chunk_id == self.current[0]:
+            self.current = (chunk_id, k, v)
+            return
+        for i, (cid, _, _) in enumerate(self.history):
+            if cid == chunk_id:
+                self.history[i] = (cid, k, v)
+                return
+        raise CacheStateError("chunk %d is not in the window" % chunk_id)
+
+    def prefix_len(self, bank):
+        """Persistent (prefix) tokens of `bank`."""
+        return self.pk[bank].shape[0]
+
     def evict(self):
         if not self.history:
             raise CacheStateError("nothing to evict")

@@ -64,3 +64,33 @@ def full_sequence_attention(prefix_k, prefix_v, chunks_k, chunks_v, q, window, c
         o[:, h, :] = np.exp(s - lz) @ widen(V[:, h, :], dtype)
         lse[h] = lz[:, 0]
     return o, lse
+
+
+def window_mask(prefix_len, moving_len):
+    """bool [P + M, P + M] over one window laid out as [prefix; moving part]: prefix rows
+    see the prefix columns only, moving rows see every column (bidirectional window)."""
+    n = prefix_len + moving_len
+    mask = np.ones((n, n), dtype=bool)
+    mask[:prefix_len, prefix_len:] = False
+    return mask
+
+
+def window_full_attention(prefix_k, prefix_v, moving_k, moving_v, q_prefix, q_moving, scale, dtype):
+    """Every row of one window as a query over the window itself, with the asymmetric mask
+    of the prefix cache (project page "3.1.2 Historical Context and Temporal Consistency").
+    moving_k/v: the moving part's chunks oldest first (lists of [n][H][D]); q_prefix [P][H][D],
+    q_moving [M][H][D].  Returns (o [P+M][H][D], lse [H][P+M]) fp64, prefix rows first."""
+    K = np.concatenate([prefix_k] + list(moving_k), axis=0)
+    V = np.concatenate([prefix_v] + list(moving_v), axis=0)
+    Q = np.concatenate([q_prefix, q_moving], axis=0)
+    mask = window_mask(prefix_k.shape[0], K.shape[0] - prefix_k.shape[0])
+    H = Q.shape[1]
+    o = np.zeros((Q.shape[0], H, V.shape[2]))
+    lse = np.zeros((H, Q.shape[0]))
+    for h in range(H):
+        s = scale * (widen(Q[:, h, :], dtype) @ widen(K[:, h, :], dtype).T)
+        s[~mask] = -np.inf
+        lz = logsumexp(s, axis=1, keepdims=True)
+        o[:, h, :] = np.exp(s - lz) @ widen(V[:, h, :], dtype)
+        lse[h] = lz[:, 0]
+    return o, lse

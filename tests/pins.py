@@ -202,3 +202,122 @@ def pin_window_rule(cache_cls, seed=11, n_ops=400):
                 except Exception as ex:
                     assert not ok, ex
             assert cache.visible_ids() == hist + ([cur] if cur is not None else [])
+
+
+# ---------------------------------------------------------------- page-literal window pins
+
+def _f32(r, *shape):
+    return r.standard_normal(shape).astype(np.float32)
+
+
+def pin_window_equals_full(cache_cls, window_attn, prefix_attn, full_attn, W=2, n_chunks=5, steps=2, banks=2,
+                           P=5, Tc=4, H=2, D=3, seed=17):
+    """A stream whose moving rows are recomputed every step (each history chunk updated in
+    place, then the current chunk appended): the moving rows' attention through the cache,
+    and the prefix rows' attention over their bank, equal one dense pass over the window
+    [prefix; history; current] with the prefix cache's asymmetric mask."""
+    r = _rng(seed)
+    pk, pv = _f32(r, banks, P, H, D), _f32(r, banks, P, H, D)
+    cache = cache_cls(pk, pv, W)
+    scale = 0.55
+    for c in range(n_chunks):
+        if W > 0 and c >= W + 1:
+            cache.evict()
+        ids = [c - j for j in range(min(c, W), 0, -1)]
+        for s in range(steps):
+            kv = {cid: (_f32(r, Tc, H, D), _f32(r, Tc, H, D)) for cid in ids}
+            for cid in ids:
+                cache.update(cid, *kv[cid])
+            kc, vc = _f32(r, Tc, H, D), _f32(r, Tc, H, D)
+            cache.append(c, kc, vc)
+            bank = s % banks
+            qm, qp = _f32(r, Tc * (len(ids) + 1), H, D), _f32(r, P, H, D)
+            o, lse = window_attn(cache, bank, qm, scale, "f32")
+            op, lp = prefix_attn(cache, bank, qp, scale, "f32")
+            of, lf = full_attn(pk[bank], pv[bank], [kv[i][0] for i in ids] + [kc], [kv[i][1] for i in ids] + [vc],
+                               qp, qm, scale, "f32")
+            assert np.abs(o - of[P:]).max() <= 1e-12 and np.abs(lse - lf[:, P:]).max() <= 1e-12, (c, s)
+            assert np.abs(op - of[:P]).max() <= 1e-12 and np.abs(lp - lf[:, :P]).max() <= 1e-12, (c, s)
+
+
+def pin_window_brute_force(cache_cls, window_attn, prefix_attn, seeds=range(3)):
+    """Tiny windows against the decimal brute force, visible sets written out from the rule:
+    a moving row sees prefix, history and current; a prefix row sees the prefix."""
+    for sd in seeds:
+        r = _rng(400 + sd)
+        W, P, Tc, H, D = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(1, 4)), 1, int(r.integers(1, 4))
+        pk, pv = _f32(r, 1, P, H, D), _f32(r, 1, P, H, D)
+        cache = cache_cls(pk, pv, W)
+        ks, vs = [], []
+        for c in range(W + 1):
+            k, v = _f32(r, Tc, H, D), _f32(r, Tc, H, D)
+            cache.append(c, k, v)
+            ks.append(k)
+            vs.append(v)
+        K = np.concatenate([pk[0]] + ks).astype(np.float64)[:, 0]
+        V = np.concatenate([pv[0]] + vs).astype(np.float64)[:, 0]
+        qm, qp = _f32(r, Tc * (W + 1), H, D), _f32(r, P, H, D)
+        o, lse = window_attn(cache, 0, qm, 0.8, "f32")
+        ob, lb = brute_attention(qm[:, 0].astype(np.float64).tolist(), K.tolist(), V.tolist(),
+                                 [[True] * K.shape[0]] * qm.shape[0], 0.8)
+        assert np.abs(o[:, 0] - np.array(ob)).max() <= 1e-13 * max(1.0, np.abs(ob).max()), sd
+        assert np.abs(lse[0] - np.array(lb)).max() <= 1e-13 * max(1.0, np.abs(lb).max()), sd
+        op, _ = prefix_attn(cache, 0, qp, 0.8, "f32")
+        ob, _ = brute_attention(qp[:, 0].astype(np.float64).tolist(), K[:P].tolist(), V[:P].tolist(),
+                                [[True] * P] * P, 0.8)
+        assert np.abs(op[:, 0] - np.array(ob)).max() <= 1e-13 * max(1.0, np.abs(ob).max()), sd
+
+
+def pin_window_chunking_free(cache_cls, window_attn, seed=23):
+    """Attention inside the window is bidirectional: the moving rows' results depend on the
+    moving tokens only, not on how they are cut into chunks (here 9 tokens as 3 + 2 + 4 in a
+    W = 2 window, and as 5 + 4 in a W = 1 window)."""
+    r = _rng(seed)
+    P, H, D = 3, 2, 4
+    pk, pv = _f32(r, 1, P, H, D), _f32(r, 1, P, H, D)
+    k, v, q = _f32(r, 9, H, D), _f32(r, 9, H, D), _f32(r, 9, H, D)
+    a = cache_cls(pk, pv, 2)
+    for cid, (lo, hi) in enumerate([(0, 3), (3, 5), (5, 9)]):
+        a.append(cid, k[lo:hi], v[lo:hi])
+    b = cache_cls(pk, pv, 1)
+    for cid, (lo, hi) in enumerate([(0, 5), (5, 9)]):
+        b.append(cid, k[lo:hi], v[lo:hi])
+    oa, la = window_attn(a, 0, q, 0.5, "f32")
+    ob, lb = window_attn(b, 0, q, 0.5, "f32")
+    assert np.abs(oa - ob).max() <= 1e-13 and np.abs(la - lb).max() <= 1e-13
+
+
+def pin_update_rule(cache_cls, seed=29):
+    """update replaces exactly the named chunk of the window (history or current) and
+    nothing else; an id outside the window is rejected with the state unchanged."""
+    r = _rng(seed)
+    pk = _f32(r, 1, 2, 1, 2)
+    cache = cache_cls(pk, pk, 2)
+    chunks = [(_f32(r, 3, 1, 2), _f32(r, 3, 1, 2)) for _ in range(3)]
+    for cid, (k, v) in enumerate(chunks):
+        cache.append(cid, k, v)
+    k_new, v_new = _f32(r, 2, 1, 2), _f32(r, 2, 1, 2)
+    cache.update(1, k_new, v_new)
+    ks, vs, _ = cache.sequence(0)
+    want_k = np.concatenate([pk[0], chunks[0][0], k_new, chunks[2][0]])
+    want_v = np.concatenate([pk[0], chunks[0][1], v_new, chunks[2][1]])
+    assert ks.shape == want_k.shape and (ks == want_k).all() and (vs == want_v).all()
+    before = cache.sequence(0)
+    for bad in (3, 7, -1):
+        try:
+            cache.update(bad, k_new, v_new)
+            raise AssertionError("update of a chunk outside the window was accepted")
+        except AssertionError:
+            raise
+        except Exception:
+            pass
+    after = cache.sequence(0)
+    assert all((x == y).all() for x, y in zip(before[:2], after[:2])) and before[2] == after[2]
+    cache.evict()
+    try:
+        cache.update(0, k_new, v_new)
+        raise AssertionError("update of an evicted chunk was accepted")
+    except AssertionError:
+        raise
+    except Exception:
+        pass

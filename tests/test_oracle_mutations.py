@@ -131,3 +131,91 @@ def test_cache_model_mutant_is_caught(cls):
     assert _caught(pins.pin_window_rule, cls) or \
         _caught(pins.pin_stream_equals_full_sequence, cls, oracle.chunk_attention, oracle.full_sequence_attention) \
         or _caught(pins.pin_stream_brute_force, cls, oracle.chunk_attention), cls.__name__
+
+
+# ---------------------------------------------------------------- page-literal window
+
+def _window_variant(kind):
+    """window_attention with a planted mistake in the visible set of the moving rows."""
+    def window_attn(cache, bank, q, scale, dtype):
+        k, v, _ = cache.sequence(bank)
+        P = cache.prefix_len(bank)
+        M = k.shape[0] - P
+        chunk_of = np.concatenate([np.full(x.shape[0], i) for i, x in
+                                   enumerate([h[1] for h in cache.history] + [cache.current[1]])])
+        vis = np.ones((M, P + M), bool)
+        if kind == "no_current":
+            vis[:, P + M - cache.current[1].shape[0]:] = False
+            vis[np.arange(M), P + np.arange(M)] = True   # keep every row defined
+        elif kind == "chunk_causal":
+            vis[:, P:] = chunk_of[None, :] <= chunk_of[:, None]
+        elif kind == "no_prefix":
+            vis[:, :P] = False
+        elif kind == "history_only_own":
+            vis[:, P:] = chunk_of[None, :] == chunk_of[:, None]
+        H = q.shape[1]
+        o = np.zeros((M, H, v.shape[2]))
+        lse = np.zeros((H, M))
+        for h in range(H):
+            o[:, h], lse[h] = oracle.masked_attention(widen(q[:, h], dtype), widen(k[:, h], dtype),
+                                                      widen(v[:, h], dtype), vis, scale)
+        return o, lse
+    return window_attn
+
+
+@pytest.mark.parametrize("kind", ["no_current", "chunk_causal", "no_prefix", "history_only_own"])
+def test_window_mutant_is_caught(kind):
+    wa = _window_variant(kind)
+    assert _caught(pins.pin_window_equals_full, oracle.StreamingCache, wa, oracle.prefix_attention,
+                   oracle.window_full_attention) or \
+        _caught(pins.pin_window_brute_force, oracle.StreamingCache, wa, oracle.prefix_attention) or \
+        _caught(pins.pin_window_chunking_free, oracle.StreamingCache, wa), kind
+
+
+def _prefix_sees_window(cache, bank, q, scale, dtype):
+    """prefix_attention mutant: the prefix rows also see the moving part."""
+    k, v, _ = cache.sequence(bank)
+    H = q.shape[1]
+    o = np.zeros((q.shape[0], H, v.shape[2]))
+    lse = np.zeros((H, q.shape[0]))
+    for h in range(H):
+        o[:, h], lse[h] = oracle.masked_attention(widen(q[:, h], dtype), widen(k[:, h], dtype), widen(v[:, h], dtype),
+                                                  np.ones((q.shape[0], k.shape[0]), bool), scale)
+    return o, lse
+
+
+def test_prefix_mutant_is_caught():
+    assert _caught(pins.pin_window_equals_full, oracle.StreamingCache, oracle.window_attention, _prefix_sees_window,
+                   oracle.window_full_attention)
+
+
+class _UpdateCurrentOnly(oracle.StreamingCache):
+    def update(self, chunk_id, k, v):
+        if self.current is not None and chunk_id == self.current[0]:
+            self.current = (chunk_id, np.array(k), np.array(v))
+        elif chunk_id not in [c for c, _, _ in self.history]:
+            raise oracle.CacheStateError("not in the window")
+
+
+class _UpdateOldest(oracle.StreamingCache):
+    def update(self, chunk_id, k, v):
+        if self.history and chunk_id != self.current[0]:
+            cid = self.history[0][0]
+            self.history[0] = (cid, np.array(k), np.array(v))
+            return
+        super().update(chunk_id, k, v)
+
+
+class _UpdateAnyId(oracle.StreamingCache):
+    def update(self, chunk_id, k, v):
+        try:
+            super().update(chunk_id, k, v)
+        except oracle.CacheStateError:
+            self.current = (self.current[0], np.array(k), np.array(v))
+
+
+@pytest.mark.parametrize("cls", [_UpdateCurrentOnly, _UpdateOldest, _UpdateAnyId], ids=lambda c: c.__name__)
+def test_update_mutant_is_caught(cls):
+    assert _caught(pins.pin_update_rule, cls) or \
+        _caught(pins.pin_window_equals_full, cls, oracle.window_attention, oracle.prefix_attention,
+                oracle.window_full_attention), cls.__name__

@@ -76,3 +76,26 @@ def test_lse_large_logits_finite():
     e = np.exp(-1.0)
     assert abs(o[0, 0] - 1.0 / (1.0 + e)) <= 1e-15
     assert abs(lse[0] - (1000.0 + np.log1p(e))) <= 1e-12
+
+
+def test_window_equals_full_window():
+    pins.pin_window_equals_full(oracle.StreamingCache, oracle.window_attention, oracle.prefix_attention,
+                                oracle.window_full_attention)
+
+
+@pytest.mark.parametrize("W", [0, 1, 3])
+def test_window_equals_full_window_shapes(W):
+    pins.pin_window_equals_full(oracle.StreamingCache, oracle.window_attention, oracle.prefix_attention,
+                                oracle.window_full_attention, W=W, n_chunks=6, seed=40 + W)
+
+
+def test_window_brute_force():
+    pins.pin_window_brute_force(oracle.StreamingCache, oracle.window_attention, oracle.prefix_attention)
+
+
+def test_window_chunking_free():
+    pins.pin_window_chunking_free(oracle.StreamingCache, oracle.window_attention)
+
+
+def test_update_rule():
+    pins.pin_update_rule(oracle.StreamingCache)
