@@ -77,6 +77,9 @@ def load():
         "sr_kvcache_append_chunk": [P, I64, P, P, I32, P],
         "sr_kvcache_evict": [P, ctypes.POINTER(I64)],
         "sr_chunk_attention": [P, I32, P, P, P, F32, P],
+        "sr_window_attention": [P, I32, P, I32, P, P, F32, P],
+        "sr_prefix_attention": [P, I32, P, P, P, F32, P],
+        "sr_kvcache_update_chunk": [P, I64, P, P, I32, P],
         "sr_kvcache_gather": [P, I32, P, P, I32, ctypes.POINTER(I32), P],
         "sr_kvcache_destroy": [P],
         "sr_attention_workspace_bytes": [cfgp, I32, ctypes.POINTER(SZ)],
@@ -84,6 +87,7 @@ def load():
         "sr_ring_create": [cfgp, ctypes.POINTER(P)],
         "sr_ring_append": [P, I64, I32, ctypes.POINTER(I32), ctypes.POINTER(I64)],
         "sr_ring_evict": [P, ctypes.POINTER(I64)],
+        "sr_ring_update": [P, I64, I32, ctypes.POINTER(I32)],
         "sr_ring_segments": [P, I32, ctypes.POINTER(sr_segment), I32, ctypes.POINTER(I32)],
         "sr_ring_destroy": [P],
     }
@@ -164,6 +168,25 @@ def sr_chunk_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=Non
                                      _stream(stream)))
 
 
+def sr_window_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    _check(load().sr_window_attention(h, bank, _ptr(q), q.shape[0], _ptr(out), _ptr(lse), float(softmax_scale),
+                                      _stream(stream)))
+
+
+def sr_prefix_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    _check(load().sr_prefix_attention(h, bank, _ptr(q), _ptr(out), _ptr(lse), float(softmax_scale),
+                                      _stream(stream)))
+
+
+def sr_kvcache_update_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
+    n = k.shape[0] if n_tokens is None else n_tokens
+    _check(load().sr_kvcache_update_chunk(h, chunk_id, _ptr(k), _ptr(v), n, _stream(stream)))
+
+
 def sr_kvcache_gather(h, bank, k_out, v_out, stream=None):
     n = ctypes.c_int32()
     _check(load().sr_kvcache_gather(h, bank, _ptr(k_out), _ptr(v_out), k_out.shape[0], ctypes.byref(n),
@@ -215,6 +238,12 @@ def sr_ring_evict(r):
     e = ctypes.c_int64()
     _check(load().sr_ring_evict(r, ctypes.byref(e)))
     return e.value
+
+
+def sr_ring_update(r, chunk_id, n_tokens):
+    slot = ctypes.c_int32()
+    _check(load().sr_ring_update(r, chunk_id, n_tokens, ctypes.byref(slot)))
+    return slot.value
 
 
 def sr_ring_segments(r, bank, max_segments=MAX_WINDOW + 2):
@@ -269,6 +298,12 @@ class KVCache:
         self._check_tensor(v, k.shape)
         sr_kvcache_append_chunk(self.h, chunk_id, k, v, k.shape[0], stream)
 
+    def update(self, chunk_id, k, v, stream=None):
+        """Rewrite, in place, a chunk in the window (history or current)."""
+        self._check_tensor(k, (k.shape[0], self.cfg.num_heads, self.cfg.head_dim))
+        self._check_tensor(v, k.shape)
+        sr_kvcache_update_chunk(self.h, chunk_id, k, v, k.shape[0], stream)
+
     def evict(self):
         return sr_kvcache_evict(self.h)
 
@@ -284,6 +319,28 @@ class KVCache:
         if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (self.cfg.num_heads, q.shape[0])):
             raise ValueError("lse must be float32 [H][n]")
         sr_chunk_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def _out_lse(self, q, out, lse):
+        import torch
+        self._check_tensor(q, (q.shape[0], self.cfg.num_heads, self.cfg.head_dim))
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_tensor(out, q.shape)
+        if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (self.cfg.num_heads, q.shape[0])):
+            raise ValueError("lse must be float32 [H][n]")
+        return out
+
+    def window_attention(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        """Moving rows q (history oldest first, then current) over the whole window."""
+        out = self._out_lse(q, out, lse)
+        sr_window_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def prefix_attention(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        """Prefix rows q [P][H][D] of bank `bank` over that bank only."""
+        out = self._out_lse(q, out, lse)
+        sr_prefix_attention(self.h, bank, q, out, lse, softmax_scale, stream)
         return out
 
     def gather(self, bank=0, max_tokens=None, stream=None):

@@ -724,13 +724,13 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
       Op v = M::load(reinterpret_cast<const char*>(src + ks * M::K));
       qop[qb][ks] = ok ? v : Op{};
     }
-    lim_cur[qb] = ok ? min(cur_len, (qrow / cb + 1) * cb) : cur_len;
+    lim_cur[qb] = ok && cb > 0 ? min(cur_len, (qrow / cb + 1) * cb) : cur_len;
   }
 
   // Keys of the current chunk visible to every / to some query of this workgroup.
   const int qlast = min(q0 + G::BM, n_q) - 1;
-  const int cur_all = uniform(min(cur_len, (q0 / cb + 1) * cb));
-  const int cur_any = uniform(min(cur_len, (qlast / cb + 1) * cb));
+  const int cur_all = uniform(cb > 0 ? min(cur_len, (q0 / cb + 1) * cb) : cur_len);
+  const int cur_any = uniform(cb > 0 ? min(cur_len, (qlast / cb + 1) * cb) : cur_len);
 
   RowState<G> st;
 #pragma unroll
@@ -901,14 +901,14 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     const int g = local + xcd * per + (xcd < rem ? xcd : rem);
     h = uniform(g / a.q_tiles);
     qt = uniform(g - h * a.q_tiles);
-    te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block));
+    te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
   } else {
     p = uniform_plan(a.plan[xcd]);
     if (local < p.whole) {
       const int item = p.first + local;
       h = uniform(item / a.q_tiles);
       qt = uniform(item - h * a.q_tiles);
-      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block));
+      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
     } else {
       const int j = local - p.whole;
       if (j >= p.wgs) return;
@@ -966,8 +966,8 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
 }
 
 template <class G>
-hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                    float scale, const SplitWorkspace& ws, hipStream_t st) {
+hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb, const void* q,
+                    void* o, float* lse, float scale, const SplitWorkspace& ws, hipStream_t st) {
   static_assert(SR_MAX_VISIBLE_PAGES <= 32767, "tile counts are stored as int16");
   AttnArgs a{};
   a.q = q;
@@ -975,10 +975,10 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
   a.lse = lse;
   a.kpool = static_cast<const char*>(pool);
   a.vpool = static_cast<const char*>(pool) + L.half_bytes;
-  a.n_q = t.s[t.n - 1].len;
+  a.n_q = n_q;
   a.H = L.H;
   a.total_pages = L.total_pages;
-  a.causal_block = L.cb;
+  a.causal_block = cb;
   a.q_tiles = (a.n_q + G::BM - 1) / G::BM;
   a.scale_log2 = scale * kLog2e;
   a.fixed_tiles = 0;
@@ -993,7 +993,8 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
     // whole items + split workgroups.
     int32_t per = 0;
     for (int x = 0; x < 8; ++x) {
-      const XcdPlan p = xcd_plan(x, a.n_items, a.q_tiles, a.fixed_tiles, a.n_q, L.cb, ws.cus_per_xcd, a.left_tiles[x]);
+      const XcdPlan p = xcd_plan(x, a.n_items, a.q_tiles, a.fixed_tiles, a.n_q, cb, t.s[t.n - 1].len, ws.cus_per_xcd,
+                                 a.left_tiles[x]);
       a.plan[x] = p;
       per = p.whole + p.wgs > per ? p.whole + p.wgs : per;
     }
@@ -1008,14 +1009,15 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, const 
 
 }  // namespace
 
-hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                            float softmax_scale, const SplitWorkspace& ws, hipStream_t st) {
+hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
+                            const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
+                            hipStream_t st) {
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st)
-                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st);
+    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st)
+                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
   // fp32 caches are head_dim 64 only (validated on the host): a double-buffered 128-key
   // fp32 tile at head_dim 128 would need 256 KiB of LDS.
-  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, q, o, lse, softmax_scale, ws, st);
+  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
 }
 
 }  // namespace sr

@@ -51,6 +51,29 @@ sr_status device_cus(int32_t* n) {
   return SR_OK;
 }
 
+// Checks shared by the attention calls (before anything is enqueued).
+sr_status check_attention_args(const sr_kvcache* c, int32_t bank, const void* q, const void* out, const float* lse,
+                               float softmax_scale) {
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!q || !out || !sr::aligned16(q) || !sr::aligned16(out))
+    return sr::fail(SR_E_INVALID, "q and out must be non-null and 16-byte aligned");
+  if (q == out) return sr::fail(SR_E_INVALID, "q must not alias out");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return sr::fail(SR_E_INVALID, "lse must be 4-byte aligned");
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return sr::fail(SR_E_INVALID, "softmax_scale must be finite and > 0");
+  const sr::Layout& L = c->ring.L;
+  if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  return SR_OK;
+}
+
+sr_status check_pages(const sr::SegTable& t) {
+  int32_t pages = 0;
+  for (int i = 0; i < t.n; ++i) pages += (t.s[i].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+  if (pages > SR_MAX_VISIBLE_PAGES)
+    return sr::fail(SR_E_UNSUPPORTED, "the call visits %d pages of keys, more than %d", pages, SR_MAX_VISIBLE_PAGES);
+  return SR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,24 +142,69 @@ sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id) {
 sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse, float softmax_scale,
                              void* stream) {
   sr::clear_error();
-  if (!c) return sr::fail(SR_E_INVALID, "null cache");
-  if (!q || !out || !sr::aligned16(q) || !sr::aligned16(out))
-    return sr::fail(SR_E_INVALID, "q and out must be non-null and 16-byte aligned");
-  if (q == out) return sr::fail(SR_E_INVALID, "q must not alias out");
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return sr::fail(SR_E_INVALID, "lse must be 4-byte aligned");
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
-    return sr::fail(SR_E_INVALID, "softmax_scale must be finite and > 0");
-  const sr::Layout& L = c->ring.L;
-  if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
   if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
   const sr::SegTable t = make_table(c->ring, bank, nullptr);
-  int32_t pages = 0;
-  for (int i = 0; i < t.n; ++i) pages += (t.s[i].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
-  if (pages > SR_MAX_VISIBLE_PAGES)
-    return sr::fail(SR_E_UNSUPPORTED, "the call visits %d pages of keys, more than %d", pages, SR_MAX_VISIBLE_PAGES);
-  return device_status(
-      sr::launch_attention(L, c->pool, t, q, out, lse, softmax_scale, c->split, static_cast<hipStream_t>(stream)),
-      "chunk attention");
+  st = check_pages(t);
+  if (st != SR_OK) return st;
+  const sr::Layout& L = c->ring.L;
+  return device_status(sr::launch_attention(L, c->pool, t, c->ring.cur_len, L.cb, q, out, lse, softmax_scale, c->split,
+                                            static_cast<hipStream_t>(stream)),
+                       "chunk attention");
+}
+
+sr_status sr_window_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
+                              float softmax_scale, void* stream) {
+  sr::clear_error();
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
+  const int32_t moving = sr::moving_tokens(c->ring);
+  if (n_rows != moving)
+    return sr::fail(SR_E_INVALID, "n_rows %d: the window's moving part (history + current) has %d tokens", n_rows,
+                    moving);
+  const sr::SegTable t = make_table(c->ring, bank, nullptr);
+  st = check_pages(t);
+  if (st != SR_OK) return st;
+  return device_status(sr::launch_attention(c->ring.L, c->pool, t, n_rows, 0, q, out, lse, softmax_scale, c->split,
+                                            static_cast<hipStream_t>(stream)),
+                       "window attention");
+}
+
+sr_status sr_prefix_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse, float softmax_scale,
+                              void* stream) {
+  sr::clear_error();
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
+  const sr::Layout& L = c->ring.L;
+  if (L.P == 0) return sr::fail(SR_E_INVALID, "the cache has no persistent tokens");
+  sr::SegTable t{};
+  t.n = 1;
+  t.s[0] = sr::DevSeg{L.bank_page(bank), L.P};
+  st = check_pages(t);
+  if (st != SR_OK) return st;
+  return device_status(sr::launch_attention(L, c->pool, t, L.P, 0, q, out, lse, softmax_scale, c->split,
+                                            static_cast<hipStream_t>(stream)),
+                       "prefix attention");
+}
+
+sr_status sr_kvcache_update_chunk(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v, int32_t n_tokens,
+                                  void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
+    return sr::fail(SR_E_INVALID, "chunk K/V must be non-null and 16-byte aligned");
+  int32_t slot;
+  sr_status st = sr::plan_update(c->ring, chunk_id, n_tokens, &slot);
+  if (st != SR_OK) return st;
+  const sr::Layout& L = c->ring.L;
+  st = device_status(sr::launch_append(L, c->pool, k, v, n_tokens, L.slot_page(slot), L.pages_per_slot,
+                                       static_cast<hipStream_t>(stream)),
+                     "chunk update");
+  if (st != SR_OK) return st;
+  sr::commit_update(c->ring, chunk_id, n_tokens);
+  return SR_OK;
 }
 
 sr_status sr_attention_workspace_bytes(const sr_kvcache_config* cfg, int32_t num_workgroups, size_t* bytes) {

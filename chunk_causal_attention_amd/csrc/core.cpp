@@ -89,6 +89,31 @@ void commit_append(sr_ring& r, int64_t chunk_id, int32_t n_tokens) {
   r.cur_len = n_tokens;
 }
 
+sr_status plan_update(const sr_ring& r, int64_t chunk_id, int32_t n_tokens, int32_t* slot) {
+  if (n_tokens < 1 || n_tokens > r.L.cap)
+    return fail(SR_E_INVALID, "n_tokens %d outside [1, chunk_capacity=%d]", n_tokens, r.L.cap);
+  bool resident = r.has_current && chunk_id == r.cur_id;
+  for (int i = 0; i < r.hist_count && !resident; ++i) resident = r.hist_id[i] == chunk_id;
+  if (!resident) return fail(SR_E_INVALID, "chunk %lld is not in the window", (long long)chunk_id);
+  if (slot) *slot = r.slot_of(chunk_id);
+  return SR_OK;
+}
+
+void commit_update(sr_ring& r, int64_t chunk_id, int32_t n_tokens) {
+  if (r.has_current && chunk_id == r.cur_id) {
+    r.cur_len = n_tokens;
+    return;
+  }
+  for (int i = 0; i < r.hist_count; ++i)
+    if (r.hist_id[i] == chunk_id) r.hist_len[i] = n_tokens;
+}
+
+int32_t moving_tokens(const sr_ring& r) {
+  int32_t n = r.has_current ? r.cur_len : 0;
+  for (int i = 0; i < r.hist_count; ++i) n += r.hist_len[i];
+  return n;
+}
+
 }  // namespace sr
 
 extern "C" {
@@ -116,6 +141,17 @@ sr_status sr_ring_append(sr_ring* r, int64_t chunk_id, int32_t n_tokens, int32_t
   sr::commit_append(*r, chunk_id, n_tokens);
   if (slot) *slot = s;
   if (committed_id) *committed_id = com;
+  return SR_OK;
+}
+
+sr_status sr_ring_update(sr_ring* r, int64_t chunk_id, int32_t n_tokens, int32_t* slot) {
+  sr::clear_error();
+  if (!r) return sr::fail(SR_E_INVALID, "null ring");
+  int32_t s;
+  sr_status st = sr::plan_update(*r, chunk_id, n_tokens, &s);
+  if (st != SR_OK) return st;
+  sr::commit_update(*r, chunk_id, n_tokens);
+  if (slot) *slot = s;
   return SR_OK;
 }
 

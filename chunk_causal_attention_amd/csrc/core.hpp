@@ -51,4 +51,11 @@ namespace sr {
 sr_status plan_append(const sr_ring& r, int64_t chunk_id, int32_t n_tokens, int32_t* slot, int64_t* committed);
 // Applies a planned append (must follow a successful plan_append with the same arguments).
 void commit_append(sr_ring& r, int64_t chunk_id, int32_t n_tokens);
+// Validates an in-place update of a chunk in the window (a history chunk or the current one)
+// without changing the ring; on success fills the chunk's slot.
+sr_status plan_update(const sr_ring& r, int64_t chunk_id, int32_t n_tokens, int32_t* slot);
+// Applies a planned update: the chunk's length becomes n_tokens.
+void commit_update(sr_ring& r, int64_t chunk_id, int32_t n_tokens);
+// Tokens of the moving part of the window: history chunks plus the current chunk.
+int32_t moving_tokens(const sr_ring& r);
 }  // namespace sr

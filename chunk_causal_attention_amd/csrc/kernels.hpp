@@ -18,7 +18,8 @@ struct DevSeg {
 
 // Segment table of one call, built on the host when the ring changes and passed by value
 // (no per-call host-to-device copy).  Segments are in visiting order; the last one is the
-// current chunk.
+// "current" segment, the only one whose visibility can depend on the query row (see
+// item_tiles): the current chunk for chunk and window calls, the bank for prefix calls.
 struct SegTable {
   int32_t n;
   DevSeg s[kMaxSegs];
@@ -27,13 +28,20 @@ struct SegTable {
 // Queries per workgroup of the attention kernel (8 waves x 32 queries).
 constexpr int kQueryTile = 256;
 
-// Key tiles (cache pages) that query tile `qt` visits: every page of the bank and history
-// segments (`fixed_tiles`) plus the current chunk's pages up to the last causal block that
-// one of the tile's queries can see.  n_q is the current chunk's length.
-__host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, int32_t n_q, int32_t cb) {
-  const int32_t end = (qt + 1) * kQueryTile < n_q ? (qt + 1) * kQueryTile : n_q;
-  const int32_t blocks_end = ((end - 1) / cb + 1) * cb;
-  const int32_t any = blocks_end < n_q ? blocks_end : n_q;
+// Key tiles (cache pages) that query tile `qt` visits: every page of the segments before the
+// last (`fixed_tiles`) plus the last segment's pages up to the last causal block that one of
+// the tile's queries can see.  Query row i sees the last segment's keys j with
+// floor(j / cb) <= floor(i / cb) (chunk calls: the rows are the current chunk's tokens), or
+// all of them when cb == 0 (window and prefix calls).  n_q: query rows; cur_len: length of
+// the last segment.
+__host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, int32_t n_q, int32_t cb,
+                                              int32_t cur_len) {
+  int32_t any = cur_len;
+  if (cb > 0) {
+    const int32_t end = (qt + 1) * kQueryTile < n_q ? (qt + 1) * kQueryTile : n_q;
+    const int32_t blocks_end = ((end - 1) / cb + 1) * cb;
+    any = blocks_end < cur_len ? blocks_end : cur_len;
+  }
   return fixed_tiles + (any + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
 }
 
@@ -102,7 +110,7 @@ inline int32_t split_estimate(const int16_t* T, int32_t left, int32_t C, int32_t
 
 // Plan of XCD x; T receives the tile counts of its split items.
 inline XcdPlan xcd_plan(int32_t x, int32_t n_items, int32_t q_tiles, int32_t fixed_tiles, int32_t n_q, int32_t cb,
-                        int32_t C, int16_t* T) {
+                        int32_t cur_len, int32_t C, int16_t* T) {
   XcdPlan p{};
   p.first = int32_t(int64_t(x) * n_items / 8);
   const int32_t n = int32_t(int64_t(x + 1) * n_items / 8) - p.first;
@@ -111,7 +119,7 @@ inline XcdPlan xcd_plan(int32_t x, int32_t n_items, int32_t q_tiles, int32_t fix
   if (p.left == 0) return p;
   int32_t tmax = 0;
   for (int32_t r = 0; r < p.left; ++r) {
-    T[r] = int16_t(item_tiles((p.first + p.whole + r) % q_tiles, fixed_tiles, n_q, cb));
+    T[r] = int16_t(item_tiles((p.first + p.whole + r) % q_tiles, fixed_tiles, n_q, cb, cur_len));
     tmax = T[r] > tmax ? T[r] : tmax;
   }
   // Best b: every stride-th candidate, then the neighbours of the best one.
@@ -170,9 +178,11 @@ hipError_t launch_append(const Layout& L, void* pool, const void* k, const void*
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
                          hipStream_t st);
 
-// Chunk attention of the current chunk's queries over the segments of `t`.  With
+// Attention of n_q query rows q over the key segments of t (pages of `pool`), the last
+// segment seen per causal block of cb rows (cb == 0: whole; see item_tiles).  With
 // ws.cus_per_xcd > 0 the split schedule (xcd_plan) is used.
-hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, const void* q, void* o, float* lse,
-                            float softmax_scale, const SplitWorkspace& ws, hipStream_t st);
+hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
+                            const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
+                            hipStream_t st);
 
 }  // namespace sr

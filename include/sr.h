@@ -24,6 +24,12 @@
  * where current query i sees current key j iff floor(j / causal_block) <= floor(i / causal_block).
  * With causal_block >= chunk size the whole window is visible (bidirectional).
  *
+ * Page-literal window variant (same pages, "3.1.2", prefix cache): the moving part of the
+ * window -- the history chunks and the current chunk -- is recomputed every step, so all of
+ * its rows are queries over the whole window, bidirectionally (sr_window_attention), its K/V
+ * are rewritten in place (sr_kvcache_update_chunk), and the prefix rows attend to their bank
+ * only (sr_prefix_attention), which yields the next layer's bank once per denoising step.
+ *
  * Conventions shared by every call
  *   - Device memory is owned by the caller (e.g. torch tensors): pools, inputs, outputs and
  *     the optional attention workspace.  The library never allocates or frees device
@@ -115,6 +121,10 @@ sr_status sr_ring_create(const sr_kvcache_config* cfg, sr_ring** out);
 sr_status sr_ring_append(sr_ring* r, int64_t chunk_id, int32_t n_tokens, int32_t* slot, int64_t* committed_id);
 /* Drops the oldest history chunk; *evicted_id (nullable) receives its id. */
 sr_status sr_ring_evict(sr_ring* r, int64_t* evicted_id);
+/* Replaces, in place, a chunk that is in the window (a history chunk or the current one):
+ * its length becomes n_tokens and *slot (nullable) receives its ring slot.  SR_E_INVALID for
+ * an id outside the window or n_tokens outside [1, chunk_capacity]; the state is unchanged. */
+sr_status sr_ring_update(sr_ring* r, int64_t chunk_id, int32_t n_tokens, int32_t* slot);
 /* Logical key segments of an attention call on `bank`, in visiting order:
  * persistent bank (omitted when P == 0), history oldest first, current.  Writes at most
  * `max` entries to `out` and the count to *n.  SR_E_STATE if there is no current chunk,
@@ -160,6 +170,17 @@ sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k
 /* Drops the oldest history chunk (host metadata only; nothing is enqueued). */
 sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
 
+/* Rewrites, in place, the K/V of a chunk in the window (device, [n_tokens][H][D]): a history
+ * chunk or the current one (for the current one this equals appending its id again).  The
+ * slot past n_tokens is zeroed and the chunk's length becomes n_tokens.  For the page-literal
+ * window variant, where the recent history is recomputed every step ("3.1.2 Historical
+ * Context and Temporal Consistency", prefix cache; "3.3 Inference Acceleration", persistent
+ * KV layout: the dynamic region is updated in place).  SR_E_INVALID (nothing enqueued) for an
+ * id outside the window, n_tokens outside [1, chunk_capacity] or bad pointers.  The caller
+ * may reuse k / v once the stream has passed the call. */
+sr_status sr_kvcache_update_chunk(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v,
+                                  int32_t n_tokens, void* stream);
+
 /* Attention of the current chunk's queries q (device, [n][H][D], n = current chunk length)
  * over bank `bank` + history + current (see top of file).  out: device [n][H][D] in the
  * cache dtype.  lse: device fp32 [H][n] natural-log log-sum-exp of the scaled logits, or
@@ -168,6 +189,24 @@ sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
  * pages.  q must not alias out.  Uses the cache's workspace, if one is attached (below). */
 sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
                              float softmax_scale, void* stream);
+
+/* Page-literal window variant ("3.1.2 Historical Context and Temporal Consistency": the moving
+ * part attends to the entire window, attention inside the window is bidirectional).  Queries:
+ * the n_rows moving rows q (device, [n_rows][H][D]), history chunks oldest first and then the
+ * current chunk, n_rows = their total length (else SR_E_INVALID).  Every row sees every key of
+ * bank `bank` + history + current; the cache's causal_block does not apply.  out [n_rows][H][D]
+ * in the cache dtype, lse fp32 [H][n_rows] or NULL, softmax_scale, errors, workspace and
+ * aliasing as for sr_chunk_attention. */
+sr_status sr_window_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out,
+                              float* lse, float softmax_scale, void* stream);
+
+/* The prefix rows' attention ("3.1.2", prefix cache: the prefix attends only to itself; "3.3",
+ * static-context KV caching: computed once per denoising step and session).  Queries: the P
+ * prefix rows q (device, [P][H][D]) of bank `bank`; keys: that bank's persistent tokens only.
+ * out [P][H][D], lse fp32 [H][P] or NULL.  Needs no current chunk.  SR_E_INVALID when the
+ * cache has no persistent tokens; otherwise as sr_chunk_attention. */
+sr_status sr_prefix_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
+                              float softmax_scale, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Attention workspace (optional, caller-owned device memory).

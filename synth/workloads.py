@@ -75,6 +75,9 @@ WORKLOADS = {
     "c1s": Workload("c1s", 11, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, 1.0, _SIGMA),
     "c4s": Workload("c4s", 14, "bf16", 32, 128, 2072, 9360, 2, 3120, 1, 3, 1, 1.0, _SIGMA,
                     boost_fraction=0.01),
+    # page-literal window variant at c1 shapes: the 3 x 4680 moving rows (2 history chunks and
+    # the current one) attend to the whole window, 2072 + 14040 keys
+    "c1w": Workload("c1w", 31, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, _SIGMA, _SIGMA),
     # reduced shapes the oracle finishes in seconds; they still span several tiles and ragged tails
     "t_stream": Workload("t_stream", 21, "bf16", 3, 128, 300, 600, 2, 600, 2, 5, 2, 1.0, 1.0,
                          ar_rho=0.9, single_step=False),
@@ -82,6 +85,10 @@ WORKLOADS = {
                         boost_fraction=0.01),
     "t_d64": Workload("t_d64", 23, "bf16", 3, 64, 130, 333, 1, 111, 1, 3, 1, 1.0, 1.0),
     "t_f32": Workload("t_f32", 24, "f32", 3, 64, 70, 300, 2, 100, 2, 5, 2, 1.0, 1.0, single_step=False),
+    # window-variant streams: two banks, ragged tiles; fp32 and head_dim 64 too
+    "t_win": Workload("t_win", 32, "bf16", 3, 128, 300, 420, 2, 420, 2, 5, 2, 1.0, 1.0, single_step=False),
+    "t_win64": Workload("t_win64", 33, "bf16", 2, 64, 130, 200, 3, 200, 1, 5, 1, 1.0, 1.0, single_step=False),
+    "t_winf32": Workload("t_winf32", 34, "f32", 2, 64, 70, 150, 1, 150, 2, 4, 2, 1.0, 1.0, single_step=False),
 }
 
 
@@ -187,6 +194,49 @@ class SessionStream:
                 q = _draw(w, "Q", shape, w.qk_std, chunk=c, step=s)
                 yield {"chunk": c, "step": s, "bank": s % w.banks, "evict_before": evict and s == 0,
                        "k": _store(w, k), "v": _store(w, v), "q": _store(w, q)}
+
+
+class WindowStream:
+    """Seeded chunk-steps of the page-literal window variant of a workload.
+
+    The moving part of the window (the history chunks still in it and the current chunk)
+    is recomputed every step: each chunk-step draws fresh K/V for every history chunk in the
+    window (tags KH/VH, keyed by the history chunk's id, the step and its distance to the
+    current chunk), fresh K/V for the current chunk (K/V, as in SessionStream) and queries
+    for every moving row (tag QM).  No boosted keys.  Every chunk has w.chunk tokens.
+    `prefix_queries(bank)` draws the prefix rows' queries of a bank (tag QP).
+
+    Yields per chunk-step {"chunk", "step", "bank", "evict_before", "history": [(id, k, v)]
+    oldest first, "k", "v", "q"} with q the moving rows [M][H][D], history oldest first and
+    then the current chunk's tokens.
+    """
+
+    def __init__(self, w):
+        self.w = w
+
+    def persistent(self):
+        pk, pv = persistent_inputs(self.w)
+        return _store(self.w, pk), _store(self.w, pv)
+
+    def prefix_queries(self, bank):
+        w = self.w
+        return _store(w, _draw(w, "QP", (w.persistent, w.heads, w.head_dim), w.qk_std, bank=bank))
+
+    def __iter__(self):
+        w = self.w
+        shape = (w.chunk, w.heads, w.head_dim)
+        for c in range(w.chunks):
+            evict = w.window > 0 and c >= w.window + 1
+            ids = list(range(max(0, c - w.window), c))
+            for s in range(w.steps):
+                hist = [(i, _store(w, _draw(w, "KH", shape, w.qk_std, chunk=i, step=s, bank=c - i)),
+                         _store(w, _draw(w, "VH", shape, w.v_std, chunk=i, step=s, bank=c - i))) for i in ids]
+                k = _store(w, _draw(w, "K", shape, w.qk_std, chunk=c, step=s))
+                v = _store(w, _draw(w, "V", shape, w.v_std, chunk=c, step=s))
+                q = _store(w, _draw(w, "QM", ((len(ids) + 1) * w.chunk, w.heads, w.head_dim), w.qk_std, chunk=c,
+                                    step=s))
+                yield {"chunk": c, "step": s, "bank": s % w.banks, "evict_before": evict and s == 0,
+                       "history": hist, "k": k, "v": v, "q": q}
 
 
 def single_step_inputs(w):

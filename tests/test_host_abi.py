@@ -118,6 +118,9 @@ def test_init_validation_before_device_work(sr):
         assert st == want, (pool, nbytes, pk, pv, st, sr.sr_last_error())
         assert not h.value
     assert lib.sr_chunk_attention(None, 0, P(4096), P(8192), None, 0.1, None) == 1
+    assert lib.sr_window_attention(None, 0, P(4096), 1, P(8192), None, 0.1, None) == 1
+    assert lib.sr_prefix_attention(None, 0, P(4096), P(8192), None, 0.1, None) == 1
+    assert lib.sr_kvcache_update_chunk(None, 0, P(4096), P(4096), 1, None) == 1
     assert lib.sr_kvcache_append_chunk(None, 0, P(4096), P(4096), 1, None) == 1
     assert lib.sr_kvcache_evict(None, None) == 1
     assert lib.sr_kvcache_destroy(None) == 0
@@ -135,8 +138,28 @@ def _ring_vs_model(sr, W, P, banks, cap, seed, n_ops=600):
     cur = None
     try:
         for _ in range(n_ops):
-            op = r.integers(0, 5)
-            if op == 0:
+            op = r.integers(0, 6)
+            if op == 5:
+                # in-place update of a chunk in the window (or of one that is not)
+                ids = model.visible_ids()
+                cid = int(r.choice(ids)) if ids and r.random() < 0.8 else int(r.integers(-1, 2100))
+                n = int(r.integers(0, cap + 2)) if r.random() < 0.1 else int(r.integers(1, cap + 1))
+                try:
+                    model.update(cid, np.zeros((n, 1, 1), np.float32), np.zeros((n, 1, 1), np.float32))
+                    m_ok = True
+                except oracle.CacheStateError:
+                    m_ok = False
+                try:
+                    slot = sr.sr_ring_update(ring, cid, n)
+                    r_ok = True
+                    assert slot == cid % (W + 1)
+                except sr.SrError as ex:
+                    r_ok = False
+                    assert ex.status == 1
+                assert m_ok == r_ok, ("update", cid, n, model.visible_ids())
+                if r_ok:
+                    lens[cid] = n
+            elif op == 0:
                 try:
                     e_model = model.evict()
                 except oracle.CacheStateError:
