@@ -8,6 +8,11 @@ Deployment").  Steps cycle over several independent layer caches, the way a DiT 
 visits its layers, so each step finds its cache cold in the 256 MB last-level cache
 (the 832x480 workload's K/V are ~200 MB per layer); `--layers 1` gives the warm number.
 
+`--workload c1w` times the page-literal window variant instead: per step, evict, rewrite the
+W history chunks in place, append the current chunk, and the attention of all moving rows
+(history + current) over the whole window ("3.1.2 Historical Context and Temporal
+Consistency", prefix cache).
+
 Prints one JSON line (see --help).  Inputs are seeded synthetic tensors resident in HBM
 before the timed region; timing brackets exactly --steps steps with device syncs, and HIP
 events around each attention launch give the kernel's average duration for the roofline.
@@ -36,8 +41,10 @@ PEAK_HBM_GBS = 8000.0
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 219914.0, "write_kib": 103840.4,
-           "attention_sha256": "7b828b3d2741478b812ffd8aff94175d519e12599e7ed27cd6f95b493fde0e54"},
+    "c1": {"fetch_kib": 220291.4, "write_kib": 103829.5,
+           "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
+    "c1w": {"fetch_kib": 320250.9, "write_kib": 125276.1,
+            "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 
@@ -109,6 +116,174 @@ def make_inputs(sr, w, n_sets, torch):
     return to_dev(pk, w.dtype), to_dev(pv, w.dtype), sets
 
 
+def copy_calibration(res, torch, dev):
+    """A plain device copy of known size, for scaling the profiler's HBM byte counters."""
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    res["copy_calibration_bytes"] = n
+
+
+# Workloads run in the page-literal window variant (moving rows over the whole window).
+WINDOW_WORKLOADS = ("c1w",)
+
+
+def window_flops(w):
+    """Algorithmic flops of one window call: every moving row sees every key of the window."""
+    m = (w.window + 1) * w.chunk
+    return 4.0 * w.heads * w.head_dim * m * float(w.persistent + m)
+
+
+def cpu_baseline_window(w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on whole heads of the window variant's full-window step."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    stream = synth.WindowStream(w)
+    pk, pv = stream.persistent()
+    m = oracle.StreamingCache(pk, pv, w.window)
+    ev = None
+    for ev in stream:
+        if ev["evict_before"]:
+            m.evict()
+        for i, k, v in ev["history"]:
+            m.update(i, k, v)
+        m.append(ev["chunk"], ev["k"], ev["v"])
+    scale = 1.0 / math.sqrt(w.head_dim)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        oracle.window_attention(m, ev["bank"], ev["q"], scale, w.dtype, heads=[heads])
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = window_flops(w) * heads / w.heads
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads x all {ev['q'].shape[0]} moving rows of {w.name} "
+                      f"({w.persistent + ev['q'].shape[0]} keys), fp64 numpy oracle, {dt:.1f} s wall"}
+
+
+def run_window(args, w):
+    """Window-variant step: evict, rewrite the W history chunks in place, append the current
+    chunk, and the moving rows' attention over the whole window."""
+    import torch
+    import synth
+    import chunk_causal_attention_amd as sr
+    from synth.torch_io import to_dev
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    stream = synth.WindowStream(w)
+    pk, pv = (to_dev(x, w.dtype) for x in stream.persistent())
+    full = None
+    for ev in stream:
+        full = ev          # the last chunk-step: full window
+    hist = [(to_dev(k, w.dtype), to_dev(v, w.dtype)) for _, k, v in full["history"]]
+    kc, vc, q = (to_dev(full[x], w.dtype) for x in ("k", "v", "q"))
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
+                        sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
+    t_init = time.perf_counter()
+    layers = []
+    ws = None if args.no_split else sr.workspace_for(cfg)
+    for _ in range(args.layers):
+        c = sr.KVCache(cfg, pk, pv, workspace=ws)
+        for j in range(w.window + 1):
+            c.append(j, kc, vc)
+        layers.append({"cache": c, "next": w.window + 1})
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t_init
+    m = q.shape[0]
+    out = torch.empty_like(q)
+    lse = torch.empty((w.heads, m), dtype=torch.float32, device=dev)
+    ev_pairs = []
+
+    def step(i, timed):
+        L = layers[i % len(layers)]
+        c = L["cache"]
+        cid = L["next"]
+        L["next"] += 1
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if w.window > 0:
+            c.evict()
+        if timed:
+            e[0].record()
+        for j, (k, v) in enumerate(hist):
+            c.update(cid - w.window + j, k, v)
+        c.append(cid, kc, vc)
+        if timed:
+            e[1].record()
+        c.window_attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+        if timed:
+            e[2].record()
+            ev_pairs.append(e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_write = np.array([a.elapsed_time(b) for a, b, _ in ev_pairs])
+    t_attn = np.array([b.elapsed_time(c) for _, b, c in ev_pairs])
+    ms_step = elapsed * 1e3 / args.steps
+    F = window_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    if args.traffic_kib is not None:
+        traffic = args.traffic_kib * 1024.0
+    res = {
+        "metric": "ms per window step & attention TFLOP/s (frac of bf16 MFMA peak), 1 MI355X",
+        "value": round(F / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: window step (page-literal variant), {w.heads} heads x {w.head_dim}, "
+                        f"{m} moving rows ({w.window}x{w.chunk} history + {w.chunk} current) over "
+                        f"{w.persistent} persistent + {m} window tokens, bidirectional",
+            "heads": w.heads, "head_dim": w.head_dim, "queries": m, "keys_visible": w.persistent + m,
+            "layers_cycled": args.layers,
+            "step": "evict + update_chunk x W + append_chunk + window_attention",
+            "schedule": "whole items" if args.no_split else "key tiles split evenly over the CUs",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "ms_attention": round(float(t_attn.mean()), 4),
+        "ms_attention_p10_p50_p90": [round(float(np.percentile(t_attn, p)), 4) for p in (10, 50, 90)],
+        "ms_kv_writes": round(float(t_write.mean()), 4),
+        "kv_writes_GBps": round((w.window + 1) * append_bytes(w) / (t_write.mean() * 1e-3) / 1e9, 1),
+        "attention_gflop_per_call": round(F / 1e9, 3),
+        "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
+    }
+    for L in layers:
+        L["cache"].close()
+    if args.copy_calibration:
+        copy_calibration(res, torch, dev)
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_window(w, args.cpu_budget)
+    return res
+
+
 def run(args):
     import torch
     import synth
@@ -116,6 +291,8 @@ def run(args):
 
     sr.load()
     w = synth.get_workload(args.workload)
+    if w.name in WINDOW_WORKLOADS:
+        return run_window(args, w)
     if not w.single_step:
         raise SystemExit(f"workload {w.name} is a parity case, not a bench workload")
     torch.cuda.init()
@@ -218,14 +395,7 @@ def run(args):
     for L in layers:
         L["cache"].close()
     if args.copy_calibration:
-        # A plain device copy of known size, for scaling the profiler's HBM byte counters.
-        n = 256 << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = n
+        copy_calibration(res, torch, dev)
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     return res
@@ -236,7 +406,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="c1", help="c1 (default), c3, c4, c1s, c4s or c2")
+    ap.add_argument("--workload", default="c1",
+                    help="c1 (default), c3, c4, c1s, c4s; c1w: the page-literal window variant at c1 shapes")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-split", action="store_true",
