@@ -23,6 +23,7 @@ Modules
                  (also over one window with the prefix cache's asymmetric mask)
   window_attention  page-literal variant: moving rows over the whole window, prefix rows
                  over their bank
+  qk_prep        qk-RMSNorm and rotary embedding of the qkv projection before the cache write
   brute          arbitrary-precision (decimal) brute force for tiny inputs
 
 Every function has at least one pin in tests/test_oracle_pins.py that does not
@@ -35,8 +36,9 @@ from .cache_model import StreamingCache, CacheStateError
 from .chunk_attention import chunk_attention, current_block_mask
 from .full_sequence import full_sequence_attention, window_full_attention
 from .window_attention import window_attention, prefix_attention
+from .qk_prep import rms_norm, rope, rope_angles, prep_qkv
 from .brute import brute_attention
 
 __all__ = ["masked_attention", "widen", "StreamingCache", "CacheStateError", "chunk_attention",
            "current_block_mask", "full_sequence_attention", "window_full_attention", "window_attention",
-           "prefix_attention", "brute_attention"]
+           "prefix_attention", "rms_norm", "rope", "rope_angles", "prep_qkv", "brute_attention"]

@@ -321,3 +321,100 @@ def pin_update_rule(cache_cls, seed=29):
         raise
     except Exception:
         pass
+
+
+# ---------------------------------------------------------------- qk-RMSNorm + rotary embedding pins
+
+def pin_rms_norm(rms_norm):
+    """Unit RMS with gamma = 1 and eps = 0; scale invariance; the eps closed form on a constant
+    vector; gamma multiplies feature by feature."""
+    r = _rng(51)
+    x = r.standard_normal((5, 3, 16)) * 3.0
+    y = rms_norm(x, np.ones(16), 0.0)
+    assert np.abs(np.mean(y * y, axis=-1) - 1.0).max() <= 1e-14
+    assert np.abs(rms_norm(7.5 * x, np.ones(16), 0.0) - y).max() <= 1e-14
+    a, eps = 0.3, 0.05
+    c = rms_norm(np.full((1, 8), a), np.ones(8), eps)
+    assert np.abs(c - a / math.sqrt(a * a + eps)).max() <= 1e-15
+    g = r.uniform(0.5, 2.0, 16)
+    assert np.abs(rms_norm(x, g, 1e-6) - rms_norm(x, np.ones(16), 1e-6) * g).max() <= 1e-13
+
+
+def pin_rope_closed_form(rope):
+    """A unit vector on the first element of pair j turns by pos_a * base^(-k / n_a) into the
+    pair (cos, sin); written out for one pair in each section, with base and sections chosen
+    so the exponent and the section bookkeeping matter."""
+    sections, base, D = (2, 3, 3), 500.0, 16
+    cases = [(0, 0, 0), (1, 0, 1), (2, 1, 0), (4, 1, 2), (5, 2, 0), (7, 2, 2)]   # (pair j, axis a, index k)
+    pos = np.array([[37, -5, 11]])
+    for j, a, k in cases:
+        x = np.zeros((1, 1, D))
+        x[0, 0, 2 * j] = 1.0
+        y = rope(x, pos, sections, base)
+        ang = pos[0, a] * base ** (-k / sections[a])
+        want = np.zeros(D)
+        want[2 * j], want[2 * j + 1] = math.cos(ang), math.sin(ang)
+        assert np.abs(y[0, 0] - want).max() <= 1e-12, (j, a, k)
+
+
+def pin_rope_relative(rope, seed=53):
+    """Scores depend only on position differences (project page 3.2, iteration 4): shifting
+    both positions by the same amount on any axis leaves q'.k' unchanged; position 0 is the
+    identity; pair norms are preserved; rotations compose."""
+    r = _rng(seed)
+    sections, base, D = (3, 2, 3), 10000.0, 16
+    q, k = r.standard_normal((4, 2, D)), r.standard_normal((4, 2, D))
+    pq = r.integers(-50, 50, (4, 3))
+    pk = r.integers(-50, 50, (4, 3))
+    s0 = np.einsum("nhd,nhd->nh", rope(q, pq, sections, base), rope(k, pk, sections, base))
+    for shift in ([100, 0, 0], [0, -7, 0], [3, 5, 1000]):
+        s1 = np.einsum("nhd,nhd->nh", rope(q, pq + shift, sections, base), rope(k, pk + shift, sections, base))
+        assert np.abs(s1 - s0).max() <= 1e-9, shift
+    assert np.abs(rope(q, np.zeros((4, 3), int), sections, base) - q).max() == 0.0
+    y = rope(q, pq, sections, base)
+    assert np.abs((y[..., 0::2] ** 2 + y[..., 1::2] ** 2) - (q[..., 0::2] ** 2 + q[..., 1::2] ** 2)).max() <= 1e-12
+    p2 = r.integers(-50, 50, (4, 3))
+    assert np.abs(rope(rope(q, pq, sections, base), p2, sections, base) - rope(q, pq + p2, sections, base)).max() <= 1e-11
+
+
+def pin_rope_sections(rope, seed=57):
+    """A pair only sees its own axis: changing the y position leaves the t and x pairs as they
+    were, and so on for each axis."""
+    r = _rng(seed)
+    sections, base, D = (2, 3, 3), 10000.0, 16
+    x = r.standard_normal((3, 1, D))
+    pos = r.integers(0, 40, (3, 3))
+    y0 = rope(x, pos, sections, base)
+    bounds = np.cumsum((0,) + sections)
+    for a in range(3):
+        p = pos.copy()
+        p[:, a] += 13
+        y1 = rope(x, p, sections, base)
+        own = np.zeros(D, bool)
+        own[2 * bounds[a]:2 * bounds[a + 1]] = True
+        assert (y1[..., ~own] == y0[..., ~own]).all(), a
+        assert not np.allclose(y1[..., own], y0[..., own]), a
+
+
+def pin_prep_qkv(prep_qkv, rms_norm, rope, seed=59):
+    """q and k are normalised with their own gains and then rotated; v passes unchanged."""
+    r = _rng(seed)
+    n, H, D = 6, 2, 8
+    qkv = r.standard_normal((n, 3, H, D)).astype(np.float32)
+    pos = r.integers(0, 9, (n, 3))
+    gq, gk = r.uniform(0.5, 2, D), r.uniform(0.5, 2, D)
+    q, k, v = prep_qkv(qkv, pos, gq, gk, 1e-5, (2, 1, 1), 100.0, "f32")
+    assert (v == qkv[:, 2].astype(np.float64)).all()
+    # independent route: rotate a normalised vector pair by pair with explicit cos/sin
+    for name, got, src, g in (("q", q, qkv[:, 0], gq), ("k", k, qkv[:, 1], gk)):
+        xs = src.astype(np.float64)
+        xn = xs / np.sqrt((xs ** 2).mean(-1, keepdims=True) + 1e-5) * g
+        want = np.empty_like(xn)
+        for i in range(n):
+            for j in range(D // 2):
+                a, kk, na = (0, j, 2) if j < 2 else ((1, 0, 1) if j == 2 else (2, 0, 1))
+                ang = pos[i, a] * 100.0 ** (-kk / na)
+                c, s = math.cos(ang), math.sin(ang)
+                want[i, :, 2 * j] = xn[i, :, 2 * j] * c - xn[i, :, 2 * j + 1] * s
+                want[i, :, 2 * j + 1] = xn[i, :, 2 * j] * s + xn[i, :, 2 * j + 1] * c
+        assert np.abs(got - want).max() <= 1e-12, name

@@ -219,3 +219,77 @@ def test_update_mutant_is_caught(cls):
     assert _caught(pins.pin_update_rule, cls) or \
         _caught(pins.pin_window_equals_full, cls, oracle.window_attention, oracle.prefix_attention,
                 oracle.window_full_attention), cls.__name__
+
+
+# ---------------------------------------------------------------- qk-RMSNorm + rotary embedding
+
+def _rms_variant(kind):
+    def rms_norm(x, gamma, eps):
+        x = np.asarray(x, dtype=np.float64)
+        ms = np.sum(x * x, axis=-1, keepdims=True) if kind == "sum" else np.mean(x * x, axis=-1, keepdims=True)
+        if kind == "eps_outside":
+            return x / (np.sqrt(ms) + eps) * np.asarray(gamma, dtype=np.float64)
+        if kind == "no_gamma":
+            return x / np.sqrt(ms + eps)
+        return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+    return rms_norm
+
+
+@pytest.mark.parametrize("kind", ["sum", "eps_outside", "no_gamma"])
+def test_rms_norm_mutant_is_caught(kind):
+    assert _caught(pins.pin_rms_norm, _rms_variant(kind)), kind
+
+
+def _rope_variant(kind):
+    from oracle.qk_prep import rope_angles
+
+    def rope(x, pos, sections, base):
+        x = np.asarray(x, dtype=np.float64)
+        if kind == "exponent":
+            pos_ = np.asarray(pos, dtype=np.float64)
+            cols = []
+            for a, n_a in enumerate(sections):
+                k = np.arange(n_a, dtype=np.float64)
+                cols.append(pos_[:, a:a + 1] * np.power(float(base), -2 * k / n_a)[None, :])
+            ang = np.concatenate(cols, axis=1)[:, None, :]
+        elif kind == "axes_swapped":
+            ang = rope_angles(np.asarray(pos)[:, [1, 0, 2]], sections, base)[:, None, :]
+        else:
+            ang = rope_angles(pos, sections, base)[:, None, :]
+        c, s = np.cos(ang), np.sin(ang)
+        if kind == "sign":
+            s = -s
+        out = np.empty_like(x)
+        if kind == "rotate_half":
+            h = x.shape[-1] // 2
+            a, b = x[..., :h], x[..., h:]
+            out[..., :h] = a * c - b * s
+            out[..., h:] = a * s + b * c
+            return out
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * c - b * s
+        out[..., 1::2] = a * s + b * c
+        return out
+    return rope
+
+
+@pytest.mark.parametrize("kind", ["exponent", "axes_swapped", "sign", "rotate_half"])
+def test_rope_mutant_is_caught(kind):
+    rp = _rope_variant(kind)
+    assert _caught(pins.pin_rope_closed_form, rp) or _caught(pins.pin_rope_relative, rp) or \
+        _caught(pins.pin_rope_sections, rp), kind
+
+
+def _prep_rotate_then_norm(qkv, pos, gamma_q, gamma_k, eps, sections, base, dtype):
+    q, k, v = (widen(qkv[:, i], dtype) for i in range(3))
+    return (oracle.rms_norm(oracle.rope(q, pos, sections, base), gamma_q, eps),
+            oracle.rms_norm(oracle.rope(k, pos, sections, base), gamma_k, eps), v)
+
+
+def _prep_shared_gain(qkv, pos, gamma_q, gamma_k, eps, sections, base, dtype):
+    return oracle.prep_qkv(qkv, pos, gamma_q, gamma_q, eps, sections, base, dtype)
+
+
+@pytest.mark.parametrize("fn", [_prep_rotate_then_norm, _prep_shared_gain], ids=lambda f: f.__name__)
+def test_prep_mutant_is_caught(fn):
+    assert _caught(pins.pin_prep_qkv, fn, oracle.rms_norm, oracle.rope)

@@ -99,3 +99,23 @@ def test_window_chunking_free():
 
 def test_update_rule():
     pins.pin_update_rule(oracle.StreamingCache)
+
+
+def test_rms_norm():
+    pins.pin_rms_norm(oracle.rms_norm)
+
+
+def test_rope_closed_form():
+    pins.pin_rope_closed_form(oracle.rope)
+
+
+def test_rope_relative_positions():
+    pins.pin_rope_relative(oracle.rope)
+
+
+def test_rope_sections():
+    pins.pin_rope_sections(oracle.rope)
+
+
+def test_prep_qkv():
+    pins.pin_prep_qkv(oracle.prep_qkv, oracle.rms_norm, oracle.rope)
