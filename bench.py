@@ -13,6 +13,11 @@ W history chunks in place, append the current chunk, and the attention of all mo
 (history + current) over the whole window ("3.1.2 Historical Context and Temporal
 Consistency", prefix cache).
 
+`--workload c1p` runs c1 chunk-steps whose chunk enters through the fused append
+(sr_kvcache_append_qkv: qk-RMSNorm, rotary embedding at stream-absolute positions and the
+cache write in one kernel, "3.2 Fast Causal H3 VAE", iteration 6) and reports that kernel's
+HBM roofline beside the attention one.
+
 Prints one JSON line (see --help).  Inputs are seeded synthetic tensors resident in HBM
 before the timed region; timing brackets exactly --steps steps with device syncs, and HIP
 events around each attention launch give the kernel's average duration for the roofline.
@@ -43,10 +48,18 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC = {
     "c1": {"fetch_kib": 220291.4, "write_kib": 103829.5,
            "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
+    "c1p": {"fetch_kib": 220364.0, "write_kib": 103828.0,
+            "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
     "c1w": {"fetch_kib": 320250.9, "write_kib": 125276.1,
             "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
+# The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
+PREP_TRAFFIC = {
+    "c1p": {"fetch_kib": 42276.0, "write_kib": 84912.0,
+            "kv_sha256": "ea9510bd8e362d889f855546f39422a15c81623ed90088ae213f072f05f6867d"},
+}
+KV_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "kv_kernels.hip")
 
 
 def attention_source_sha256():
@@ -59,6 +72,15 @@ def measured_traffic(workload):
     """Scaled bytes per launch for `workload`, or None if not measured on this kernel source."""
     t = TRAFFIC.get(workload)
     if not t or t["fetch_kib"] is None or t["attention_sha256"] != attention_source_sha256():
+        return None
+    return (2.0 * t["fetch_kib"] + 1.0 * t["write_kib"]) * 1024.0
+
+
+def measured_prep_traffic(workload):
+    """Scaled bytes per fused-append launch, or None if not measured on this kernel source."""
+    import hashlib
+    t = PREP_TRAFFIC.get(workload)
+    if not t or t["kv_sha256"] != hashlib.sha256(open(KV_SRC, "rb").read()).hexdigest():
         return None
     return (2.0 * t["fetch_kib"] + 1.0 * t["write_kib"]) * 1024.0
 
@@ -284,6 +306,146 @@ def run_window(args, w):
     return res
 
 
+# Workloads whose chunks enter through the fused append (qk-RMSNorm + rotary + cache write).
+PREP_WORKLOADS = ("c1p",)
+PEAK_HBM_GBPS = 8000.0
+# Latent grid of the 832x480 workloads: 52 x 30 tokens per latent frame.
+GRID_W, FRAME_TOKENS = 52, 1560
+
+
+def prep_bytes(w):
+    """Algorithmic bytes of one fused append: read qkv [n][3][H][D] and the positions; write the
+    prepared queries [n][H][D] and the K/V pages of the slot (with its zero tail)."""
+    es = 2 if w.dtype == "bf16" else 4
+    slot_tokens = math.ceil(w.chunk / 128) * 128
+    return es * w.heads * w.head_dim * (3 * w.chunk + w.chunk + 2 * slot_tokens) + 12 * w.chunk
+
+
+def run_prep(args, w):
+    """Fused-append step: evict, append the chunk's qkv projection through the fused kernel
+    (queries and keys RMS-normalised and rotated at their stream-absolute positions), then
+    chunk attention of the prepared queries."""
+    import torch
+    import synth
+    import chunk_causal_attention_amd as sr
+    from synth.torch_io import to_dev
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    pk, pv = (to_dev(x, w.dtype) for x in synth.SessionStream(w).persistent())
+    n_sets = w.window + 2
+    qkvs = [to_dev(synth.qkv_inputs(w, w.chunk, chunk=j), w.dtype) for j in range(n_sets)]
+    frames = w.chunk // FRAME_TOKENS
+    poss = [torch.from_numpy(synth.latent_positions(w.chunk, FRAME_TOKENS, GRID_W, frames * j)).to(dev)
+            for j in range(n_sets)]
+    gq, gk = (torch.from_numpy(g).to(dev) for g in synth.prep_gains(w))
+    prep = sr.qk_prep((w.head_dim // 8, 3 * w.head_dim // 16, 3 * w.head_dim // 16), 10000.0, 1e-6)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
+                        sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
+    q = torch.empty((w.chunk, w.heads, w.head_dim), dtype=qkvs[0].dtype, device=dev)
+    t_init = time.perf_counter()
+    layers = []
+    ws = None if args.no_split else sr.workspace_for(cfg)
+    for _ in range(args.layers):
+        c = sr.KVCache(cfg, pk, pv, workspace=ws)
+        for j in range(w.window + 1):
+            c.append_qkv(j, qkvs[j % n_sets], poss[j % n_sets], gq, gk, prep, q_out=q)
+        layers.append({"cache": c, "next": w.window + 1})
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t_init
+    out = torch.empty_like(q)
+    lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device=dev)
+    ev_pairs = []
+
+    def step(i, timed):
+        L = layers[i % len(layers)]
+        c = L["cache"]
+        cid = L["next"]
+        L["next"] += 1
+        if w.window > 0:
+            c.evict()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record()
+        c.append_qkv(cid, qkvs[cid % n_sets], poss[cid % n_sets], gq, gk, prep, q_out=q)
+        if timed:
+            e[1].record()
+        c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+        if timed:
+            e[2].record()
+            ev_pairs.append(e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_prep = np.array([a.elapsed_time(b) for a, b, _ in ev_pairs])
+    t_attn = np.array([b.elapsed_time(c) for _, b, c in ev_pairs])
+    ms_step = elapsed * 1e3 / args.steps
+    F = attention_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
+    prep_gbps = prep_bytes(w) / (t_prep.mean() * 1e-3) / 1e9
+    res = {
+        "metric": "ms per chunk-step & attention TFLOP/s (frac of bf16 MFMA peak), 1 MI355X",
+        "value": round(F / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: chunk-step through the fused append, {w.heads} heads x {w.head_dim}, "
+                        f"{w.persistent} persistent + {w.window}x{w.chunk} history + {w.chunk} current tokens",
+            "heads": w.heads, "head_dim": w.head_dim, "queries": w.chunk, "keys_visible": w.visible_keys,
+            "layers_cycled": args.layers,
+            "step": "evict + append_qkv (qk-RMSNorm + rotary + cache write) + chunk_attention",
+            "schedule": "whole items" if args.no_split else "key tiles split evenly over the CUs",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": measured_traffic(w.name),
+        },
+        "prep_roofline": {
+            "bound": "hbm",
+            "achieved": round(prep_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(prep_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": measured_prep_traffic(w.name),
+        },
+        "ms_attention": round(float(t_attn.mean()), 4),
+        "ms_attention_p10_p50_p90": [round(float(np.percentile(t_attn, p)), 4) for p in (10, 50, 90)],
+        "ms_append_qkv": round(float(t_prep.mean()), 4),
+        "ms_append_qkv_p10_p50_p90": [round(float(np.percentile(t_prep, p)), 4) for p in (10, 50, 90)],
+        "append_qkv_bytes": prep_bytes(w),
+        "attention_gflop_per_call": round(F / 1e9, 3),
+        "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
+    }
+    for L in layers:
+        L["cache"].close()
+    if args.copy_calibration:
+        copy_calibration(res, torch, dev)
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    return res
+
+
 def run(args):
     import torch
     import synth
@@ -293,6 +455,8 @@ def run(args):
     w = synth.get_workload(args.workload)
     if w.name in WINDOW_WORKLOADS:
         return run_window(args, w)
+    if w.name in PREP_WORKLOADS:
+        return run_prep(args, w)
     if not w.single_step:
         raise SystemExit(f"workload {w.name} is a parity case, not a bench workload")
     torch.cuda.init()
@@ -407,7 +571,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="c1",
-                    help="c1 (default), c3, c4, c1s, c4s; c1w: the page-literal window variant at c1 shapes")
+                    help="c1 (default), c3, c4, c1s, c4s; c1w: the page-literal window variant at c1 shapes; "
+                         "c1p: c1 chunk-steps entering through the fused qk-RMSNorm + rotary append")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-split", action="store_true",

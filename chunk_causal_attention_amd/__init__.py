@@ -52,6 +52,15 @@ class sr_segment(ctypes.Structure):
                 ("page", ctypes.c_int32), ("length", ctypes.c_int32)]
 
 
+class sr_qk_prep(ctypes.Structure):
+    _fields_ = [("rope_sections", ctypes.c_int32 * 3), ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+def qk_prep(sections, base=10000.0, eps=1e-6):
+    """sr_qk_prep for rotation-pair sections (t, y, x), frequency base and RMSNorm epsilon."""
+    return sr_qk_prep((ctypes.c_int32 * 3)(*sections), float(base), float(eps))
+
+
 _lib = None
 
 
@@ -80,6 +89,7 @@ def load():
         "sr_window_attention": [P, I32, P, I32, P, P, F32, P],
         "sr_prefix_attention": [P, I32, P, P, P, F32, P],
         "sr_kvcache_update_chunk": [P, I64, P, P, I32, P],
+        "sr_kvcache_append_qkv": [P, I64, P, P, I32, P, P, ctypes.POINTER(sr_qk_prep), P, P],
         "sr_kvcache_gather": [P, I32, P, P, I32, ctypes.POINTER(I32), P],
         "sr_kvcache_destroy": [P],
         "sr_attention_workspace_bytes": [cfgp, I32, ctypes.POINTER(SZ)],
@@ -153,6 +163,12 @@ def sr_kvcache_init(cfg, pool, persistent_k=None, persistent_v=None, stream=None
 def sr_kvcache_append_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
     n = k.shape[0] if n_tokens is None else n_tokens
     _check(load().sr_kvcache_append_chunk(h, chunk_id, _ptr(k), _ptr(v), n, _stream(stream)))
+
+
+def sr_kvcache_append_qkv(h, chunk_id, qkv, positions, q_gain, k_gain, prep, q_out, n_tokens=None, stream=None):
+    n = qkv.shape[0] if n_tokens is None else n_tokens
+    _check(load().sr_kvcache_append_qkv(h, chunk_id, _ptr(qkv), _ptr(positions), n, _ptr(q_gain), _ptr(k_gain),
+                                        ctypes.byref(prep), _ptr(q_out), _stream(stream)))
 
 
 def sr_kvcache_evict(h):
@@ -303,6 +319,25 @@ class KVCache:
         self._check_tensor(k, (k.shape[0], self.cfg.num_heads, self.cfg.head_dim))
         self._check_tensor(v, k.shape)
         sr_kvcache_update_chunk(self.h, chunk_id, k, v, k.shape[0], stream)
+
+    def append_qkv(self, chunk_id, qkv, positions, q_gain, k_gain, prep, q_out=None, stream=None):
+        """Fused append after the qkv projection: qkv [n][3][H][D], positions int32 [n][3],
+        gains fp32 [D]; writes the prepared K and V to the chunk's slot and returns the
+        prepared queries [n][H][D]."""
+        import torch
+        H, D = self.cfg.num_heads, self.cfg.head_dim
+        self._check_tensor(qkv, (qkv.shape[0], 3, H, D))
+        n = qkv.shape[0]
+        if positions.dtype != torch.int32 or tuple(positions.shape) != (n, 3) or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 [n][3] device tensor")
+        for g in (q_gain, k_gain):
+            if g.dtype != torch.float32 or tuple(g.shape) != (D,) or not g.is_contiguous():
+                raise ValueError("gains must be contiguous float32 [D] device tensors")
+        if q_out is None:
+            q_out = torch.empty((n, H, D), dtype=self.dtype, device=qkv.device)
+        self._check_tensor(q_out, (n, H, D))
+        sr_kvcache_append_qkv(self.h, chunk_id, qkv, positions, q_gain, k_gain, prep, q_out, n, stream)
+        return q_out
 
     def evict(self):
         return sr_kvcache_evict(self.h)

@@ -133,6 +133,54 @@ sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k
   return SR_OK;
 }
 
+sr_status sr_kvcache_append_qkv(sr_kvcache* c, int64_t chunk_id, const void* qkv, const int32_t* positions,
+                                int32_t n_tokens, const float* q_gain, const float* k_gain, const sr_qk_prep* prep,
+                                void* q_out, void* stream) {
+  sr::clear_error();
+  if (!c || !prep) return sr::fail(SR_E_INVALID, "null cache or parameters");
+  if (!qkv || !q_out || !sr::aligned16(qkv) || !sr::aligned16(q_out))
+    return sr::fail(SR_E_INVALID, "qkv and q_out must be non-null and 16-byte aligned");
+  if (!positions || !q_gain || !k_gain || (reinterpret_cast<uintptr_t>(positions) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q_gain) & 3u) || (reinterpret_cast<uintptr_t>(k_gain) & 3u))
+    return sr::fail(SR_E_INVALID, "positions and gains must be non-null and 4-byte aligned");
+  const sr::Layout& L = c->ring.L;
+  const int32_t pairs = L.D / 2;
+  const int32_t* sec = prep->rope_sections;
+  if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != pairs)
+    return sr::fail(SR_E_INVALID, "rope_sections (%d, %d, %d) must be >= 0 and sum to head_dim / 2 = %d", sec[0],
+                    sec[1], sec[2], pairs);
+  if (!(prep->rope_base > 1.0f) || !std::isfinite(prep->rope_base))
+    return sr::fail(SR_E_INVALID, "rope_base must be finite and > 1");
+  if (!(prep->rms_eps >= 0.0f) || !std::isfinite(prep->rms_eps))
+    return sr::fail(SR_E_INVALID, "rms_eps must be finite and >= 0");
+  int32_t slot;
+  int64_t committed;
+  sr_status st = sr::plan_append(c->ring, chunk_id, n_tokens, &slot, &committed);
+  if (st != SR_OK) return st;
+  // q_out [n][H][D] must not overlap the qkv rows the kernel still reads.
+  const size_t row = size_t(L.H) * L.D * L.esize;
+  const char* a0 = static_cast<const char*>(qkv);
+  const char* b0 = static_cast<const char*>(q_out);
+  if (b0 < a0 + 3 * row * n_tokens && a0 < b0 + row * n_tokens)
+    return sr::fail(SR_E_INVALID, "q_out must not overlap qkv");
+  sr::RopeTable rt{};
+  for (int32_t j = 0, a = 0, k = 0; j < pairs; ++j, ++k) {
+    while (k >= sec[a]) {
+      k = 0;
+      ++a;
+    }
+    rt.axis[j] = a;
+    rt.theta[j] = std::pow(double(prep->rope_base), -double(k) / double(sec[a]));
+  }
+  st = device_status(sr::launch_prep_append(L, c->pool, qkv, positions, n_tokens, q_gain, k_gain, prep->rms_eps, rt,
+                                            q_out, L.slot_page(slot), L.pages_per_slot,
+                                            static_cast<hipStream_t>(stream)),
+                     "qkv append");
+  if (st != SR_OK) return st;
+  sr::commit_append(c->ring, chunk_id, n_tokens);
+  return SR_OK;
+}
+
 sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id) {
   sr::clear_error();
   if (!c) return sr::fail(SR_E_INVALID, "null cache");

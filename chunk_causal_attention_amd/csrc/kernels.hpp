@@ -174,6 +174,20 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_append(const Layout& L, void* pool, const void* k, const void* v, int32_t n, int32_t page0,
                          int32_t npages, hipStream_t st);
 
+// Rotary table of one call: for rotation pair j (features 2j, 2j+1), the position axis it
+// follows (0 time, 1 y, 2 x) and its angle per unit of position.
+struct RopeTable {
+  double theta[64];
+  int32_t axis[64];
+};
+
+// Fused qk-RMSNorm + rotary embedding + cache write: qkv [n][3][H][D], positions [n][3];
+// writes the normalised, rotated queries to qout [n][H][D] and the normalised, rotated keys
+// and the values into pages [page0, page0 + npages) of every head (zeros past token n).
+hipError_t launch_prep_append(const Layout& L, void* pool, const void* qkv, const int32_t* pos, int32_t n,
+                              const float* gq, const float* gk, float eps, const RopeTable& rt, void* qout,
+                              int32_t page0, int32_t npages, hipStream_t st);
+
 // Writes the logical sequence of `t` ([ntok][H][D], token-major) to kout / vout.
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
                          hipStream_t st);

@@ -90,6 +90,144 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
   }
 }
 
+// ---- fused qk-RMSNorm + rotary embedding + cache write ---------------------------------
+// StreamRender-H3 project page, "3.2 Fast Causal H3 VAE": after the qkv projection, qk-norm,
+// the rotary embedding and the K/V cache write run as one kernel (iteration 6); each token
+// gets its rotary position once, when it is written (inference items), at its stream-absolute
+// position (iteration 4).  Per (token, head): y = x / sqrt(mean(x^2) + eps) * gain, then
+// rotation pair j = (y_2j, y_2j+1) turns by pos[axis_j] * theta_j.
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+// The E values of one 16-byte piece, widened to fp32, and back (round to nearest even).
+__device__ __forceinline__ void widen_piece(const u32x4_t& w, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen_piece(const u32x4_t& w, float (&f)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+}
+__device__ __forceinline__ unsigned bf16_rne(float x) {
+  const unsigned u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN -> quiet NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ u32x4_t narrow_piece(const float (&f)[8]) {
+  u32x4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = bf16_rne(f[2 * i]) | (bf16_rne(f[2 * i + 1]) << 16);
+  return w;
+}
+__device__ __forceinline__ u32x4_t narrow_piece(const float (&f)[4]) {
+  return u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+}
+
+// RMS-normalises and rotates one piece (features x*E .. x*E+E-1) of one (token, head) row;
+// the CPR lanes holding the pieces of the row are consecutive and reduce together.  cs holds
+// the row's (cos, sin) per rotation pair.
+template <int E, int CPR, int D>
+__device__ __forceinline__ void prep_piece(float (&f)[E], int x, const float* __restrict__ gain, float eps,
+                                           const float2* cs) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+#pragma unroll
+  for (int m = CPR / 2; m >= 1; m /= 2) ss += __shfl_xor(ss, m, CPR);
+  const float scale = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+  for (int e = 0; e < E; ++e) f[e] = f[e] * scale * gain[x * E + e];
+#pragma unroll
+  for (int e = 0; e < E; e += 2) {
+    const float2 r = cs[(x * E + e) / 2];
+    const float a = f[e], b = f[e + 1];
+    f[e] = a * r.x - b * r.y;
+    f[e + 1] = a * r.y + b * r.x;
+  }
+}
+
+constexpr int kPrepHeads = 4;  // heads per workgroup of the fused append (they share the rotations)
+
+// Workgroup (64-token half page, kPrepHeads heads); qkv [n][3][H][D], positions [n][3].  The
+// (cos, sin) of every (token, rotation pair) of the tile is computed once, into LDS: the angle
+// pos * theta in fp64, reduced to [-pi, pi], then the fp32 sine and cosine.  Per head, Q goes
+// straight to q_out; normalised, rotated K and plain V go through LDS into the page, as in
+// append_kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prep_append_kernel(const T* __restrict__ qkv, const int32_t* __restrict__ pos,
+                                                          int n, int H, const float* __restrict__ gq,
+                                                          const float* __restrict__ gk, float eps, RopeTable rt,
+                                                          T* __restrict__ qout, T* __restrict__ kpool,
+                                                          T* __restrict__ vpool, int total_pages, int page0) {
+  constexpr int E = 16 / int(sizeof(T));
+  constexpr int CPR = D / E;
+  constexpr int PITCH = D + E;
+  constexpr int NP = D / 2;          // rotation pairs
+  constexpr int CSP = NP + 1;        // LDS pitch of a token's rotation row (float2), padded
+  static_assert(64 % CPR == 0, "the lanes of one row stay inside a wave");
+  __shared__ __align__(16) T ktile[kAppendTokens * PITCH];
+  __shared__ __align__(16) T vtile[kAppendTokens * PITCH];
+  __shared__ float2 rot[kAppendTokens * CSP];
+
+  const int t0 = blockIdx.x * kAppendTokens;
+  const int tp = t0 % SR_PAGE_TOKENS;
+  const u32x4_t z = {0, 0, 0, 0};
+  const size_t hd = size_t(H) * D;
+
+  for (int i = threadIdx.x; i < kAppendTokens * NP; i += blockDim.x) {
+    const int r = i / NP, j = i % NP, t = t0 + r;
+    const int p = t < n ? pos[size_t(t) * 3 + rt.axis[j]] : 0;
+    const double ang = double(p) * rt.theta[j];
+    const double red = ang - 6.283185307179586 * __builtin_rint(ang * 0.15915494309189535);
+    float sn, cs;
+    sincosf(float(red), &sn, &cs);
+    rot[r * CSP + j] = make_float2(cs, sn);
+  }
+  __syncthreads();
+
+  for (int hh = 0; hh < kPrepHeads; ++hh) {
+    const int h = blockIdx.y * kPrepHeads + hh;
+    if (h >= H) break;  // uniform
+    const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
+    // Every lane of a row group runs the reduction, also for rows past n (their values are
+    // zero and their results are dropped).
+    for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
+      const int r = ci / CPR, x = ci % CPR, t = t0 + r;
+      const bool ok = t < n;
+      const size_t src = (size_t(ok ? t : 0) * 3 * H + h) * D + x * E;
+      const u32x4_t wq = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src) : z;
+      const u32x4_t wk = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + hd) : z;
+      const u32x4_t wv = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + 2 * hd) : z;
+      float fq[E], fk[E];
+      widen_piece(wq, fq);
+      widen_piece(wk, fk);
+      prep_piece<E, CPR, D>(fq, x, gq, eps, rot + r * CSP);
+      prep_piece<E, CPR, D>(fk, x, gk, eps, rot + r * CSP);
+      if (ok) *reinterpret_cast<u32x4_t*>(qout + (size_t(t) * H + h) * D + x * E) = narrow_piece(fq);
+      *reinterpret_cast<u32x4_t*>(ktile + r * PITCH + x * E) = ok ? narrow_piece(fk) : z;
+      *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = wv;
+    }
+    __syncthreads();
+    T* kpage = kpool + page * SR_PAGE_TOKENS * D;
+    for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
+      const int x = ci / kAppendTokens, r = ci % kAppendTokens;
+      *reinterpret_cast<u32x4_t*>(kpage + (size_t(x) * SR_PAGE_TOKENS + row_pos<T>(tp + r)) * E) =
+          *reinterpret_cast<const u32x4_t*>(ktile + r * PITCH + x * E);
+    }
+    T* vpage = vpool + page * SR_PAGE_TOKENS * D;
+    constexpr int GROUPS = kAppendTokens / E;
+    for (int ci = threadIdx.x; ci < GROUPS * D; ci += blockDim.x) {
+      const int g = ci / D, d = ci % D;
+      *reinterpret_cast<u32x4_t*>(vpage + (size_t(tp / E + g) * D + d) * E) =
+          column_piece(vtile + g * E * PITCH + d, PITCH);
+    }
+    __syncthreads();  // the tiles are refilled for the next head
+  }
+}
+
 // Thread per (token, feature).  Test/debug path; not tuned.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool, const T* __restrict__ vpool,
@@ -127,6 +265,18 @@ hipError_t append_t(const Layout& L, void* pool, const void* k, const void* v, i
 }
 
 template <typename T, int D>
+hipError_t prep_append_t(const Layout& L, void* pool, const void* qkv, const int32_t* pos, int32_t n, const float* gq,
+                         const float* gk, float eps, const RopeTable& rt, void* qout, int32_t page0, int32_t npages,
+                         hipStream_t st) {
+  T* kpool = static_cast<T*>(pool);
+  T* vpool = reinterpret_cast<T*>(static_cast<char*>(pool) + L.half_bytes);
+  dim3 grid(npages * (SR_PAGE_TOKENS / kAppendTokens), (L.H + kPrepHeads - 1) / kPrepHeads);
+  hipLaunchKernelGGL((prep_append_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(qkv), pos, n, L.H,
+                     gq, gk, eps, rt, static_cast<T*>(qout), kpool, vpool, L.total_pages, page0);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
 hipError_t gather_t(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
                     hipStream_t st) {
   const T* kpool = static_cast<const T*>(pool);
@@ -155,6 +305,16 @@ hipError_t launch_append(const Layout& L, void* pool, const void* k, const void*
     return L.D == 128 ? append_t<uint16_t, 128>(L, pool, k, v, n, page0, npages, st)
                       : append_t<uint16_t, 64>(L, pool, k, v, n, page0, npages, st);
   return append_t<float, 64>(L, pool, k, v, n, page0, npages, st);
+}
+
+hipError_t launch_prep_append(const Layout& L, void* pool, const void* qkv, const int32_t* pos, int32_t n,
+                              const float* gq, const float* gk, float eps, const RopeTable& rt, void* qout,
+                              int32_t page0, int32_t npages, hipStream_t st) {
+  if (npages == 0) return hipSuccess;
+  if (L.dtype == SR_BF16)
+    return L.D == 128 ? prep_append_t<uint16_t, 128>(L, pool, qkv, pos, n, gq, gk, eps, rt, qout, page0, npages, st)
+                      : prep_append_t<uint16_t, 64>(L, pool, qkv, pos, n, gq, gk, eps, rt, qout, page0, npages, st);
+  return prep_append_t<float, 64>(L, pool, qkv, pos, n, gq, gk, eps, rt, qout, page0, npages, st);
 }
 
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,

@@ -167,6 +167,35 @@ sr_status sr_kvcache_init(const sr_kvcache_config* cfg, void* pool, size_t pool_
 sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v,
                                   int32_t n_tokens, void* stream);
 
+/* Parameters of the qk preparation done by sr_kvcache_append_qkv. */
+typedef struct {
+  int32_t rope_sections[3]; /* rotation pairs following position axis t, y, x (in that order of
+                               pairs); each >= 0, summing to head_dim / 2 */
+  float rope_base;          /* > 1: pair k of a section of n pairs turns by pos * base^(-k/n) */
+  float rms_eps;            /* >= 0, added to the mean square */
+} sr_qk_prep;
+
+/* Fused append after the qkv projection ("3.2 Fast Causal H3 VAE", iteration 6: qk-norm, the
+ * rotary embedding and the K/V cache write in one kernel after the qkv GEMM; inference items:
+ * each new token gets its rotary position once, when it is written; iteration 4: positions are
+ * stream-absolute, so scores depend only on position differences).
+ *   qkv        device [n_tokens][3][H][D] in the cache dtype: q, k, v of each token.
+ *   positions  device int32 [n_tokens][3]: (t, y, x) of each token, t the stream-absolute
+ *              latent-frame index.
+ *   q_gain, k_gain  device fp32 [D]: RMSNorm gains of q and k (shared by the heads).
+ *   q_out      device [n_tokens][H][D] in the cache dtype (must not overlap qkv): the prepared
+ *              queries, for the attention call that follows.
+ * For q and k of every (token, head): y = x / sqrt(mean(x^2) + rms_eps) * gain, then rotation
+ * pair j = (y_2j, y_2j+1) in section a (pairs assigned to t, y, x in order) at index k within
+ * it turns by positions[a] * rope_base^(-k / rope_sections[a]).  Computed in fp32 and rounded
+ * to the cache dtype (nearest even).  The prepared K and the unchanged V are then appended
+ * exactly as by sr_kvcache_append_chunk (same ring rules and errors).  SR_E_INVALID, with
+ * nothing enqueued, for bad pointers or parameters.  The caller may reuse qkv / positions
+ * once the stream has passed the call. */
+sr_status sr_kvcache_append_qkv(sr_kvcache* c, int64_t chunk_id, const void* qkv, const int32_t* positions,
+                                int32_t n_tokens, const float* q_gain, const float* k_gain,
+                                const sr_qk_prep* prep, void* q_out, void* stream);
+
 /* Drops the oldest history chunk (host metadata only; nothing is enqueued). */
 sr_status sr_kvcache_evict(sr_kvcache* c, int64_t* evicted_chunk_id);
 

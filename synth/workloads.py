@@ -78,6 +78,9 @@ WORKLOADS = {
     # page-literal window variant at c1 shapes: the 3 x 4680 moving rows (2 history chunks and
     # the current one) attend to the whole window, 2072 + 14040 keys
     "c1w": Workload("c1w", 31, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, _SIGMA, _SIGMA),
+    # fused append at c1 shapes: the chunk's qkv projection output is normalised, rotated and
+    # written by one kernel before the chunk attention of the prepared queries
+    "c1p": Workload("c1p", 35, "bf16", 24, 128, 2072, 4680, 2, 4680, 1, 3, 1, _SIGMA, _SIGMA),
     # reduced shapes the oracle finishes in seconds; they still span several tiles and ragged tails
     "t_stream": Workload("t_stream", 21, "bf16", 3, 128, 300, 600, 2, 600, 2, 5, 2, 1.0, 1.0,
                          ar_rho=0.9, single_step=False),
@@ -237,6 +240,31 @@ class WindowStream:
                                     step=s))
                 yield {"chunk": c, "step": s, "bank": s % w.banks, "evict_before": evict and s == 0,
                        "history": hist, "k": k, "v": v, "q": q}
+
+
+def latent_positions(n_tokens, frame_tokens, grid_w, first_frame):
+    """int32 [n][3] (t, y, x) of a chunk's tokens laid out frame by frame, row by row: token i
+    is in latent frame first_frame + i // frame_tokens (stream-absolute), at grid row
+    (i % frame_tokens) // grid_w and column i % grid_w."""
+    i = np.arange(n_tokens)
+    f = i % frame_tokens
+    return np.stack([first_frame + i // frame_tokens, f // grid_w, f % grid_w], axis=1).astype(np.int32)
+
+
+def qkv_inputs(w, n_tokens, chunk=0, step=0):
+    """Seeded output of a qkv projection: storage array [n][3][H][D] (q and k ~ N(0, 1), v with
+    the workload's v_std)."""
+    shape = (n_tokens, 3, w.heads, w.head_dim)
+    x = _draw(w, "QKV", shape, 1.0, chunk=chunk, step=step)
+    x[:, 2] *= w.v_std
+    return _store(w, x)
+
+
+def prep_gains(w):
+    """RMSNorm gains of q and k: fp32 [D] each, uniform-ish around 1 (drawn as 1 + 0.25 N(0,1))."""
+    gq = 1.0 + _draw(w, "GQ", (w.head_dim,), 0.25)
+    gk = 1.0 + _draw(w, "GK", (w.head_dim,), 0.25)
+    return gq.astype(np.float32), gk.astype(np.float32)
 
 
 def single_step_inputs(w):
