@@ -418,3 +418,160 @@ def pin_prep_qkv(prep_qkv, rms_norm, rope, seed=59):
                 want[i, :, 2 * j] = xn[i, :, 2 * j] * c - xn[i, :, 2 * j + 1] * s
                 want[i, :, 2 * j + 1] = xn[i, :, 2 * j] * s + xn[i, :, 2 * j + 1] * c
         assert np.abs(got - want).max() <= 1e-12, name
+
+
+# ---------------------------------------------------------------- MXFP6 / FP8 quantization pins
+# The formats are those of the OCP Microscaling (MX) specification v1.0: the value sets
+# below are the ones it publishes; the rounding rule is the nearest value, ties to the
+# even mantissa, with saturation.  Each pin takes the oracle.mx module (or a copy with a
+# planted mistake) as `m`.
+
+# Magnitudes of FP6 E2M3 codes 0..31 as the specification lists them: 8 subnormals in
+# steps of 1/8, then binades [1, 2), [2, 4), [4, 8) of 8 values each; largest 7.5.
+E2M3_MAGNITUDES = [0.0, 0.125, 0.25, 0.375, 0.5, 0.625, 0.75, 0.875,
+                   1.0, 1.125, 1.25, 1.375, 1.5, 1.625, 1.75, 1.875,
+                   2.0, 2.25, 2.5, 2.75, 3.0, 3.25, 3.5, 3.75,
+                   4.0, 4.5, 5.0, 5.5, 6.0, 6.5, 7.0, 7.5]
+
+
+def pin_e2m3_values(m):
+    """All 64 FP6 E2M3 codes decode to the published value set (sign bit 5 on top)."""
+    for c in range(32):
+        pos, neg = m.element_value(c, m.E2M3), m.element_value(32 + c, m.E2M3)
+        assert pos == E2M3_MAGNITUDES[c] and not math.copysign(1.0, pos) < 0, c
+        assert neg == -E2M3_MAGNITUDES[c] and math.copysign(1.0, neg) < 0, c
+
+
+def pin_e4m3_values(m):
+    """All 256 FP8 E4M3 codes decode as torch's float8_e4m3fn does (NaN at S.1111.111)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([m.element_value(c, m.E4M3) for c in range(256)])
+    assert (np.isnan(got) == np.isnan(ref)).all()
+    ok = ~np.isnan(ref)
+    assert (got[ok] == ref[ok]).all() and (np.signbit(got[ok]) == np.signbit(ref[ok])).all()
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+
+
+def _nearest_codes(m, fmt, x):
+    """Brute force: the code whose value is nearest to x, ties to the even code (the
+    mantissa's last bit), magnitudes past the largest value saturating, sign from x."""
+    width = 1 + fmt[0] + fmt[1]
+    half = 1 << (width - 1)
+    mags = np.array([m.element_value(c, fmt) for c in range(half)])
+    ok = ~np.isnan(mags)
+    idx = np.arange(half)[ok]
+    mags = mags[ok]
+    a = np.abs(x)[:, None]
+    d = np.abs(a - mags[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among tied candidates prefer the even code
+    pick = np.where(cand & (idx[None, :] % 2 == 0), idx[None, :], -1).max(axis=1)
+    single = cand.sum(axis=1) == 1
+    pick = np.where(single, idx[np.argmax(cand, axis=1)], pick)
+    return (pick | np.where(np.signbit(x), half, 0)).astype(np.int64)
+
+
+def _encode_samples(m, fmt, r):
+    width = 1 + fmt[0] + fmt[1]
+    mags = np.array([m.element_value(c, fmt) for c in range(1 << (width - 1))])
+    mags = np.sort(mags[~np.isnan(mags)])
+    mids = (mags[1:] + mags[:-1]) / 2                      # exact ties
+    tiny, big = mags[1], mags[-1]
+    logu = np.exp2(r.uniform(np.log2(tiny) - 3, np.log2(big) + 2, 3000))
+    x = np.concatenate([mags, mids, logu, mids * (1 + 1e-12), mids * (1 - 1e-12), [0.0, big * 1.06, big * 1e6]])
+    sign = np.where(r.random(x.size) < 0.5, -1.0, 1.0)
+    return np.concatenate([x * sign, [-0.0]])
+
+
+def pin_encode_nearest(m, seed=61):
+    """encode() picks the nearest value, ties to even, saturating, sign kept -- checked by
+    brute force over every code of both formats, on exact ties and random magnitudes."""
+    r = _rng(seed)
+    for fmt in (m.E2M3, m.E4M3):
+        x = _encode_samples(m, fmt, r)
+        got = m.encode(x, fmt).astype(np.int64)
+        want = _nearest_codes(m, fmt, x)
+        assert (got == want).all(), (fmt, x[got != want][:5], got[got != want][:5], want[got != want][:5])
+
+
+def pin_e4m3_encode_torch(m, seed=67):
+    """Within +-448, FP8 E4M3 rounding agrees with torch's float32 -> float8_e4m3fn conversion
+    (nearest, ties to even), bit for bit, including subnormals and signed zeros."""
+    import torch
+    r = _rng(seed)
+    x = np.concatenate([r.standard_normal(4000) * np.exp2(r.integers(-12, 9, 4000)),
+                        r.uniform(-448, 448, 1000), [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 447.9, -448.0]])
+    x = x.astype(np.float32)
+    x = np.clip(x, -448, 448).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = m.encode(x, m.E4M3)
+    assert (got == ref).all(), (x[got != ref][:5], got[got != ref][:5], ref[got != ref][:5])
+    assert (m.fp8_values(np.array([1000.0, -1e6, 460.0])) == [448.0, -448.0, 448.0]).all()
+
+
+def pin_mx_scale(m, seed=71):
+    """E8M0 block exponent: max |x| / 2^X lies in [4, 8) (E2M3's top binade), one exponent per
+    32 consecutive elements, clamped at -127 (also for an all-zero block)."""
+    r = _rng(seed)
+    n, D = 200, 128
+    x = r.standard_normal((n, D)) * np.exp2(r.integers(-100, 100, (n, 1)))
+    x[0, :32] = 0.0
+    x[1, :32] = r.uniform(-1, 1, 32) * 2.0 ** -140   # below the clamp
+    x[2:4, :32] = r.uniform(-1, 1, (2, 32)) * 2.0 ** 39
+    x[2, 5] = 2.0 ** 40                              # exact power of two as the block max
+    x[3, 7] = 2.0 ** 40 * (1 - 2.0 ** -30)           # just below a power of two
+    X = m.mx_scale_exponents(x)
+    assert X.shape == (n, D // 32)
+    amax = np.abs(x.reshape(n, D // 32, 32)).max(-1)
+    ok = amax > 2.0 ** -120
+    ratio = amax[ok] / np.exp2(X[ok])
+    assert (ratio >= 4).all() and (ratio < 8).all()
+    assert X[0, 0] == -127 and X[1, 0] == -127 and X[2, 0] == 38 and X[3, 0] == 37
+    # one element changes only its own block's exponent, and elements 31 / 32 belong to
+    # different blocks
+    y = x[10:11].copy()
+    y[0, 31] = 2.0 ** 60
+    Xy = m.mx_scale_exponents(y)
+    assert Xy[0, 0] == 58 and (Xy[0, 1:] == X[10, 1:]).all()
+    y = x[10:11].copy()
+    y[0, 32] = 2.0 ** 60
+    Xy = m.mx_scale_exponents(y)
+    assert Xy[0, 1] == 58 and Xy[0, 0] == X[10, 0] and (Xy[0, 2:] == X[10, 2:]).all()
+
+
+def pin_mx_quantize(m, seed=73):
+    """MXFP6 quantization: the textbook error bound of rounding to 3 mantissa bits (2^-4
+    relative on the normal range, 2^(X-4) absolute below it, saturation at 7.5 2^X); values
+    already on the grid come back unchanged; and a worked example by hand."""
+    r = _rng(seed)
+    n, D = 300, 64
+    x = r.standard_normal((n, D)) * np.exp2(r.integers(-30, 30, (n, 1))) * r.uniform(0.01, 3, (n, D))
+    codes, X = m.mx_quantize(x)
+    assert codes.shape == x.shape and X.shape == (n, D // 32)
+    deq = m.mx_dequantize(codes, X)
+    Xe = np.repeat(X, 32, axis=1).astype(np.float64)
+    u = np.abs(x) / np.exp2(Xe)
+    err = np.abs(deq - x)
+    sat = u > 7.5
+    assert (deq[sat] == np.sign(x[sat]) * 7.5 * np.exp2(Xe[sat])).all()
+    norm = (u >= 1) & ~sat
+    assert (err[norm] <= 2.0 ** -4 * np.abs(x[norm])).all()
+    assert (err[u < 1] <= np.exp2(Xe[u < 1] - 4)).all()
+    assert (m.mxfp6_values(x) == deq).all()
+    # grid values round-trip: random codes with one element of each block in [4, 7.5]
+    c = r.integers(0, 64, (50, D)).astype(np.uint8)
+    c[:, ::32] = (r.integers(24, 32, (50, D // 32)) | (r.integers(0, 2, (50, D // 32)) << 5)).astype(np.uint8)
+    Xg = r.integers(-120, 120, (50, D // 32))
+    g = m.mx_dequantize(c, Xg)
+    c2, X2 = m.mx_quantize(g)
+    assert (X2 == Xg).all() and (c2 == c).all()
+    # by hand: block max 8 -> X = 3 - 2 = 1; 0.3 / 2 = 0.15 -> 0.125, -0.2 / 2 = -0.1 -> -0.125,
+    # 15.6 / 2 would be 7.8 but the max is 8 here; 7.7 / 2 = 3.85 -> 3.75 (step 0.25)
+    blk = np.zeros(32)
+    blk[:5] = [8.0, 1.0, 0.3, -0.2, 7.7]
+    assert (m.mxfp6_values(blk[None])[0, :5] == [8.0, 1.0, 0.25, -0.25, 7.5]).all()
+    blk[0] = 15.5                                       # X = 1; 15.5 / 2 = 7.75 -> saturates to 7.5
+    assert m.mxfp6_values(blk[None])[0, 0] == 15.0

@@ -293,3 +293,89 @@ def _prep_shared_gain(qkv, pos, gamma_q, gamma_k, eps, sections, base, dtype):
 @pytest.mark.parametrize("fn", [_prep_rotate_then_norm, _prep_shared_gain], ids=lambda f: f.__name__)
 def test_prep_mutant_is_caught(fn):
     assert _caught(pins.pin_prep_qkv, fn, oracle.rms_norm, oracle.rope)
+
+
+# ---------------------------------------------------------------- MXFP6 / FP8 quantization
+# Mutants replace one function of oracle.mx for the duration of a test (monkeypatch), so the
+# module's other functions (decode, mx_quantize, fp8_values) pick the mistake up too.
+
+import oracle.mx as mx  # noqa: E402
+
+MX_PINS = [pins.pin_e2m3_values, pins.pin_e4m3_values, pins.pin_encode_nearest, pins.pin_e4m3_encode_torch,
+           pins.pin_mx_scale, pins.pin_mx_quantize]
+
+
+def _element_value_variant(kind):
+    def element_value(code, fmt):
+        eb, mb, bias, _ = fmt
+        if kind == "e2m3_bias0" and fmt == mx.E2M3:
+            bias = 0
+        width = 1 + eb + mb
+        sign = -1.0 if (int(code) >> (width - 1)) & 1 else 1.0
+        e = (int(code) >> mb) & ((1 << eb) - 1)
+        m = int(code) & ((1 << mb) - 1)
+        if fmt == mx.E4M3 and e == 15 and m == 7 and kind != "no_nan":
+            return float("nan")
+        if e == 0:
+            return sign * (m / 2.0 ** mb) * 2.0 ** ((-bias) if kind == "subnormal_exp" else (1 - bias))
+        return sign * (1.0 + m / 2.0 ** mb) * 2.0 ** (e - bias)
+    return element_value
+
+
+def _encode_variant(kind):
+    def encode(x, fmt):
+        eb, mb, bias, vmax = fmt
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        emin = (-bias) if kind == "subnormal_quantum" else 1 - bias
+        _, fe = np.frexp(a)
+        ex = np.maximum(np.where(a > 0, fe - 1, emin), emin).astype(np.float64)
+        quantum = np.exp2(ex - mb)
+        if kind == "truncate":
+            r = np.floor(a / quantum) * quantum
+        elif kind == "ties_away":
+            r = np.floor(a / quantum + 0.5) * quantum
+        else:
+            r = np.rint(a / quantum) * quantum
+        if kind != "no_saturate":
+            r = np.minimum(r, vmax)
+        emin = 1 - bias
+        sub = r < 2.0 ** emin
+        m_sub = np.rint(r / 2.0 ** (emin - mb))
+        _, re = np.frexp(np.where(sub, 1.0, r))
+        m_norm = np.rint((np.where(sub, 1.0, r) / np.exp2(re - 1) - 1.0) * 2 ** mb)
+        e_field = np.where(sub, 0, re - 1 + bias).astype(np.int64)
+        m_field = np.where(sub, m_sub, m_norm).astype(np.int64)
+        sign = np.zeros(x.shape, np.int64) if kind == "drop_sign" else np.signbit(x).astype(np.int64)
+        return (((sign << (eb + mb)) | (e_field << mb) | m_field) & 0xFF).astype(np.uint8)
+    return encode
+
+
+def _scale_variant(kind):
+    def mx_scale_exponents(x):
+        x = np.asarray(x, dtype=np.float64)
+        blk = 16 if kind == "block16" else 32
+        blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // blk, blk))
+        amax = np.abs(blocks).max(axis=-1)
+        if kind == "row_amax":
+            amax = np.repeat(amax.max(axis=-1, keepdims=True), amax.shape[-1], axis=-1)
+        _, fe = np.frexp(amax)
+        fl = fe - 1
+        if kind == "ceil":
+            fl = np.where(amax == np.exp2(fl), fl, fl + 1)
+        X = np.where(amax > 0, fl - (3 if kind == "emax3" else 2), -127)
+        return (X if kind == "no_clamp" else np.clip(X, -127, 127)).astype(np.int64)
+    return mx_scale_exponents
+
+
+MX_MUTANTS = ([("element_value", k, _element_value_variant(k)) for k in ("e2m3_bias0", "subnormal_exp", "no_nan")] +
+              [("encode", k, _encode_variant(k)) for k in ("truncate", "ties_away", "no_saturate", "drop_sign",
+                                                           "subnormal_quantum")] +
+              [("mx_scale_exponents", k, _scale_variant(k)) for k in ("emax3", "ceil", "block16", "row_amax",
+                                                                      "no_clamp")])
+
+
+@pytest.mark.parametrize("name,kind,fn", MX_MUTANTS, ids=[f"{n}-{k}" for n, k, _ in MX_MUTANTS])
+def test_mx_mutant_is_caught(monkeypatch, name, kind, fn):
+    monkeypatch.setattr(mx, name, fn)
+    assert any(_caught(p, mx) for p in MX_PINS), (name, kind)

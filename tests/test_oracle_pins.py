@@ -119,3 +119,12 @@ def test_rope_sections():
 
 def test_prep_qkv():
     pins.pin_prep_qkv(oracle.prep_qkv, oracle.rms_norm, oracle.rope)
+
+
+@pytest.mark.parametrize("pin", ["pin_e2m3_values", "pin_e4m3_values", "pin_encode_nearest", "pin_e4m3_encode_torch",
+                                 "pin_mx_scale", "pin_mx_quantize"])
+def test_mx_quantization(pin):
+    """MXFP6 E2M3 / FP8 E4M3 quantization ("The road to the fastest, cheapest H3", reduced
+    precision in video attention) against the published formats and brute force."""
+    import oracle.mx as mx
+    getattr(pins, pin)(mx)
