@@ -16,7 +16,7 @@ __all__ = [
     "sr_chunk_attention", "sr_kvcache_gather", "sr_kvcache_ring", "sr_kvcache_destroy",
     "sr_attention_workspace_bytes", "sr_kvcache_set_workspace", "workspace_for",
     "sr_ring_create", "sr_ring_append", "sr_ring_evict", "sr_ring_segments", "sr_ring_destroy",
-    "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "PAGE_TOKENS", "MAX_WINDOW",
+    "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "SR_MX", "PAGE_TOKENS", "MAX_WINDOW",
     "MAX_VISIBLE_PAGES",
 ]
 
@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsr.so")
 
 SR_OK, SR_E_INVALID, SR_E_STATE, SR_E_NOMEM, SR_E_DEVICE, SR_E_UNSUPPORTED = range(6)
-SR_BF16, SR_F32 = 0, 1
+SR_BF16, SR_F32, SR_MX = 0, 1, 2   # SR_MX: MXFP6 keys, FP8 values; bf16 inputs and outputs
 PAGE_TOKENS = 128         # SR_PAGE_TOKENS
 MAX_WINDOW = 14           # SR_MAX_WINDOW
 MAX_VISIBLE_PAGES = 1024  # SR_MAX_VISIBLE_PAGES
@@ -285,7 +285,7 @@ class KVCache:
         import torch
         self.cfg = cfg
         self.h = None
-        self.dtype = torch.bfloat16 if cfg.dtype == SR_BF16 else torch.float32
+        self.dtype = torch.float32 if cfg.dtype == SR_F32 else torch.bfloat16   # of inputs and outputs
         self.bytes = sr_kvcache_required_bytes(cfg)
         self.pool = torch.empty(self.bytes, dtype=torch.uint8, device=device)
         for t in (persistent_k, persistent_v):

@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
+#include "mx_codec.hpp"
 
 namespace sr {
 namespace {
@@ -60,6 +61,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byte piece
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));  // operand of the scaled MX instruction
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -170,6 +174,7 @@ struct Geo {
   using M = Mma<T>;
   using Op = typename M::Op;
   using Elem = T;
+  static constexpr bool MX = false;
   static constexpr int D = D_, QB = QB_, NW = NW_;
   static constexpr int ES = int(sizeof(T));
   static constexpr int SUB = M::SUB;           // keys per compute sub-tile
@@ -180,15 +185,50 @@ struct Geo {
   static constexpr int KSTEPS = D / M::K;      // contraction steps of K.Q^T
   static constexpr int PSTEPS = 32 / M::K;     // contraction steps of V^T.P^T per 32-key block
   static constexpr int KTILE = BN * D * ES;    // bytes of the K page (and of the V page)
+  static constexpr int KPAGE = KTILE, VPAGE = KTILE;
   static constexpr int VBASE = 2 * KTILE;      // LDS: K page buffers 0, 1, then V page buffers 0, 1
   static constexpr int TABLE = 4 * KTILE;      // then the tile table (16 bytes per tile)
   static constexpr int LDS_BYTES = TABLE + kMaxTiles * 16;
-  static constexpr int LOADS = KTILE / 1024 / NW;  // 1 KiB global-to-LDS loads per wave, per page
-  static_assert(LOADS * NW * 1024 == KTILE, "page loads must split evenly");
+  __device__ static constexpr int key_of_reg(int i, int hl) { return M::key_of_reg(i, hl); }
+  struct QOps {
+    Op op[QB][KSTEPS];  // query operands, resident for the whole piece
+  };
   static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
   static constexpr int RPL = QB * (NDB * 16 + 2);  // record floats per lane: O^T, max, sum
   static constexpr int REC = NW * 64 * RPL;        // record floats per workgroup
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
+};
+
+// Geometry of the reduced-precision kernel (SR_MX caches): K pages of MXFP6 codes and
+// scales, V pages of FP8 codes (layout in kv_kernels.hip, MxPage), bf16 queries quantized to
+// MXFP6 in the prologue, bf16 output.  One LDS tile = one page = 2 sub-tiles of 64 keys, as in
+// Geo, with one wave per 32 queries.
+template <int D_>
+struct GeoMx {
+  using M = Mma<uint16_t>;  // bf16 output stores
+  using Elem = uint16_t;
+  using Op = i32x8_t;
+  static constexpr bool MX = true;
+  static constexpr int D = D_, QB = 1, NW = 8;
+  static constexpr int SUB = 64, BN = SR_PAGE_TOKENS, BM = NW * 32;
+  static constexpr int NKB = SUB / 32, NDB = D / 32, NB = D / 32;
+  static constexpr int KSTEPS = D / 64;  // contraction steps of K.Q^T (64 features each)
+  static constexpr int KPAGE = int(mx_kpage_bytes(D)), VPAGE = int(mx_vpage_bytes(D));
+  static constexpr int LO = 0, HI = NB * BN * 16, SC = HI + NB * BN * 8;  // K page regions
+  static constexpr int VBASE = 2 * KPAGE;  // LDS: K page buffers 0, 1, then V page buffers 0, 1
+  static constexpr int TABLE = VBASE + 2 * VPAGE;
+  static constexpr int LDS_BYTES = TABLE + kMaxTiles * 16;
+  static constexpr int RPL = QB * (NDB * 16 + 2);
+  static constexpr int REC = NW * 64 * RPL;
+  static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
+  static_assert(SC + NB * BN <= KPAGE && KPAGE % 1024 == 0 && VPAGE % 1024 == 0, "page layout");
+  // Score register i of lane half hl holds key 8*(i/4) + 4*hl + i%4 of its 32-key block (the
+  // accumulator layout; MX pages keep the keys in order).
+  __device__ static constexpr int key_of_reg(int i, int hl) { return 8 * (i / 4) + 4 * hl + (i % 4); }
+  struct QOps {
+    i32x8_t op[KSTEPS];  // MXFP6 codes of the lane's query block in each contraction step
+    int sc;              // their E8M0 scale bytes: byte ks for step ks
+  };
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -205,16 +245,28 @@ __device__ __forceinline__ void lds_load16(const void* g, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
 }
 
-// Issues the global-to-LDS loads of one page (K or V, `src` = its first byte) into `dst`:
-// a contiguous copy; load j of wave w moves 1 KiB block (j*NW + w), lane i its piece i.
-template <class G>
-__device__ __forceinline__ void issue_page(const char* src, char* dst, int wave, int lane) {
+// Issues the global-to-LDS loads of one page of BYTES bytes (`src` = its first byte) into
+// `dst`: a contiguous copy; load j of wave w moves 1 KiB block (j*NW + w), lane i its piece
+// i.  BYTES is a whole number of KiB, so a wave loads whole blocks or none (the last round
+// may leave waves out).
+template <int BYTES, int NW>
+__device__ __forceinline__ void issue_bytes(const char* src, char* dst, int wave, int lane) {
+  static_assert(BYTES % 1024 == 0, "pages are copied in 1 KiB blocks");
+  constexpr int BLOCKS = BYTES / 1024;
   const unsigned base = unsigned(size_t((lds_ptr_t)dst));
 #pragma unroll
-  for (int j = 0; j < G::LOADS; ++j) {
-    const int blk = (j * G::NW + wave) * 1024;
-    lds_load16(src + blk + lane * 16, uniform(int(base) + blk));
+  for (int j = 0; j < (BLOCKS + NW - 1) / NW; ++j) {
+    const int b = j * NW + wave;
+    if ((j + 1) * NW <= BLOCKS || b < BLOCKS) lds_load16(src + b * 1024 + lane * 16, uniform(int(base) + b * 1024));
   }
+}
+template <class G>
+__device__ __forceinline__ void issue_k(const char* src, char* dst, int wave, int lane) {
+  issue_bytes<G::KPAGE, G::NW>(src, dst, wave, lane);
+}
+template <class G>
+__device__ __forceinline__ void issue_v(const char* src, char* dst, int wave, int lane) {
+  issue_bytes<G::VPAGE, G::NW>(src, dst, wave, lane);
 }
 
 // s_waitcnt vmcnt(N): at most N of this wave's vector memory operations (global loads,
@@ -277,14 +329,13 @@ __device__ __forceinline__ void scores(Scores<G>& sc, const typename G::Op (&qop
 // Key r of the sub-tile is visible to query block qb iff r < lim[qb]; the others get -inf.
 template <class G>
 __device__ __forceinline__ void mask_sub(Scores<G>& sc, const int (&lim)[G::QB], int hl) {
-  using M = typename G::M;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb)
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (kb * 32 + M::key_of_reg(i, hl) >= lim[qb]) sc[kb][qb][i] = -INFINITY;
+        if (kb * 32 + G::key_of_reg(i, hl) >= lim[qb]) sc[kb][qb][i] = -INFINITY;
 }
 
 // Row max of the raw scores (both lane halves hold the same value).
@@ -640,8 +691,8 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
   for (int qb = 0; qb < G::QB; ++qb)
     lim[qb] = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[qb] - cur_k0 - sub0 : all_rel);
   if (!CLOSING && all_rel < SUB) mask_sub<G>(sc, lim, hl);
-  const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::KTILE;  // sub-tile i-1
-  const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KTILE;             // sub-tile i+1
+  const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::VPAGE;  // sub-tile i-1
+  const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KPAGE;             // sub-tile i+1
   float rmax[G::QB];
   if constexpr (G::ES == 2 && G::QB == 1) {
     float lsum = 0.0f, mnew = 0.0f;
@@ -658,7 +709,7 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
     st.l[0] += lsum;
     mid();
     // Odd i: the next iteration's P.V reads sub-tile i, the second half of V page i / 2.
-    const char* vnext = smem + G::VBASE + ((i >> 1) & 1) * G::KTILE;
+    const char* vnext = smem + G::VBASE + ((i >> 1) & 1) * G::VPAGE;
     block_b<G, ODD == 1>(st, sc, pop, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, c, hl);
   } else {
     accumulate<G>(st, pop, vpage, NEXT, c, hl);
@@ -669,6 +720,193 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
     scores<G>(sn, qop, kpage, NEXT, c, hl);
     softmax_exp<G>(st, sc, pop, sl2);
   }
+}
+
+// ---- reduced-precision path (SR_MX) -------------------------------------------------
+// "The road to the fastest, cheapest H3", Accelerating the denoiser, item 2: MXFP6 queries
+// and keys, FP8 values.  Scores: v_mfma_scale_f32_32x32x64_f8f6f4 with FP6 E2M3 operands,
+// each lane holding one 32-feature block of a key (A) or query (B) row, 24 bytes of codes,
+// with its own E8M0 scale byte.  P.V: the same instruction with FP8 E4M3 operands; the
+// probabilities are converted to FP8 as p * 2^kPShift (round to nearest even) and the
+// instruction's B scale 2^-kPShift takes the factor out again, so that probabilities down to
+// 2^-15 of the running max stay representable.  The lazy rescale threshold is
+// kMxRescale = 2 (log2), so p * 2^kPShift <= 2^8 stays below FP8's largest value 448.  The
+// row sums are those of the rounded probabilities, taken by one more instruction with an
+// all-ones A operand (every output row is then the row sum), which keeps the vector ALU free
+// for the exponentials.
+constexpr int kFmtFp8 = 0, kFmtFp6 = 2;  // format codes of the scaled MX instruction
+constexpr int kPShift = 6;
+constexpr float kMxRescale = 2.0f;
+constexpr int kScaleOne = 127;  // E8M0 byte of 1.0
+constexpr int kOnesFp8 = 0x38383838;  // four E4M3 1.0
+
+template <int FA, int FB, int OA, int OB>
+__device__ __forceinline__ f32x16_t mma_mx(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OA, sa, OB, sb);
+}
+
+// Quantizes the lane's query row (bf16, `row` = its first feature) for the B operand of the
+// score instruction: contraction step ks uses block 2*ks + hl.  Same codes as the cache's
+// keys (mx_codec.hpp).  Rows past n_q get zero codes.
+template <class G>
+__device__ __forceinline__ void mx_queries(typename G::QOps& qo, const uint16_t* row, bool ok, int hl) {
+  qo.sc = 0;
+#pragma unroll
+  for (int ks = 0; ks < G::KSTEPS; ++ks) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(row + (2 * ks + hl) * 32);
+    unsigned xs[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t w = ok ? src[j] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[8 * j + 2 * i] = w[i] & 0xFFFFu;
+        xs[8 * j + 2 * i + 1] = w[i] >> 16;
+      }
+    }
+    unsigned w[6];
+    const int X = mx::quantize_block(xs, w);
+    qo.op[ks] = i32x8_t{int(w[0]), int(w[1]), int(w[2]), int(w[3]), int(w[4]), int(w[5]), 0, 0};
+    qo.sc |= (X + 127) << (8 * ks);
+  }
+}
+
+// A operand of the score instruction: block 2*ks + hl of key row `row` of the K page (16 + 8
+// bytes; the last two dwords are not read for FP6).
+template <class G>
+__device__ __forceinline__ i32x8_t mx_k_operand(const char* kpage, int row, int ks, int hl) {
+  const int b = 2 * ks + hl;
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kpage + G::LO + (b * G::BN + row) * 16);
+  const i32x2_t hi = *reinterpret_cast<const i32x2_t*>(kpage + G::HI + (b * G::BN + row) * 8);
+  const i32x4_t hi4 = __builtin_shufflevector(hi, hi, 0, 1, -1, -1);
+  return __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+// Scale bytes of key row `row` for lane half hl: byte ks is block 2*ks + hl.
+template <class G>
+__device__ __forceinline__ int mx_k_scales(const char* kpage, int row, int hl) {
+  if constexpr (G::NB == 4) return *reinterpret_cast<const uint16_t*>(kpage + G::SC + row * 4 + hl * 2);
+  return *reinterpret_cast<const uint8_t*>(kpage + G::SC + row * 2 + hl);
+}
+// A operand of the P.V instruction for output block db, sub-tile `sub`: feature row
+// db*32 + c, the 16 keys of each 32-key block that lane half hl's probabilities cover.
+template <class G>
+__device__ __forceinline__ i32x8_t mx_v_operand(const char* vpage, int sub, int db, int c, int hl) {
+  const int d = db * 32 + c, g0 = 4 * sub + hl;
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vpage + (g0 * G::D + d) * 16);
+  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vpage + ((g0 + 2) * G::D + d) * 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// S^T = K Q^T for sub-tile `sub` of the K page.
+template <class G>
+__device__ __forceinline__ void mx_scores(f32x16_t (&sn)[2], const typename G::QOps& qo, const char* kpage, int sub,
+                                          int c, int hl) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = sub * G::SUB + kb * 32 + c;
+    const int ksc = mx_k_scales<G>(kpage, row, hl);
+    sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 0, 0>(mx_k_operand<G>(kpage, row, 0, hl), qo.op[0], f32x16_t{}, ksc, qo.sc);
+    if constexpr (G::KSTEPS > 1)
+      sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 1, 1>(mx_k_operand<G>(kpage, row, 1, hl), qo.op[1], sn[kb], ksc, qo.sc);
+  }
+}
+
+// Iteration i of the reduced-precision key loop (ODD: i odd), the same steps and buffers as
+// key_step: mask sub-tile i if partial; P.V of sub-tile i-1 (pop); row max of sub-tile i and
+// the lazy rescale; `mid`; scores of sub-tile i+1 into sn; probabilities of sub-tile i into
+// pop.  CLOSING: only the P.V of the last sub-tile.
+template <class G, int ODD, bool CLOSING = false, class Mid = NoWork>
+__device__ __forceinline__ void mx_key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[1], char* smem,
+                                            RowState<G>& st, f32x16_t& lacc, f32x16_t (&sc)[2], f32x16_t (&sn)[2],
+                                            i32x8_t& pop, const typename G::QOps& qo, float sl2, int c, int hl,
+                                            Mid mid = Mid{}) {
+  constexpr int SUB = G::SUB;
+  constexpr int NEXT = ODD ? 0 : 1;
+  const int sub0 = ODD * SUB;
+  const bool in_seq = i < nsub;
+  const int any_rel = in_seq ? uniform(ent.z) - sub0 : 0;
+  const int all_rel = in_seq ? uniform(ent.w) - sub0 : 0;
+  const int cur_k0 = uniform(ent.y);
+  const int lim = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[0] - cur_k0 - sub0 : all_rel);
+  if (!CLOSING && all_rel < SUB) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + G::key_of_reg(r, hl) >= lim) sc[kb][r] = -INFINITY;
+  }
+  const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::VPAGE;  // sub-tile i-1
+  const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KPAGE;             // sub-tile i+1
+  const i32x8_t ones = {kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8};
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db)
+    st.acc[0][db] = mma_mx<kFmtFp8, kFmtFp8, 0, 0>(mx_v_operand<G>(vpage, NEXT, db, c, hl), pop, st.acc[0][db],
+                                                    kScaleOne, kScaleOne - kPShift);
+  lacc = mma_mx<kFmtFp8, kFmtFp8, 0, 0>(ones, pop, lacc, kScaleOne, kScaleOne - kPShift);
+  if (CLOSING) return;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+  const float mnew = fmaxf(st.m[0], pair_max(mx) * sl2);
+  if (__any(mnew > st.m[0] + kMxRescale)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m[0] - mnew);
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) st.acc[0][db] *= alpha;
+    lacc *= alpha;
+    st.m[0] = mnew;
+  }
+  mid();
+  mx_scores<G>(sn, qo, kpage, NEXT, c, hl);
+  const float mneg = float(kPShift) - st.m[0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * q + e], sl2, mneg));
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      pop[4 * kb + q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+    }
+}
+
+// The key loop of a reduced-precision piece: the same page schedule as the bf16 loop in
+// run_piece (pages requested in iteration 2t+1, one barrier per page), with the row sums
+// accumulated in `lacc` and handed to st.l at the end (on lane half 0, so that the pair sum
+// of the epilogue and the merge of split pieces see each row once).
+template <class G>
+__device__ __forceinline__ void mx_key_loop(const AttnArgs& a, char* smem, const int4* tab, RowState<G>& st,
+                                            const typename G::QOps& qo, const int (&lim_cur)[1], int ntiles,
+                                            size_t head_page, float sl2, int wave, int lane) {
+  const int c = lane & 31, hl = lane >> 5;
+  const int nsub = 2 * ntiles;
+  f32x16_t lacc = {};
+  f32x16_t sc[2], sn[2];
+  i32x8_t pop = {0, 0, 0, 0, 0, 0, 0, 0};  // iteration 0 multiplies the zeroed V buffer 1
+  int4 ent = tab[0];
+  asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w) : "memory");
+  mx_scores<G>(sc, qo, smem, 0, c, hl);
+  for (int t = 0; t < ntiles; ++t) {
+    mx_key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pop, qo, sl2, c, hl);
+    const int4 ent_next = tab[min(t + 1, ntiles - 1)];
+    const int kpage_next = tab[min(t + 2, ntiles - 1)].x;
+    const int vpage_next = ent_next.x;
+    if (t >= 1) wait_loads<0>();
+    __syncthreads();
+    if (t + 1 < ntiles)
+      issue_v<G>(a.vpool + (head_page + uniform(vpage_next)) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE,
+                 wave, lane);
+    const auto request_k = [&] {
+      if (t + 2 < ntiles)
+        issue_k<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KPAGE, smem + (t & 1) * G::KPAGE, wave, lane);
+    };
+    mx_key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, lacc, sn, sc, pop, qo, sl2, c, hl, request_k);
+    ent = ent_next;
+  }
+  mx_key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pop, qo, sl2, c, hl);
+  st.l[0] = hl == 0 ? lacc[0] : 0.0f;
 }
 
 // Pool page (relative to the head's first page) of tile t of the call's tile list: the
@@ -706,23 +944,27 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   // The first pages (K and V of tile tb, K of tile tb+1) are requested first, their page
   // indices walked from the segment table in scalar code, so that their latency overlaps
   // the query loads and the tile-table build below.
-  issue_page<G>(a.kpool + (head_page + tile_page_index(a, tb)) * G::KTILE, smem, wave, lane);
-  issue_page<G>(a.vpool + (head_page + tile_page_index(a, tb)) * G::KTILE, smem + G::VBASE, wave, lane);
-  if (ntiles > 1) issue_page<G>(a.kpool + (head_page + tile_page_index(a, tb + 1)) * G::KTILE, smem + G::KTILE, wave, lane);
+  issue_k<G>(a.kpool + (head_page + tile_page_index(a, tb)) * G::KPAGE, smem, wave, lane);
+  issue_v<G>(a.vpool + (head_page + tile_page_index(a, tb)) * G::VPAGE, smem + G::VBASE, wave, lane);
+  if (ntiles > 1) issue_k<G>(a.kpool + (head_page + tile_page_index(a, tb + 1)) * G::KPAGE, smem + G::KPAGE, wave, lane);
 
   // Query operands (B operand of K.Q^T), resident for the whole piece.
-  Op qop[G::QB][G::KSTEPS];
+  typename G::QOps qo;
   int lim_cur[G::QB];
   const T* __restrict__ qg = static_cast<const T*>(a.q);
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
     const int qrow = q0 + (wave * G::QB + qb) * 32 + c;
     const bool ok = qrow < n_q;
-    const T* src = qg + (size_t(ok ? qrow : 0) * H + h) * D + hl * M::EPL;
+    if constexpr (G::MX) {
+      mx_queries<G>(qo, qg + (size_t(ok ? qrow : 0) * H + h) * D, ok, hl);
+    } else {
+      const T* src = qg + (size_t(ok ? qrow : 0) * H + h) * D + hl * M::EPL;
 #pragma unroll
-    for (int ks = 0; ks < G::KSTEPS; ++ks) {
-      Op v = M::load(reinterpret_cast<const char*>(src + ks * M::K));
-      qop[qb][ks] = ok ? v : Op{};
+      for (int ks = 0; ks < G::KSTEPS; ++ks) {
+        Op v = M::load(reinterpret_cast<const char*>(src + ks * M::K));
+        qo.op[qb][ks] = ok ? v : Op{};
+      }
     }
     lim_cur[qb] = ok && cb > 0 ? min(cur_len, (qrow / cb + 1) * cb) : cur_len;
   }
@@ -761,13 +1003,17 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   }
   // V buffer 1 zeroed: iteration 0 multiplies it by all-zero probabilities, so it must not
   // hold NaN bit patterns.
-  u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::KTILE);
-  for (int x = tid; x < G::KTILE / 16; x += G::NW * 64) vz[x] = u32x4_t{0, 0, 0, 0};
+  u32x4_t* vz = reinterpret_cast<u32x4_t*>(smem + G::VBASE + G::VPAGE);
+  for (int x = tid; x < G::VPAGE / 16; x += G::NW * 64) vz[x] = u32x4_t{0, 0, 0, 0};
   wait_loads<0>();  // first pages and query operands
   __syncthreads();
 
   const float sl2 = a.scale_log2;
   const int nsub = 2 * ntiles;  // sub-tiles j = 2t, 2t+1 of tile t
+  if constexpr (G::MX) {
+    mx_key_loop<G>(a, smem, tab, st, qo, lim_cur, ntiles, head_page, sl2, wave, lane);
+  } else {
+  const auto& qop = qo.op;
   Scores<G> sc;
   Probs<G> pop;
 #pragma unroll
@@ -787,7 +1033,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   Op ring[AH];
   if constexpr (G::ES == 2 && G::QB == 1) {
 #pragma unroll
-    for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(smem + G::VBASE + G::KTILE, 1, r, c, hl);
+    for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(smem + G::VBASE + G::VPAGE, 1, r, c, hl);
   }
 
   // Pair t = iterations 2t (even, first half of tile t) and 2t+1 (odd, second half), then
@@ -810,16 +1056,17 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     if (t >= 1) wait_loads<0>();
     __syncthreads();
     if (t + 1 < ntiles)
-      issue_page<G>(a.vpool + (head_page + uniform(vpage_next)) * G::KTILE, smem + G::VBASE + ((t + 1) & 1) * G::KTILE,
-                    wave, lane);
+      issue_v<G>(a.vpool + (head_page + uniform(vpage_next)) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE,
+                 wave, lane);
     const auto request_k = [&] {
       if (t + 2 < ntiles)
-        issue_page<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KTILE, smem + (t & 1) * G::KTILE, wave, lane);
+        issue_k<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KPAGE, smem + (t & 1) * G::KPAGE, wave, lane);
     };
     key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, ring, sl2, c, hl, request_k);
     ent = ent_next;
   }
   key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
+  }
   __syncthreads();
 
   // A piece of a split item leaves its partial result in its record; the last of the item's
@@ -1012,6 +1259,9 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
                             const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
                             hipStream_t st) {
+  if (L.dtype == SR_MX)
+    return L.D == 128 ? launch_t<GeoMx<128>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st)
+                      : launch_t<GeoMx<64>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
   if (L.dtype == SR_BF16)
     return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st)
                       : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);

@@ -144,6 +144,7 @@ sr_status sr_kvcache_append_qkv(sr_kvcache* c, int64_t chunk_id, const void* qkv
       (reinterpret_cast<uintptr_t>(q_gain) & 3u) || (reinterpret_cast<uintptr_t>(k_gain) & 3u))
     return sr::fail(SR_E_INVALID, "positions and gains must be non-null and 4-byte aligned");
   const sr::Layout& L = c->ring.L;
+  if (L.dtype == SR_MX) return sr::fail(SR_E_UNSUPPORTED, "the fused qkv append is not available for SR_MX caches");
   const int32_t pairs = L.D / 2;
   const int32_t* sec = prep->rope_sections;
   if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != pairs)

@@ -26,7 +26,8 @@ static int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 sr_status make_layout(const sr_kvcache_config* cfg, Layout* out) {
   if (!cfg || !out) return fail(SR_E_INVALID, "null config or output");
   const sr_kvcache_config& c = *cfg;
-  if (c.dtype != SR_BF16 && c.dtype != SR_F32) return fail(SR_E_INVALID, "dtype %d is not SR_BF16 or SR_F32", c.dtype);
+  if (c.dtype != SR_BF16 && c.dtype != SR_F32 && c.dtype != SR_MX)
+    return fail(SR_E_INVALID, "dtype %d is not SR_BF16, SR_F32 or SR_MX", c.dtype);
   if (c.num_heads < 1 || c.num_heads > 4096) return fail(SR_E_INVALID, "num_heads %d outside [1, 4096]", c.num_heads);
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SR_E_UNSUPPORTED, "head_dim %d: only 64 and 128", c.head_dim);
   if (c.dtype == SR_F32 && c.head_dim != 64) return fail(SR_E_UNSUPPORTED, "SR_F32 supports head_dim 64 only");
@@ -48,14 +49,20 @@ sr_status make_layout(const sr_kvcache_config* cfg, Layout* out) {
   L.W = c.window_chunks;
   L.cb = c.causal_block;
   L.dtype = c.dtype;
-  L.esize = c.dtype == SR_BF16 ? 2 : 4;
+  L.esize = c.dtype == SR_F32 ? 4 : 2;  // element size of the token-major inputs and outputs
   L.pages_per_bank = ceil_div(L.P, SR_PAGE_TOKENS);
   L.pages_per_slot = ceil_div(L.cap, SR_PAGE_TOKENS);
   const int64_t pages = int64_t(L.banks) * L.pages_per_bank + int64_t(L.W + 1) * L.pages_per_slot;
   if (pages > (int64_t(1) << 30) / SR_PAGE_TOKENS) return fail(SR_E_INVALID, "pool of %lld pages is too large", (long long)pages);
   L.total_pages = static_cast<int32_t>(pages);
-  L.half_bytes = size_t(L.H) * size_t(L.total_pages) * SR_PAGE_TOKENS * size_t(L.D) * size_t(L.esize);
-  L.bytes = 2 * L.half_bytes;
+  if (c.dtype == SR_MX) {
+    L.kpage_bytes = mx_kpage_bytes(L.D);
+    L.vpage_bytes = mx_vpage_bytes(L.D);
+  } else {
+    L.kpage_bytes = L.vpage_bytes = size_t(SR_PAGE_TOKENS) * size_t(L.D) * size_t(L.esize);
+  }
+  L.half_bytes = size_t(L.H) * size_t(L.total_pages) * L.kpage_bytes;
+  L.bytes = L.half_bytes + size_t(L.H) * size_t(L.total_pages) * L.vpage_bytes;
   *out = L;
   return SR_OK;
 }

@@ -13,6 +13,7 @@ namespace sr {
 struct Layout {
   int32_t H = 0, D = 0, P = 0, banks = 0, cap = 0, W = 0, cb = 0, dtype = 0, esize = 0;
   int32_t pages_per_bank = 0, pages_per_slot = 0, total_pages = 0;
+  size_t kpage_bytes = 0, vpage_bytes = 0;  // one (head, page) of K / of V
   size_t half_bytes = 0;  // bytes of the K region; the V region follows at this offset
   size_t bytes = 0;       // whole pool
 
@@ -28,6 +29,12 @@ void clear_error();
 sr_status make_layout(const sr_kvcache_config* cfg, Layout* out);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bytes of one (head, page) of a reduced-precision (SR_MX) cache: K holds per token and
+// 32-feature block 24 bytes of FP6 codes and one scale byte, padded to whole KiB (the
+// attention kernel copies pages to LDS in 1 KiB pieces per wave); V one FP8 byte per element.
+constexpr size_t mx_kpage_bytes(int32_t D) { return (size_t(D / 32) * (SR_PAGE_TOKENS * 25) + 1023) & ~size_t(1023); }
+constexpr size_t mx_vpage_bytes(int32_t D) { return size_t(D) * SR_PAGE_TOKENS; }
 
 }  // namespace sr
 

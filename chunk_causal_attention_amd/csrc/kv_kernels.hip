@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
+#include "mx_codec.hpp"
 
 namespace sr {
 namespace {
@@ -253,6 +254,164 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool
   }
 }
 
+// ---- reduced-precision (SR_MX) pages -------------------------------------------------
+// "The road to the fastest, cheapest H3", Accelerating the denoiser, item 2: MXFP6 keys and
+// FP8 values.  K page of one head (NB = D / 32 blocks per token): block b of token t packs 32
+// E2M3 codes into 24 bytes, bytes 0-15 in the "lo" region at (b * 128 + t) * 16 and bytes
+// 16-23 in the "hi" region at NB * 2048 + (b * 128 + t) * 8, so that one matrix operand
+// (a key row's block) is a 16-byte and an 8-byte read and 32 lanes read contiguous memory;
+// the scale bytes of token t follow at NB * 3072 + t * NB, block b at (b % 2) * NB / 2 + b / 2
+// (the byte that lane half b % 2 selects in contraction step b / 2).  V page: byte
+// (g * D + d) * 16 + i holds feature d of token t with r = t % 32,
+// g = 4 * (t / 64) + 2 * ((t / 32) % 2) + (r / 4) % 2 and i = 4 * (r / 8) + r % 4: the 16
+// tokens whose probabilities one lane half holds after the score instruction, in register
+// order, so the P.V operand of a lane is two 16-byte reads.
+template <int D>
+struct MxPage {
+  static constexpr int NB = D / 32;
+  static constexpr int LO = 0;
+  static constexpr int HI = NB * SR_PAGE_TOKENS * 16;
+  static constexpr int SC = HI + NB * SR_PAGE_TOKENS * 8;
+  static constexpr int KBYTES = int(mx_kpage_bytes(D));  // SC + NB * 128, padded to whole KiB
+  static constexpr int VBYTES = D * SR_PAGE_TOKENS;
+  static_assert(KBYTES >= SC + NB * SR_PAGE_TOKENS && VBYTES == int(mx_vpage_bytes(D)), "page sizes shared with the host");
+  static constexpr int scale_pos(int b) { return (b % 2) * (NB / 2) + b / 2; }
+};
+
+// Byte of token tp (0..127) of feature d in a V page.
+template <int D>
+__host__ __device__ __forceinline__ int mx_v_offset(int tp, int d) {
+  const int r = tp & 31;
+  const int g = 4 * (tp >> 6) + 2 * ((tp >> 5) & 1) + ((r >> 2) & 1);
+  return (g * D + d) * 16 + 4 * (r >> 3) + (r & 3);
+}
+
+// Workgroup (64-token half page, head).  K: one thread per (block, token) quantizes its 32
+// features and writes its lo/hi pieces (a wave covers 64 consecutive rows of one block:
+// contiguous writes); the scale bytes are collected in LDS and written as dwords.  V: staged
+// in LDS like append_kernel, then one thread per 16-byte piece (group, feature) converts and
+// packs 16 tokens.  Tokens >= n are written as zeros (codes 0, scale byte 0).
+template <int D>
+__global__ __launch_bounds__(256) void mx_append_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                        int n, int H, char* __restrict__ kpool,
+                                                        char* __restrict__ vpool, int total_pages, int page0) {
+  using Pg = MxPage<D>;
+  constexpr int NB = Pg::NB;
+  constexpr int CPR = D / 8;     // 16-byte pieces per bf16 row
+  constexpr int PITCH = D + 8;   // LDS row pitch (elements)
+  __shared__ __align__(16) uint16_t vtile[kAppendTokens * PITCH];
+  __shared__ __align__(4) uint8_t scales[kAppendTokens * NB];
+
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kAppendTokens;
+  const int tp = t0 % SR_PAGE_TOKENS;
+  const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
+  char* kp = kpool + page * Pg::KBYTES;
+  char* vp = vpool + page * Pg::VBYTES;
+  const u32x4_t z = {0, 0, 0, 0};
+
+  for (int ci = threadIdx.x; ci < NB * kAppendTokens; ci += blockDim.x) {
+    const int b = ci / kAppendTokens, r = ci % kAppendTokens, t = t0 + r;
+    unsigned xs[32];
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(k + (size_t(t < n ? t : 0) * H + h) * D + b * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t w = t < n ? src[j] : z;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[8 * j + 2 * i] = w[i] & 0xFFFFu;
+        xs[8 * j + 2 * i + 1] = w[i] >> 16;
+      }
+    }
+    unsigned w[6];
+    const int X = mx::quantize_block(xs, w);
+    const int row = tp + r;
+    *reinterpret_cast<u32x4_t*>(kp + Pg::LO + (b * SR_PAGE_TOKENS + row) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<uint2*>(kp + Pg::HI + (b * SR_PAGE_TOKENS + row) * 8) = make_uint2(w[4], w[5]);
+    scales[r * NB + Pg::scale_pos(b)] = uint8_t(X + 127);
+  }
+  for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
+    const int r = ci / CPR, x = ci % CPR, t = t0 + r;
+    *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * 8) =
+        t < n ? *reinterpret_cast<const u32x4_t*>(v + (size_t(t) * H + h) * D + x * 8) : z;
+  }
+  __syncthreads();
+  for (int ci = threadIdx.x; ci < kAppendTokens * NB / 4; ci += blockDim.x)
+    *reinterpret_cast<uint32_t*>(kp + Pg::SC + tp * NB + ci * 4) = reinterpret_cast<const uint32_t*>(scales)[ci];
+  // V pieces of this half page: groups 4 * (tp / 64) + gl, gl = 2 * kb + hl.
+  for (int ci = threadIdx.x; ci < 4 * D; ci += blockDim.x) {
+    const int gl = ci / D, d = ci % D, kb = gl >> 1, hl = gl & 1;
+    u32x4_t piece;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      unsigned word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q + e;                                    // byte of the piece
+        const int r = 8 * (i >> 2) + 4 * hl + (i & 3);              // token inside the 32-block
+        word |= mx::e4m3_code(vtile[(kb * 32 + r) * PITCH + d]) << (8 * e);
+      }
+      piece[q] = word;
+    }
+    *reinterpret_cast<u32x4_t*>(vp + ((4 * (tp >> 6) + gl) * D + d) * 16) = piece;
+  }
+}
+
+// Thread per (token, feature): the dequantized values as bf16.  Test/debug path; not tuned.
+template <int D>
+__global__ __launch_bounds__(256) void mx_gather_kernel(const char* __restrict__ kpool, const char* __restrict__ vpool,
+                                                        SegTable tab, int total_pages, int H, int ntok,
+                                                        uint16_t* __restrict__ kout, uint16_t* __restrict__ vout) {
+  using Pg = MxPage<D>;
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
+    const int tt = idx % 64, d = idx / 64, t = t0 + tt;
+    if (t >= ntok) continue;
+    int s = 0, off = t;
+    while (s < tab.n - 1 && off >= tab.s[s].len) {
+      off -= tab.s[s].len;
+      ++s;
+    }
+    const size_t page = size_t(h) * total_pages + tab.s[s].page + off / SR_PAGE_TOKENS;
+    const int tp = off % SR_PAGE_TOKENS;
+    const char* kp = kpool + page * Pg::KBYTES;
+    const int b = d / 32, e = d % 32;
+    const uint32_t* lo = reinterpret_cast<const uint32_t*>(kp + Pg::LO + (b * SR_PAGE_TOKENS + tp) * 16);
+    const uint32_t* hi = reinterpret_cast<const uint32_t*>(kp + Pg::HI + (b * SR_PAGE_TOKENS + tp) * 8);
+    const int bit = 6 * e, word = bit >> 5, sh = bit & 31;
+    auto wd = [&](int i) { return i < 4 ? lo[i] : hi[i - 4]; };
+    unsigned c = (wd(word) >> sh) & 63u;
+    if (sh > 26) c |= (wd(word + 1) << (32 - sh)) & 63u;
+    const int X = int(uint8_t(kp[Pg::SC + tp * Pg::NB + Pg::scale_pos(b)])) - 127;
+    kout[(size_t(t) * H + h) * D + d] = uint16_t(mx::e2m3_to_bf16(c, X));
+    const uint8_t vc = uint8_t(vpool[page * Pg::VBYTES + mx_v_offset<D>(tp, d)]);
+    vout[(size_t(t) * H + h) * D + d] = uint16_t(mx::e4m3_to_bf16(vc));
+  }
+}
+
+template <int D>
+hipError_t mx_append_t(const Layout& L, void* pool, const void* k, const void* v, int32_t n, int32_t page0,
+                       int32_t npages, hipStream_t st) {
+  char* kpool = static_cast<char*>(pool);
+  char* vpool = kpool + L.half_bytes;
+  dim3 grid(npages * (SR_PAGE_TOKENS / kAppendTokens), L.H);
+  hipLaunchKernelGGL((mx_append_kernel<D>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), n, L.H, kpool, vpool, L.total_pages, page0);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t mx_gather_t(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
+                       hipStream_t st) {
+  const char* kpool = static_cast<const char*>(pool);
+  const char* vpool = kpool + L.half_bytes;
+  dim3 grid((ntok + 63) / 64, L.H);
+  hipLaunchKernelGGL((mx_gather_kernel<D>), grid, dim3(256), 0, st, kpool, vpool, t, L.total_pages, L.H, ntok,
+                     static_cast<uint16_t*>(kout), static_cast<uint16_t*>(vout));
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t append_t(const Layout& L, void* pool, const void* k, const void* v, int32_t n, int32_t page0, int32_t npages,
                     hipStream_t st) {
@@ -301,6 +460,9 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
 hipError_t launch_append(const Layout& L, void* pool, const void* k, const void* v, int32_t n, int32_t page0,
                          int32_t npages, hipStream_t st) {
   if (npages == 0) return hipSuccess;
+  if (L.dtype == SR_MX)
+    return L.D == 128 ? mx_append_t<128>(L, pool, k, v, n, page0, npages, st)
+                      : mx_append_t<64>(L, pool, k, v, n, page0, npages, st);
   if (L.dtype == SR_BF16)
     return L.D == 128 ? append_t<uint16_t, 128>(L, pool, k, v, n, page0, npages, st)
                       : append_t<uint16_t, 64>(L, pool, k, v, n, page0, npages, st);
@@ -320,6 +482,8 @@ hipError_t launch_prep_append(const Layout& L, void* pool, const void* qkv, cons
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
                          hipStream_t st) {
   if (ntok == 0) return hipSuccess;
+  if (L.dtype == SR_MX)
+    return L.D == 128 ? mx_gather_t<128>(L, pool, t, ntok, kout, vout, st) : mx_gather_t<64>(L, pool, t, ntok, kout, vout, st);
   if (L.dtype == SR_BF16)
     return L.D == 128 ? gather_t<uint16_t, 128>(L, pool, t, ntok, kout, vout, st)
                       : gather_t<uint16_t, 64>(L, pool, t, ntok, kout, vout, st);

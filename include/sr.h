@@ -64,7 +64,12 @@ typedef enum sr_status {
   SR_E_UNSUPPORTED = 5  /* valid request this build does not implement (e.g. head_dim) */
 } sr_status;
 
-typedef enum sr_dtype { SR_BF16 = 0, SR_F32 = 1 } sr_dtype;
+/* Cache element types.  SR_MX is the reduced-precision video attention of "The road to the
+ * fastest, cheapest H3" (Accelerating the denoiser, item 2): keys stored as MXFP6 (FP6 E2M3
+ * elements, one E8M0 scale per 32 consecutive features), values as FP8 E4M3, queries
+ * quantized to MXFP6 by the attention call itself.  Its inputs and outputs (K, V, q, out,
+ * gather) are bf16; see "Reduced-precision cache" below. */
+typedef enum sr_dtype { SR_BF16 = 0, SR_F32 = 1, SR_MX = 2 } sr_dtype;
 
 /* Tokens per pool page.  Every segment starts on a page boundary. */
 #define SR_PAGE_TOKENS 128
@@ -77,7 +82,7 @@ typedef enum sr_dtype { SR_BF16 = 0, SR_F32 = 1 } sr_dtype;
 
 typedef struct sr_kvcache_config {
   int32_t num_heads;         /* H >= 1 (batch folded into heads) */
-  int32_t head_dim;          /* D: 64 or 128 for SR_BF16; 64 for SR_F32 */
+  int32_t head_dim;          /* D: 64 or 128 for SR_BF16 and SR_MX; 64 for SR_F32 */
   int32_t persistent_tokens; /* P >= 0: reference-image + prompt (+ sink) tokens per bank */
   int32_t num_banks;         /* >= 1: one per denoising step */
   int32_t chunk_capacity;    /* >= 1: most tokens a chunk may have (ring slot size) */
@@ -146,6 +151,24 @@ sr_status sr_ring_destroy(sr_ring* r);
  * kernel's matrix instructions consume the page, so a page is copied into LDS unchanged.
  * Pages are numbered: banks first (ceil(P/128) pages each), then the W+1 ring slots
  * (ceil(capacity/128) pages each).  Tokens past a segment's valid length are kept at zero.
+ *
+ * Reduced-precision cache (SR_MX).  K/V are given in bf16 and quantized when written
+ * (append, update, the persistent banks), nearest with ties to the even mantissa and
+ * saturation, the sign bit kept; every input must be finite:
+ *   K: for each token and block of 32 features, X = floor(log2 max|k|) - 2 (at least -127),
+ *      codes = E2M3(k / 2^X) (largest 7.5);
+ *   V: E4M3 per element (largest 448).
+ * The attention call quantizes q the same way as K and computes softmax(scale q~.k~) v~ over
+ * the dequantized values (probabilities are rounded to FP8 for the P.V product).
+ * The K region holds, per (head, page), 3200 * D / 32 bytes rounded up to a multiple of 1024
+ * (13312 for D = 128); the V region, after it, 128 * D bytes.  With NB = D / 32 blocks, block b of token t (0..127) packs its 32 codes
+ * little-endian, 6 bits each, into 24 bytes: bytes 0-15 at (b * 128 + t) * 16, bytes 16-23 at
+ * NB * 2048 + (b * 128 + t) * 8; the scale bytes X + 127 of token t are the NB bytes at
+ * NB * 3072 + t * NB, block b at position (b % 2) * NB / 2 + b / 2.  V code (t, d) is byte
+ * (g * D + d) * 16 + i, where r = t % 32, g = 4 * (t / 64) + 2 * ((t / 32) % 2) + (r / 4) % 2
+ * and i = 4 * (r / 8) + r % 4: the order in which the attention kernel's matrix
+ * instructions consume them.  sr_kvcache_gather returns the dequantized K/V as bf16 (exact).
+ * sr_kvcache_append_qkv is SR_E_UNSUPPORTED on such a cache.
  * ------------------------------------------------------------------------------------------ */
 typedef struct sr_kvcache sr_kvcache;
 

@@ -59,6 +59,17 @@ def test_required_bytes(sr, H, D, P, banks, cap, W, dt):
     assert sr.sr_kvcache_required_bytes(cfg) == 2 * H * pages * 128 * D * (2 if dt == 0 else 4)
 
 
+@pytest.mark.parametrize("H,D,P,banks,cap,W", [(24, 128, 2072, 1, 4680, 2), (3, 64, 130, 1, 333, 1), (2, 128, 0, 1, 1, 0)])
+def test_required_bytes_mx(sr, H, D, P, banks, cap, W):
+    """SR_MX pool: per (head, page) 3200 * D / 32 bytes of K rounded up to whole KiB, then
+    128 * D bytes of V (the layout sr.h documents)."""
+    cfg = sr.config_for(H, D, P, cap, W, None, banks, sr.SR_MX)
+    _, _, pages = _layout_pages(cfg)
+    kpage = -(-(D // 32) * 3200 // 1024) * 1024
+    assert sr.sr_kvcache_required_bytes(cfg) == H * pages * (kpage + 128 * D)
+    assert kpage == (13312 if D == 128 else 7168)
+
+
 @pytest.mark.parametrize("H,D,cap,cus", [(24, 128, 4680, 256), (2, 64, 32, 8), (40, 128, 7200, 304), (3, 64, 1, 1)])
 def test_attention_workspace_bytes(sr, H, D, cap, cus):
     """Per XCD (C = cus / 8 compute units, at least 1): 4C records of 8 waves x 64 lanes x
