@@ -13,6 +13,10 @@ W history chunks in place, append the current chunk, and the attention of all mo
 (history + current) over the whole window ("3.1.2 Historical Context and Temporal
 Consistency", prefix cache).
 
+`--workload c1x` runs the c1 chunk-steps on a reduced-precision cache (MXFP6 keys and
+queries, FP8 values: "The road to the fastest, cheapest H3", Accelerating the denoiser,
+item 2); its roofline peak is the MFMA peak of that mix (below).
+
 `--workload c1p` runs c1 chunk-steps whose chunk enters through the fused append
 (sr_kvcache_append_qkv: qk-RMSNorm, rotary embedding at stream-absolute positions and the
 cache write in one kernel, "3.2 Fast Causal H3 VAE", iteration 6) and reports that kernel's
@@ -39,6 +43,12 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
+# Reduced-precision attention: half of the algorithmic flops (Q.K^T) run on the FP6 matrix
+# rate (10.1 PFLOP/s dense), half (P.V) on the FP8 rate (5.0 PFLOP/s); the time at peak is
+# F/2 / 10.1 + F/2 / 5.0, i.e. an effective peak of 2 / (1/10.1 + 1/5.0) PFLOP/s.
+PEAK_MX_TFLOPS = round(2.0 / (1.0 / 10100.0 + 1.0 / 5000.0), 1)
+# Reduced-precision workloads: the cache type SR_MX on another workload's shapes and inputs.
+MX_WORKLOADS = {"c1x": "c1"}
 
 # Bytes moved past L2 per attention launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
 # script (profiles/chunk_attention_<workload>_counters.md), scaled by the factors a plain
@@ -94,11 +104,16 @@ def attention_flops(w):
     return 4.0 * w.heads * w.head_dim * float(vis.sum())
 
 
-def append_bytes(w):
-    """Algorithmic bytes of one append: read K,V [n][H][D] + write them (and the slot's zero tail)."""
+def append_bytes(w, mx=False):
+    """Algorithmic bytes of one append: read K,V [n][H][D] + write their pages (the slot's zero
+    tail included); reduced-precision pages hold 25 bytes per 32 K features (padded to whole KiB
+    per page) and one byte per V feature."""
     es = 2 if w.dtype == "bf16" else 4
-    slot_tokens = math.ceil(w.chunk / 128) * 128
-    return es * w.heads * w.head_dim * 2 * (w.chunk + slot_tokens)
+    pages = math.ceil(w.chunk / 128)
+    if mx:
+        kpage = (w.head_dim // 32 * 3200 + 1023) // 1024 * 1024
+        return es * w.heads * w.head_dim * 2 * w.chunk + w.heads * pages * (kpage + 128 * w.head_dim)
+    return es * w.heads * w.head_dim * 2 * (w.chunk + pages * 128)
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -122,6 +137,36 @@ def cpu_baseline(w, budget_s=10.0):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {w.heads} heads x all {w.chunk} query rows of {w.name} "
                       f"({w.visible_keys} keys), fp64 numpy oracle, {dt:.1f} s wall"}
+
+
+def cpu_baseline_mx(w, budget_s=10.0):
+    """The oracle on whole heads of the reduced-precision chunk-step: quantize that head's
+    queries, keys and values (oracle.mx) and run its attention over the dequantized values."""
+    import oracle
+    import synth
+    from oracle import mx as omx
+    from threadpoolctl import threadpool_info
+    pk, pv, hist, cur = synth.single_step_inputs(w)
+    wid = lambda a: oracle.widen(a, "bf16")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        h = slice(heads, heads + 1)
+        dk = lambda a: omx.mxfp6_values(wid(a[..., h, :])).astype(np.float32)
+        dv = lambda a: omx.fp8_values(wid(a[..., h, :])).astype(np.float32)
+        m = oracle.StreamingCache(dk(pk), dv(pv), w.window)
+        for i, (k, v) in enumerate(hist):
+            m.append(i, dk(k), dv(v))
+        m.append(len(hist), dk(cur[0]), dv(cur[1]))
+        oracle.chunk_attention(m, 0, dk(cur[2]), scale, w.causal_block, "f32")
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = attention_flops(w) * heads / w.heads
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads x all {w.chunk} query rows of {w.name} ({w.visible_keys} keys): "
+                      f"MXFP6/FP8 quantization of that head's inputs + fp64 attention over the dequantized "
+                      f"values, numpy oracle, {dt:.1f} s wall"}
 
 
 def make_inputs(sr, w, n_sets, torch):
@@ -452,7 +497,8 @@ def run(args):
     import chunk_causal_attention_amd as sr
 
     sr.load()
-    w = synth.get_workload(args.workload)
+    mx = args.workload in MX_WORKLOADS
+    w = synth.get_workload(MX_WORKLOADS.get(args.workload, args.workload))
     if w.name in WINDOW_WORKLOADS:
         return run_window(args, w)
     if w.name in PREP_WORKLOADS:
@@ -464,7 +510,7 @@ def run(args):
     pk, pv, sets = make_inputs(sr, w, w.window + 2, torch)
     scale = 1.0 / math.sqrt(w.head_dim)
     cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
-                        sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
+                        sr.SR_MX if mx else (sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32))
 
     t_init = time.perf_counter()
     layers = []
@@ -515,13 +561,15 @@ def run(args):
     t_attn = np.array([b.elapsed_time(c) for _, b, c in ev_pairs])
     ms_step = elapsed * 1e3 / args.steps
     F = attention_flops(w)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_MX_TFLOPS if mx else (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS)
     attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    name = args.workload
+    traffic = measured_traffic(name)
     if args.traffic_kib is not None:
         traffic = args.traffic_kib * 1024.0
     res = {
-        "metric": "ms per chunk-step & attention TFLOP/s (frac of bf16 MFMA peak), 1 MI355X",
+        "metric": "ms per chunk-step & attention TFLOP/s (frac of bf16 MFMA peak), 1 MI355X" if not mx else
+                  "ms per chunk-step & attention TFLOP/s (frac of the FP6/FP8 MFMA peak), 1 MI355X",
         "value": round(F / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -531,11 +579,12 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "mxfp6 q.k, fp8 p.v" if mx else w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: chunk-step, {w.heads} heads x {w.head_dim}, {w.persistent} persistent + "
-                        f"{w.window}x{w.chunk} history + {w.chunk} current tokens, causal block {w.causal_block}",
+            "workload": f"{name}: chunk-step, {w.heads} heads x {w.head_dim}, {w.persistent} persistent + "
+                        f"{w.window}x{w.chunk} history + {w.chunk} current tokens, causal block {w.causal_block}"
+                        + (", reduced-precision cache (MXFP6 keys/queries, FP8 values)" if mx else ""),
             "heads": w.heads, "head_dim": w.head_dim, "queries": w.chunk, "keys_visible": w.visible_keys,
             "layers_cycled": args.layers, "step": "evict + append_chunk + chunk_attention",
             "schedule": "whole items" if args.no_split else "key tiles split evenly over the CUs",
@@ -552,7 +601,7 @@ def run(args):
         "ms_attention": round(float(t_attn.mean()), 4),
         "ms_attention_p10_p50_p90": [round(float(np.percentile(t_attn, p)), 4) for p in (10, 50, 90)],
         "ms_append": round(float(t_append.mean()), 4),
-        "append_GBps": round(append_bytes(w) / (t_append.mean() * 1e-3) / 1e9, 1),
+        "append_GBps": round(append_bytes(w, mx) / (t_append.mean() * 1e-3) / 1e9, 1),
         "attention_gflop_per_call": round(F / 1e9, 3),
         "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
     }
@@ -561,7 +610,7 @@ def run(args):
     if args.copy_calibration:
         copy_calibration(res, torch, dev)
     if args.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        res["cpu_baseline"] = (cpu_baseline_mx if mx else cpu_baseline)(w, args.cpu_budget)
     return res
 
 
@@ -572,7 +621,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="c1",
                     help="c1 (default), c3, c4, c1s, c4s; c1w: the page-literal window variant at c1 shapes; "
-                         "c1p: c1 chunk-steps entering through the fused qk-RMSNorm + rotary append")
+                         "c1p: c1 chunk-steps entering through the fused qk-RMSNorm + rotary append; "
+                         "c1x: c1 chunk-steps on the reduced-precision (MXFP6/FP8) cache")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-split", action="store_true",

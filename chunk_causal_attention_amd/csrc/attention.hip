@@ -217,7 +217,8 @@ struct GeoMx {
   static constexpr int LO = 0, HI = NB * BN * 16, SC = HI + NB * BN * 8;  // K page regions
   static constexpr int VBASE = 2 * KPAGE;  // LDS: K page buffers 0, 1, then V page buffers 0, 1
   static constexpr int TABLE = VBASE + 2 * VPAGE;
-  static constexpr int LDS_BYTES = TABLE + kMaxTiles * 16;
+  static constexpr int LIMS = TABLE + kMaxTiles * 16;  // per-lane causal limits (int), read on partial tiles
+  static constexpr int LDS_BYTES = LIMS + NW * 64 * 4;
   static constexpr int RPL = QB * (NDB * 16 + 2);
   static constexpr int REC = NW * 64 * RPL;
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
@@ -771,55 +772,203 @@ __device__ __forceinline__ void mx_queries(typename G::QOps& qo, const uint16_t*
   }
 }
 
-// A operand of the score instruction: block 2*ks + hl of key row `row` of the K page (16 + 8
+// Byte offsets, inside a page buffer, of what lane (c, hl) reads at the start of each region
+// (block hl of key row c, its scale bytes, feature row c of lane half hl's V keys); every
+// operand read is one of them plus a constant.  Each page adds an opaque scalar zero to them
+// (mx_page), so that the operand addresses are formed next to their reads (an immediate offset
+// each) instead of being hoisted out of the loop into registers of their own.
+struct MxLane {
+  int kl, kh, ks, v;
+};
+template <class G>
+__device__ __forceinline__ MxLane mx_lane(int c, int hl) {
+  return MxLane{G::LO + (hl * G::BN + c) * 16, G::HI + (hl * G::BN + c) * 8, G::SC + c * G::NB + hl * (G::NB / 2),
+                (hl * G::D + c) * 16};
+}
+
+// A operand of the score instruction: block 2*ks + hl of key row r0 + c of the K page (16 + 8
 // bytes; the last two dwords are not read for FP6).
 template <class G>
-__device__ __forceinline__ i32x8_t mx_k_operand(const char* kpage, int row, int ks, int hl) {
-  const int b = 2 * ks + hl;
-  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kpage + G::LO + (b * G::BN + row) * 16);
-  const i32x2_t hi = *reinterpret_cast<const i32x2_t*>(kpage + G::HI + (b * G::BN + row) * 8);
+__device__ __forceinline__ i32x8_t mx_k_operand(const char* kpage, const MxLane& ln, int r0, int ks) {
+  const int cst = 2 * ks * G::BN + r0;  // rows past the lane's own
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kpage + ln.kl + cst * 16);
+  const i32x2_t hi = *reinterpret_cast<const i32x2_t*>(kpage + ln.kh + cst * 8);
   const i32x4_t hi4 = __builtin_shufflevector(hi, hi, 0, 1, -1, -1);
   return __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, -1, -1);
 }
-// Scale bytes of key row `row` for lane half hl: byte ks is block 2*ks + hl.
+// Scale bytes of key row r0 + c for the lane half: byte ks is block 2*ks + hl.
 template <class G>
-__device__ __forceinline__ int mx_k_scales(const char* kpage, int row, int hl) {
-  if constexpr (G::NB == 4) return *reinterpret_cast<const uint16_t*>(kpage + G::SC + row * 4 + hl * 2);
-  return *reinterpret_cast<const uint8_t*>(kpage + G::SC + row * 2 + hl);
+__device__ __forceinline__ int mx_k_scales(const char* kpage, const MxLane& ln, int r0) {
+  if constexpr (G::NB == 4) return *reinterpret_cast<const uint16_t*>(kpage + ln.ks + r0 * 4);
+  return *reinterpret_cast<const uint8_t*>(kpage + ln.ks + r0 * 2);
 }
 // A operand of the P.V instruction for output block db, sub-tile `sub`: feature row
-// db*32 + c, the 16 keys of each 32-key block that lane half hl's probabilities cover.
+// db*32 + c, the 16 keys of each 32-key block that lane half hl's probabilities cover
+// (groups 4*sub + hl and 4*sub + 2 + hl of the V page).
 template <class G>
-__device__ __forceinline__ i32x8_t mx_v_operand(const char* vpage, int sub, int db, int c, int hl) {
-  const int d = db * 32 + c, g0 = 4 * sub + hl;
-  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vpage + (g0 * G::D + d) * 16);
-  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vpage + ((g0 + 2) * G::D + d) * 16);
+__device__ __forceinline__ i32x8_t mx_v_operand(const char* vpage, const MxLane& ln, int sub, int db) {
+  const int cst = (4 * sub * G::D + db * 32) * 16;
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(vpage + ln.v + cst);
+  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(vpage + ln.v + cst + 2 * G::D * 16);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // S^T = K Q^T for sub-tile `sub` of the K page.
 template <class G>
-__device__ __forceinline__ void mx_scores(f32x16_t (&sn)[2], const typename G::QOps& qo, const char* kpage, int sub,
-                                          int c, int hl) {
+__device__ __forceinline__ void mx_scores(f32x16_t (&sn)[2], const typename G::QOps& qo, const char* kpage,
+                                          const MxLane& ln, int sub) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int row = sub * G::SUB + kb * 32 + c;
-    const int ksc = mx_k_scales<G>(kpage, row, hl);
-    sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 0, 0>(mx_k_operand<G>(kpage, row, 0, hl), qo.op[0], f32x16_t{}, ksc, qo.sc);
+    const int r0 = sub * G::SUB + kb * 32;
+    const int ksc = mx_k_scales<G>(kpage, ln, r0);
+    sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 0, 0>(mx_k_operand<G>(kpage, ln, r0, 0), qo.op[0], f32x16_t{}, ksc, qo.sc);
     if constexpr (G::KSTEPS > 1)
-      sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 1, 1>(mx_k_operand<G>(kpage, row, 1, hl), qo.op[1], sn[kb], ksc, qo.sc);
+      sn[kb] = mma_mx<kFmtFp6, kFmtFp6, 1, 1>(mx_k_operand<G>(kpage, ln, r0, 1), qo.op[1], sn[kb], ksc, qo.sc);
+  }
+}
+
+// ---- reduced-precision key loop: explicitly pipelined blocks --------------------------
+// As in the bf16 path, each MFMA sits in its own scheduling region with a slice of the
+// vector work, and the LDS operands of a block are read in the regions of the block before:
+// block A reads the K operands of block B, block B those of the next block A (when that
+// V page is already published).  Per 64-key sub-tile and wave the vector work is 32
+// exponentials with their scaling, 16 conversions to FP8 and 16 max3 against 4 + 1 P.V and
+// 4 score MFMAs (head_dim 128).  An exponential costs about 3.4 FMA issue slots and does not
+// overlap other vector work, and the two waves of a SIMD (one workgroup, one barrier per
+// page) run in phase, so each block carries vector work in proportion to its MFMA time: the
+// whole row max in the first region of block A, the rescale decision in the second, most
+// exponentials in the rest of block A (whose P.V MFMAs are the long ones), the remainder in
+// block B.
+template <class G>
+constexpr int mx_early() { return G::NDB == 4 ? 24 : 12; }  // probabilities computed in block A
+constexpr int kOnesFp4 = 0x22222222;      // eight FP4 (E2M1) 1.0
+constexpr int kFmtFp4 = 4;
+
+// Score operand j of a sub-tile: key block j % 2, contraction step j / 2 (consecutive
+// instructions accumulate into different score blocks).
+template <class G>
+__device__ __forceinline__ i32x8_t mx_qk_operand(const char* kpage, const MxLane& ln, int sub, int j) {
+  return mx_k_operand<G>(kpage, ln, sub * G::SUB + (j % 2) * 32, j / 2);
+}
+// Score instruction j (j is a constant once the callers' loops are unrolled).
+template <class G>
+__device__ __forceinline__ void mx_score_mma(f32x16_t (&sn)[2], int j, const i32x8_t& kop, const typename G::QOps& qo,
+                                             const int (&ksc)[2]) {
+  if (j < 2) {
+    sn[j] = mma_mx<kFmtFp6, kFmtFp6, 0, 0>(kop, qo.op[0], f32x16_t{}, ksc[j], qo.sc);
+  } else if constexpr (G::KSTEPS > 1) {
+    sn[j - 2] = mma_mx<kFmtFp6, kFmtFp6, 1, 1>(kop, qo.op[1], sn[j - 2], ksc[j - 2], qo.sc);
+  }
+}
+// Probability e of the sub-tile (score register e % 16 of key block e / 16) into sc; when a
+// group of four is complete, its FP8 codes go to dword e / 4 of pnew.
+__device__ __forceinline__ void mx_prob(f32x16_t (&sc)[2], i32x8_t& pnew, int e, float sl2, float mneg) {
+  sc[e / 16][e % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][e % 16], sl2, mneg));
+  pin(sc[e / 16][e % 16]);
+  if ((e & 3) == 3) {
+    const f32x16_t& s = sc[e / 16];
+    const int b = (e % 16) - 3;
+    // The first conversion fills bytes 0-1 and the second bytes 2-3, so the register's prior
+    // contents (the probabilities of two sub-tiles ago) do not matter; converting into it in
+    // place spares zeroing or copying.
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[b], s[b + 1], pnew[e / 4], false);
+    pnew[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(s[b + 2], s[b + 3], lo, true);
+    pin(pnew[e / 4]);
+  }
+}
+
+// Block A: O^T += V^T P^T of sub-tile i-1 (NDB instructions) and the row sums (one
+// instruction with all-ones A), with, between them, the row max of sub-tile i (region 0),
+// the rescale decision (region 1), the first mx_early probabilities of sub-tile i (regions 1
+// on) and the K operands and scales of block B.  LOADED: vop already holds the V operands.
+// SOFTMAX false: the closing step (P.V only).
+template <class G, bool LOADED, bool SOFTMAX>
+__device__ __forceinline__ void mx_block_a(RowState<G>& st, f32x16_t& lacc, f32x16_t (&sc)[2], const i32x8_t& pop,
+                                           i32x8_t& pnew, bool& grow, float& mnew, float& mneg, float sl2,
+                                           const char* vpage, int vsub, const char* kpage, int ksub,
+                                           i32x8_t (&vop)[G::NDB], i32x8_t (&kop)[2 * G::KSTEPS], int (&ksc)[2],
+                                           const i32x8_t& ones, const MxLane& ln) {
+  constexpr int NDB = G::NDB, NP = NDB + 1, NS = 2 * G::KSTEPS;
+  constexpr int EA = mx_early<G>(), EPR = EA / (NP - 1);  // probabilities per region 1 .. NP-1
+  static_assert(NS <= NP && EA % 4 == 0 && EPR * (NP - 1) == EA, "block A layout");
+  if constexpr (!LOADED) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vop[db] = mx_v_operand<G>(vpage, ln, vsub, db);
+  }
+  float mx = -INFINITY;
+  fence();
+#pragma unroll
+  for (int r = 0; r < NP; ++r) {
+    if (r < NDB)
+      st.acc[0][r] = mma_mx<kFmtFp8, kFmtFp8, 0, 0>(vop[r], pop, st.acc[0][r], kScaleOne, kScaleOne - kPShift);
+    else
+      lacc = mma_mx<kFmtFp4, kFmtFp8, 0, 0>(ones, pop, lacc, kScaleOne, kScaleOne - kPShift);
+    if constexpr (SOFTMAX) {
+      if (r < NS) kop[r] = mx_qk_operand<G>(kpage, ln, ksub, r);
+      if (r == 0) {
+        ksc[0] = mx_k_scales<G>(kpage, ln, ksub * G::SUB);
+        ksc[1] = mx_k_scales<G>(kpage, ln, ksub * G::SUB + 32);
+      }
+      if (r == 0) {
+#pragma unroll
+        for (int e = 0; e < 32; e += 2) {
+          mx = fmaxf(mx, fmaxf(sc[e / 16][e % 16], sc[(e + 1) / 16][(e + 1) % 16]));
+          pin(mx);
+        }
+      }
+      if (r == 1) {
+        const float m_old = st.m[0];
+        mnew = fmaxf(m_old, pair_max(mx) * sl2);
+        grow = __any(mnew > m_old + kMxRescale);
+        mneg = float(kPShift) - (grow ? mnew : m_old);
+      }
+      if (r >= 1) {
+#pragma unroll
+        for (int e = (r - 1) * EPR; e < r * EPR; ++e) mx_prob(sc, pnew, e, sl2, mneg);
+      }
+    }
+    fence();
+  }
+}
+
+// Block B: S^T = K Q^T of sub-tile i+1 (operands read in block A) alongside the remaining
+// probabilities of sub-tile i; NEXT_V: also reads the next block A's V operands (half 1 of
+// the V page at vnext).
+template <class G, bool NEXT_V>
+__device__ __forceinline__ void mx_block_b(f32x16_t (&sc)[2], i32x8_t& pnew, f32x16_t (&sn)[2],
+                                           const typename G::QOps& qo, const i32x8_t (&kop)[2 * G::KSTEPS],
+                                           const int (&ksc)[2], const char* vnext, i32x8_t (&vop)[G::NDB], float sl2,
+                                           float mneg, const MxLane& ln) {
+  constexpr int NS = 2 * G::KSTEPS, NDB = G::NDB;
+  constexpr int EA = mx_early<G>(), NE = 32 - EA;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    mx_score_mma<G>(sn, j, kop[j], qo, ksc);
+    if constexpr (NEXT_V) {
+#pragma unroll
+      for (int db = j * NDB / NS; db < (j + 1) * NDB / NS; ++db) vop[db] = mx_v_operand<G>(vnext, ln, 1, db);
+    }
+#pragma unroll
+    for (int e = EA + j * NE / NS; e < EA + (j + 1) * NE / NS; ++e) mx_prob(sc, pnew, e, sl2, mneg);
+    fence();
   }
 }
 
 // Iteration i of the reduced-precision key loop (ODD: i odd), the same steps and buffers as
-// key_step: mask sub-tile i if partial; P.V of sub-tile i-1 (pop); row max of sub-tile i and
-// the lazy rescale; `mid`; scores of sub-tile i+1 into sn; probabilities of sub-tile i into
-// pop.  CLOSING: only the P.V of the last sub-tile.
-template <class G, int ODD, bool CLOSING = false, class Mid = NoWork>
+// key_step: mask sub-tile i if partial; block A (P.V of sub-tile i-1 from pop, row max of
+// sub-tile i); the lazy rescale; `mid`; block B (scores of sub-tile i+1, probabilities of
+// sub-tile i into pnew).  The caller alternates two registers sets for pop and pnew.
+// CLOSING: only the P.V of the last sub-tile.  vop carries the V operands from an odd
+// iteration to the even one that follows (whose V page was published before the odd one).
+// KBUF / VBUF: the page buffers holding sub-tiles i+1 (K) and i-1 (V), VNBUF the V buffer of
+// sub-tile i (read ahead by odd iterations); constants, so every operand address is a lane
+// base plus an immediate offset.
+template <class G, int ODD, int KBUF, int VBUF, int VNBUF, bool CLOSING = false, class Mid = NoWork>
 __device__ __forceinline__ void mx_key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[1], char* smem,
                                             RowState<G>& st, f32x16_t& lacc, f32x16_t (&sc)[2], f32x16_t (&sn)[2],
-                                            i32x8_t& pop, const typename G::QOps& qo, float sl2, int c, int hl,
-                                            Mid mid = Mid{}) {
+                                            const i32x8_t& pop, i32x8_t& pnew, const typename G::QOps& qo,
+                                            i32x8_t (&vop)[G::NDB], const i32x8_t& ones, const MxLane& ln, float sl2,
+                                            int hl, Mid mid = Mid{}) {
   constexpr int SUB = G::SUB;
   constexpr int NEXT = ODD ? 0 : 1;
   const int sub0 = ODD * SUB;
@@ -827,30 +976,29 @@ __device__ __forceinline__ void mx_key_step(int i, const int4& ent, int nsub, co
   const int any_rel = in_seq ? uniform(ent.z) - sub0 : 0;
   const int all_rel = in_seq ? uniform(ent.w) - sub0 : 0;
   const int cur_k0 = uniform(ent.y);
-  const int lim = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lim_cur[0] - cur_k0 - sub0 : all_rel);
   if (!CLOSING && all_rel < SUB) {
+    // The lane's causal limit comes from LDS (kept there rather than in a register that the
+    // loop would spill).  Key kb*32 + key_of_reg(r, hl) = kb*32 + 8*(r/4) + r%4 + 4*hl: the
+    // lane half's term moves to the limit, so each comparison is against a constant.
+    const int lc = reinterpret_cast<const int*>(smem + G::LIMS)[threadIdx.x];
+    const int lim = any_rel <= 0 ? 0 : (cur_k0 >= 0 ? lc - cur_k0 - sub0 : all_rel);
+    const int limh = lim - 4 * hl;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kb * 32 + G::key_of_reg(r, hl) >= lim) sc[kb][r] = -INFINITY;
+        if (kb * 32 + G::key_of_reg(r, 0) >= limh) sc[kb][r] = -INFINITY;
   }
-  const char* vpage = smem + G::VBASE + (((i - 1) >> 1) & 1) * G::VPAGE;  // sub-tile i-1
-  const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KPAGE;             // sub-tile i+1
-  const i32x8_t ones = {kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8, kOnesFp8};
-#pragma unroll
-  for (int db = 0; db < G::NDB; ++db)
-    st.acc[0][db] = mma_mx<kFmtFp8, kFmtFp8, 0, 0>(mx_v_operand<G>(vpage, NEXT, db, c, hl), pop, st.acc[0][db],
-                                                    kScaleOne, kScaleOne - kPShift);
-  lacc = mma_mx<kFmtFp8, kFmtFp8, 0, 0>(ones, pop, lacc, kScaleOne, kScaleOne - kPShift);
+  const char* vpage = smem + G::VBASE + VBUF * G::VPAGE;  // sub-tile i-1
+  const char* kpage = smem + KBUF * G::KPAGE;             // sub-tile i+1
+  i32x8_t kop[2 * G::KSTEPS];
+  int ksc[2];
+  bool grow = false;
+  float mnew = 0.0f, mneg = 0.0f;
+  mx_block_a<G, !ODD, !CLOSING>(st, lacc, sc, pop, pnew, grow, mnew, mneg, sl2, vpage, NEXT, kpage, NEXT, vop, kop,
+                                ksc, ones, ln);
   if (CLOSING) return;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-  const float mnew = fmaxf(st.m[0], pair_max(mx) * sl2);
-  if (__any(mnew > st.m[0] + kMxRescale)) {
+  if (grow) {  // lazy rescale: some row's max grew by more than 2^kMxRescale
     const float alpha = __builtin_amdgcn_exp2f(st.m[0] - mnew);
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) st.acc[0][db] *= alpha;
@@ -858,24 +1006,54 @@ __device__ __forceinline__ void mx_key_step(int i, const int4& ent, int nsub, co
     st.m[0] = mnew;
   }
   mid();
-  mx_scores<G>(sn, qo, kpage, NEXT, c, hl);
-  const float mneg = float(kPShift) - st.m[0];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * q + e], sl2, mneg));
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      pop[4 * kb + q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
-    }
+  // Odd i: the next iteration's P.V reads sub-tile i, the second half of V page i / 2.
+  const char* vnext = smem + G::VBASE + VNBUF * G::VPAGE;
+  mx_block_b<G, ODD == 1>(sc, pnew, sn, qo, kop, ksc, vnext, vop, sl2, mneg, ln);
 }
 
-// The key loop of a reduced-precision piece: the same page schedule as the bf16 loop in
-// run_piece (pages requested in iteration 2t+1, one barrier per page), with the row sums
-// accumulated in `lacc` and handed to st.l at the end (on lane half 0, so that the pair sum
-// of the epilogue and the merge of split pieces see each row once).
+// Page t of a reduced-precision piece (PAR = t % 2, the buffer its K and V pages sit in):
+// iterations 2t and 2t+1 with the page requests and the barrier between them, as in the bf16
+// loop of run_piece.  ent holds the table entry of tile t on entry and of tile t+1 on exit.
+template <class G, int PAR>
+__device__ __forceinline__ void mx_page(const AttnArgs& a, char* smem, const int4* tab, int t, int ntiles,
+                                        size_t head_page, int4& ent, const int (&lim_cur)[1], RowState<G>& st,
+                                        f32x16_t& lacc, f32x16_t (&sc)[2], f32x16_t (&sn)[2], i32x8_t& pa,
+                                        i32x8_t& pb, const typename G::QOps& qo, i32x8_t (&vop)[G::NDB],
+                                        const i32x8_t& ones, const MxLane& lane_base, float sl2, int wave,
+                                        int lane) {
+  const int hl = lane >> 5;
+  const int nsub = 2 * ntiles;
+  int z = 0;
+  asm volatile("" : "+s"(z));  // an SGPR, so no wait for vector memory is implied
+  const MxLane ln{lane_base.kl + z, lane_base.kh + z, lane_base.ks + z, lane_base.v + z};
+  // iteration 2t: K of sub-tile 2t+1 in buffer PAR, V of sub-tile 2t-1 (tile t-1) in 1-PAR
+  mx_key_step<G, 0, PAR, 1 - PAR, PAR>(2 * t, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln,
+                                       sl2, hl);
+  // Table entries, made scalar right away (the barrier below waits for the reads anyway), so
+  // that they occupy no vector registers across the page.
+  const int4 tn = tab[min(t + 1, ntiles - 1)];
+  const int kpage_next = uniform(tab[min(t + 2, ntiles - 1)].x);
+  const int4 ent_next = make_int4(uniform(tn.x), uniform(tn.y), uniform(tn.z), uniform(tn.w));
+  const int vpage_next = ent_next.x;
+  if (t >= 1) wait_loads<0>();
+  __syncthreads();
+  if (t + 1 < ntiles)
+    issue_v<G>(a.vpool + (head_page + vpage_next) * G::VPAGE, smem + G::VBASE + (1 - PAR) * G::VPAGE, wave, lane);
+  const auto request_k = [&] {
+    if (t + 2 < ntiles)
+      issue_k<G>(a.kpool + (head_page + kpage_next) * G::KPAGE, smem + PAR * G::KPAGE, wave, lane);
+  };
+  // iteration 2t+1: K of sub-tile 2t+2 (tile t+1) in 1-PAR, V of sub-tile 2t in PAR
+  mx_key_step<G, 1, 1 - PAR, PAR, PAR>(2 * t + 1, ent, nsub, lim_cur, smem, st, lacc, sn, sc, pb, pa, qo, vop, ones,
+                                       ln, sl2, hl, request_k);
+  ent = ent_next;
+}
+
+// The key loop of a reduced-precision piece: the page schedule of the bf16 loop in run_piece
+// (pages requested in iteration 2t+1, one barrier per page), unrolled by two pages so that
+// buffer parities are constants, with the row sums accumulated in `lacc` and handed to st.l
+// at the end (on lane half 0, so that the pair sum of the epilogue and the merge of split
+// pieces see each row once).
 template <class G>
 __device__ __forceinline__ void mx_key_loop(const AttnArgs& a, char* smem, const int4* tab, RowState<G>& st,
                                             const typename G::QOps& qo, const int (&lim_cur)[1], int ntiles,
@@ -884,28 +1062,33 @@ __device__ __forceinline__ void mx_key_loop(const AttnArgs& a, char* smem, const
   const int nsub = 2 * ntiles;
   f32x16_t lacc = {};
   f32x16_t sc[2], sn[2];
-  i32x8_t pop = {0, 0, 0, 0, 0, 0, 0, 0};  // iteration 0 multiplies the zeroed V buffer 1
-  int4 ent = tab[0];
-  asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w) : "memory");
-  mx_scores<G>(sc, qo, smem, 0, c, hl);
-  for (int t = 0; t < ntiles; ++t) {
-    mx_key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pop, qo, sl2, c, hl);
-    const int4 ent_next = tab[min(t + 1, ntiles - 1)];
-    const int kpage_next = tab[min(t + 2, ntiles - 1)].x;
-    const int vpage_next = ent_next.x;
-    if (t >= 1) wait_loads<0>();
-    __syncthreads();
-    if (t + 1 < ntiles)
-      issue_v<G>(a.vpool + (head_page + uniform(vpage_next)) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE,
-                 wave, lane);
-    const auto request_k = [&] {
-      if (t + 2 < ntiles)
-        issue_k<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KPAGE, smem + (t & 1) * G::KPAGE, wave, lane);
-    };
-    mx_key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, lacc, sn, sc, pop, qo, sl2, c, hl, request_k);
-    ent = ent_next;
+  i32x8_t pa = {0, 0, 0, 0, 0, 0, 0, 0};  // P of odd sub-tiles; iteration 0 multiplies the zeroed V buffer 1
+  i32x8_t pb = {0, 0, 0, 0, 0, 0, 0, 0};  // P of even sub-tiles
+  const MxLane ln = mx_lane<G>(c, hl);
+  i32x8_t vop[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) vop[db] = mx_v_operand<G>(smem + G::VBASE + G::VPAGE, ln, 1, db);
+  const i32x8_t ones = {kOnesFp4, kOnesFp4, kOnesFp4, kOnesFp4, kOnesFp4, kOnesFp4, kOnesFp4, kOnesFp4};
+  reinterpret_cast<int*>(smem + G::LIMS)[threadIdx.x] = lim_cur[0];  // read back by this lane only
+  const int4 t0 = tab[0];
+  int4 ent = make_int4(uniform(t0.x), uniform(t0.y), uniform(t0.z), uniform(t0.w));
+  mx_scores<G>(sc, qo, smem, ln, 0);
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    mx_page<G, 0>(a, smem, tab, t, ntiles, head_page, ent, lim_cur, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln,
+                  sl2, wave, lane);
+    mx_page<G, 1>(a, smem, tab, t + 1, ntiles, head_page, ent, lim_cur, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln,
+                  sl2, wave, lane);
   }
-  mx_key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pop, qo, sl2, c, hl);
+  if (t < ntiles) {  // odd page count: the last page sits in buffer 0
+    mx_page<G, 0>(a, smem, tab, t, ntiles, head_page, ent, lim_cur, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln,
+                  sl2, wave, lane);
+    mx_key_step<G, 0, 0, 0, 0, true>(nsub, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln, sl2,
+                                     hl);
+  } else {
+    mx_key_step<G, 0, 0, 1, 0, true>(nsub, ent, nsub, lim_cur, smem, st, lacc, sc, sn, pa, pb, qo, vop, ones, ln, sl2,
+                                     hl);
+  }
   st.l[0] = hl == 0 ? lacc[0] : 0.0f;
 }
 
