@@ -56,18 +56,20 @@ MX_WORKLOADS = {"c1x": "c1"}
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 220291.4, "write_kib": 103829.5,
-           "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
-    "c1p": {"fetch_kib": 220364.0, "write_kib": 103828.0,
-            "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
-    "c1w": {"fetch_kib": 320250.9, "write_kib": 125276.1,
-            "attention_sha256": "7d4cad44f9c4351ee43c89354196c6a6b8de94a0cbfca5ffd06f56b6d25b75e9"},
+    "c1": {"fetch_kib": 220096.4, "write_kib": 103835.4,
+           "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
+    "c1p": {"fetch_kib": 221461.8, "write_kib": 103832.9,
+            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
+    "c1w": {"fetch_kib": 320248.3, "write_kib": 125267.3,
+            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
+    "c1x": {"fetch_kib": 108768.5, "write_kib": 148875.6,
+            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
 PREP_TRAFFIC = {
-    "c1p": {"fetch_kib": 42276.0, "write_kib": 84912.0,
-            "kv_sha256": "ea9510bd8e362d889f855546f39422a15c81623ed90088ae213f072f05f6867d"},
+    "c1p": {"fetch_kib": 42279.7, "write_kib": 84912.0,
+            "kv_sha256": "5eb0934b2d5d47985be424a13a54054439a4d72ddeaccfa894411b2f88ebb577"},
 }
 KV_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "kv_kernels.hip")
 
