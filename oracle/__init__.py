@@ -27,6 +27,7 @@ Modules
   brute          arbitrary-precision (decimal) brute force for tiny inputs
   mx             MXFP6 (E2M3 + E8M0 block scales) and FP8 E4M3 quantization of the
                  reduced-precision attention's operands
+  decoder        the streaming causal decoder's window attention and global-token attention
 
 Every function has at least one pin in tests/test_oracle_pins.py that does not
 go through the function itself (closed forms, invariants, brute force, an
@@ -41,8 +42,10 @@ from .window_attention import window_attention, prefix_attention
 from .qk_prep import rms_norm, rope, rope_angles, prep_qkv
 from .brute import brute_attention
 from .mx import mxfp6_values, fp8_values, mx_attention_values
+from .decoder import decoder_window_attention, decoder_global_attention, window_offsets
 
 __all__ = ["masked_attention", "widen", "StreamingCache", "CacheStateError", "chunk_attention",
            "current_block_mask", "full_sequence_attention", "window_full_attention", "window_attention",
            "prefix_attention", "rms_norm", "rope", "rope_angles", "prep_qkv", "brute_attention",
-           "mxfp6_values", "fp8_values", "mx_attention_values"]
+           "mxfp6_values", "fp8_values", "mx_attention_values",
+           "decoder_window_attention", "decoder_global_attention", "window_offsets"]

@@ -93,6 +93,17 @@ class StreamingCache:
                 return
         raise CacheStateError("chunk %d is not in the window" % chunk_id)
 
+    def set_bank(self, bank, k, v):
+        """Replace the persistent tokens of `bank` in place, same shape.  The streaming decoder's
+        global (register and class) tokens are rebuilt for every chunk and never cached (project
+        page, "3.2 Fast Causal H3 VAE", iteration 4); its cache keeps them in the bank."""
+        k, v = np.array(k), np.array(v)
+        if not 0 <= bank < self.banks:
+            raise CacheStateError("bank out of range")
+        if k.shape != self.pk[bank].shape or v.shape != self.pv[bank].shape:
+            raise CacheStateError("a bank keeps its shape")
+        self.pk[bank], self.pv[bank] = k, v
+
     def prefix_len(self, bank):
         """Persistent (prefix) tokens of `bank`."""
         return self.pk[bank].shape[0]

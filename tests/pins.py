@@ -575,3 +575,141 @@ def pin_mx_quantize(m, seed=73):
     assert (m.mxfp6_values(blk[None])[0, :5] == [8.0, 1.0, 0.25, -0.25, 7.5]).all()
     blk[0] = 15.5                                       # X = 1; 15.5 / 2 = 7.75 -> saturates to 7.5
     assert m.mxfp6_values(blk[None])[0, 0] == 15.0
+
+
+# ---------------------------------------------------------------- streaming decoder window attention
+
+def _decoder_stream(cache_cls, seed, window_tokens, frames, W, G, H, D, n_chunks, perturb=None):
+    """A seeded decoder stream: per chunk, fresh global tokens (set_bank) and the packed frame tokens;
+    returns the cache after the last chunk, that chunk's queries, the global queries, and every
+    chunk's (k, v) (for the dense route).  perturb(c, k, v) may modify chunk c's arrays."""
+    r = _rng(seed)
+    T = frames * int(np.sum(window_tokens))
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    cache = cache_cls(f(1, G, H, D), f(1, G, H, D), W)
+    chunks = []
+    for c in range(n_chunks):
+        gk, gv = f(G, H, D), f(G, H, D)
+        k, v = f(T, H, D), f(T, H, D)
+        if perturb:
+            k, v = perturb(c, k, v)
+        cache.set_bank(0, gk, gv)
+        if W and c > W:
+            cache.evict()
+        cache.append(c, k, v)
+        chunks.append((k, v))
+    return cache, f(T, H, D), f(G, H, D), chunks, (gk, gv)
+
+
+def _decoder_dense(window_tokens, frames, W, chunks, glob, q, gq, scale):
+    """Independent route: one masked attention per head over [global | every chunk still visible
+    (the last W + 1), in stream order], with an explicit mask built from each key's chunk and
+    window and each query's window."""
+    gk, gv = glob
+    vis_chunks = chunks[-(W + 1):]
+    wid = np.repeat(np.arange(len(window_tokens)), frames * np.asarray(window_tokens))
+    G = gk.shape[0]
+    keys = np.concatenate([gk] + [k for k, _ in vis_chunks], axis=0).astype(np.float64)
+    vals = np.concatenate([gv] + [v for _, v in vis_chunks], axis=0).astype(np.float64)
+    key_w = np.concatenate([np.full(G, -1)] + [wid for _ in vis_chunks])
+    key_c = np.concatenate([np.full(G, -1)] + [np.full(len(wid), i) for i in range(len(vis_chunks))])
+    cur = len(vis_chunks) - 1
+    qs = np.concatenate([q, gq], axis=0).astype(np.float64)
+    mask = np.zeros((qs.shape[0], keys.shape[0]), bool)
+    T = len(wid)
+    mask[:T] = (key_w[None, :] == wid[:, None]) | (key_w[None, :] == -1)
+    mask[T:] = (key_c[None, :] == cur) | (key_c[None, :] == -1)
+    H = q.shape[1]
+    o = np.zeros((qs.shape[0], H, q.shape[2]))
+    lse = np.zeros((H, qs.shape[0]))
+    from oracle import masked_attention
+    for h in range(H):
+        o[:, h], lse[h] = masked_attention(qs[:, h], keys[:, h], vals[:, h], mask, scale)
+    return o[:T], lse[:, :T], o[T:], lse[:, T:]
+
+
+def pin_decoder_equals_dense(cache_cls, win_attn, glob_attn):
+    """The per-window routine and the global routine equal one dense masked attention over the
+    visible stream, from the first chunk (no history: empty slots hidden) to a full, evicting
+    window, on a ragged layout."""
+    window_tokens, frames, W, G, H, D = [3, 2, 4, 1], 2, 2, 2, 2, 8
+    for n_chunks in (1, 2, 3, 5):
+        cache, q, gq, chunks, glob = _decoder_stream(cache_cls, 61 + n_chunks, window_tokens, frames, W, G, H, D,
+                                                     n_chunks)
+        o, lse = win_attn(cache, window_tokens, frames, q, 0.4, "f32")
+        og, lg = glob_attn(cache, gq, 0.4, "f32")
+        ro, rl, rog, rlg = _decoder_dense(window_tokens, frames, W, chunks, glob, q, gq, 0.4)
+        assert np.abs(o - ro).max() <= 1e-12 and np.abs(lse - rl).max() <= 1e-12, n_chunks
+        assert np.abs(og - rog).max() <= 1e-12 and np.abs(lg - rlg).max() <= 1e-12, n_chunks
+
+
+def pin_decoder_brute(cache_cls, win_attn, glob_attn):
+    """Decimal brute force on a tiny stream (two windows, W = 1, three chunks)."""
+    from oracle import brute_attention
+    window_tokens, frames, W, G, H, D = [1, 2], 2, 1, 1, 1, 3
+    cache, q, gq, chunks, glob = _decoder_stream(cache_cls, 71, window_tokens, frames, W, G, H, D, 3)
+    o, lse = win_attn(cache, window_tokens, frames, q, 0.7, "f32")
+    og, lg = glob_attn(cache, gq, 0.7, "f32")
+    ro, rl, rog, rlg = _decoder_dense(window_tokens, frames, W, chunks, glob, q, gq, 0.7)
+    gk, gv = glob
+    keys = np.concatenate([gk] + [k for k, _ in chunks[-2:]])[:, 0]
+    vals = np.concatenate([gv] + [v for _, v in chunks[-2:]])[:, 0]
+    wid = np.repeat([0, 1], [2, 4])
+    kw = np.concatenate([[-1], wid, wid])
+    vis = [[kw[j] in (-1, wid[i]) for j in range(len(kw))] for i in range(6)]
+    bo, bl = brute_attention(q[:, 0].tolist(), keys.tolist(), vals.tolist(), vis, 0.7)
+    assert np.abs(o[:, 0] - np.array(bo)).max() <= 1e-13 and np.abs(lse[0] - np.array(bl)).max() <= 1e-13
+    kc = np.concatenate([[1], np.zeros(6), np.ones(6)])
+    visg = [[bool(kc[j]) for j in range(len(kc))]]
+    bog, blg = brute_attention(gq[:, 0].tolist(), keys.tolist(), vals.tolist(), visg, 0.7)
+    assert np.abs(og[:, 0] - np.array(bog)).max() <= 1e-13 and abs(lg[0, 0] - blg[0]) <= 1e-13
+
+
+def pin_decoder_window_independence(cache_cls, win_attn, glob_attn):
+    """Changing window 1's keys and values in any chunk leaves the other windows' rows bit for bit
+    unchanged; changing a cached chunk leaves the global rows unchanged."""
+    window_tokens, frames, W, G, H, D = [2, 3, 2], 2, 2, 1, 2, 4
+    base = _decoder_stream(cache_cls, 81, window_tokens, frames, W, G, H, D, 4)
+    rows1 = np.arange(2 * 2, 2 * 2 + 2 * 3)
+
+    def bump(c, k, v):
+        k, v = k.copy(), v.copy()
+        k[rows1] += 3.0
+        v[rows1] -= 5.0
+        return k, v
+    alt = _decoder_stream(cache_cls, 81, window_tokens, frames, W, G, H, D, 4, perturb=bump)
+    o0, l0 = win_attn(base[0], window_tokens, frames, base[1], 0.5, "f32")
+    o1, l1 = win_attn(alt[0], window_tokens, frames, alt[1], 0.5, "f32")
+    other = np.setdiff1d(np.arange(o0.shape[0]), rows1)
+    assert (o0[other] == o1[other]).all() and (l0[:, other] == l1[:, other]).all()
+    assert not np.allclose(o0[rows1], o1[rows1])
+
+    def bump_cached(c, k, v):
+        return (k + 1.0, v) if c == 2 else (k, v)
+    alt2 = _decoder_stream(cache_cls, 81, window_tokens, frames, W, G, H, D, 4, perturb=bump_cached)
+    g0, _ = glob_attn(base[0], base[2], 0.5, "f32")
+    g2, _ = glob_attn(alt2[0], alt2[2], 0.5, "f32")
+    assert (g0 == g2).all()
+
+
+def pin_set_bank(cache_cls):
+    """set_bank replaces exactly the named bank, keeps shapes, refuses a new shape."""
+    r = _rng(91)
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    pk, pv = f(2, 3, 2, 4), f(2, 3, 2, 4)
+    c = cache_cls(pk, pv, 1)
+    c.append(0, f(5, 2, 4), f(5, 2, 4))
+    nk, nv = f(3, 2, 4), f(3, 2, 4)
+    c.set_bank(1, nk, nv)
+    k0, v0, _ = c.sequence(0)
+    k1, v1, _ = c.sequence(1)
+    assert (k0[:3] == pk[0]).all() and (v0[:3] == pv[0]).all()
+    assert (k1[:3] == nk).all() and (v1[:3] == nv).all()
+    try:
+        c.set_bank(0, f(4, 2, 4), f(4, 2, 4))
+    except Exception:
+        pass
+    else:
+        raise AssertionError("a bank changed its shape")
+    k0b, _, _ = c.sequence(0)
+    assert (k0b[:3] == pk[0]).all()

@@ -379,3 +379,73 @@ MX_MUTANTS = ([("element_value", k, _element_value_variant(k)) for k in ("e2m3_b
 def test_mx_mutant_is_caught(monkeypatch, name, kind, fn):
     monkeypatch.setattr(mx, name, fn)
     assert any(_caught(p, mx) for p in MX_PINS), (name, kind)
+
+
+# ---------------------------------------------------------------- streaming decoder window attention
+
+from oracle.decoder import decoder_window_attention, decoder_global_attention, window_rows  # noqa: E402
+
+
+def _decoder_window_variant(kind):
+    def win_attn(cache, window_tokens, frames, q, scale, dtype):
+        T = q.shape[0]
+        gk, gv = cache.pk[0], cache.pv[0]
+        hist = [(k, v) for _, k, v in cache.history]
+        chunks = ([] if kind == "no_history" else hist) + [(cache.current[1], cache.current[2])]
+        H = q.shape[1]
+        o = np.zeros((T, H, q.shape[2]))
+        lse = np.zeros((H, T))
+        n_win = len(window_tokens)
+        for w in range(n_win):
+            rows = window_rows(window_tokens, frames, w)
+            if kind == "frame_major":   # window rows taken from a frame-by-frame layout
+                per = np.asarray(window_tokens)
+                start = int(per[:w].sum())
+                rows = np.concatenate([f * int(per.sum()) + start + np.arange(per[w]) for f in range(frames)])
+            krows = np.arange(T) if kind == "all_windows" else rows
+            parts_k = ([] if kind == "no_global" else [gk]) + [k[krows] for k, _ in chunks]
+            parts_v = ([] if kind == "no_global" else [gv]) + [v[krows] for _, v in chunks]
+            keys, vals = np.concatenate(parts_k), np.concatenate(parts_v)
+            for h in range(H):
+                o[rows, h], lse[h, rows] = oracle.masked_attention(widen(q[rows, h], dtype), widen(keys[:, h], dtype),
+                                                                   widen(vals[:, h], dtype),
+                                                                   np.ones((len(rows), keys.shape[0]), bool), scale)
+        return o, lse
+    return win_attn
+
+
+def _decoder_global_sees_history(cache, gq, scale, dtype):
+    keys = np.concatenate([cache.pk[0]] + [k for _, k, _ in cache.history] + [cache.current[1]])
+    vals = np.concatenate([cache.pv[0]] + [v for _, _, v in cache.history] + [cache.current[2]])
+    H = gq.shape[1]
+    o = np.zeros((gq.shape[0], H, gq.shape[2]))
+    lse = np.zeros((H, gq.shape[0]))
+    for h in range(H):
+        o[:, h], lse[h] = oracle.masked_attention(widen(gq[:, h], dtype), widen(keys[:, h], dtype),
+                                                  widen(vals[:, h], dtype), np.ones((gq.shape[0], keys.shape[0]), bool),
+                                                  scale)
+    return o, lse
+
+
+DECODER_PINS = [pins.pin_decoder_equals_dense, pins.pin_decoder_brute, pins.pin_decoder_window_independence]
+
+
+@pytest.mark.parametrize("kind", ["all_windows", "no_history", "no_global", "frame_major"])
+def test_decoder_window_mutant_is_caught(kind):
+    wa = _decoder_window_variant(kind)
+    assert any(_caught(p, oracle.StreamingCache, wa, decoder_global_attention) for p in DECODER_PINS), kind
+
+
+def test_decoder_global_mutant_is_caught():
+    assert any(_caught(p, oracle.StreamingCache, decoder_window_attention, _decoder_global_sees_history)
+               for p in DECODER_PINS)
+
+
+class _SetBankZero(oracle.StreamingCache):
+    def set_bank(self, bank, k, v):
+        super().set_bank(0, k, v)
+
+
+@pytest.mark.parametrize("cls", [_SetBankZero], ids=lambda c: c.__name__)
+def test_set_bank_mutant_is_caught(cls):
+    assert _caught(pins.pin_set_bank, cls)

@@ -128,3 +128,15 @@ def test_mx_quantization(pin):
     precision in video attention) against the published formats and brute force."""
     import oracle.mx as mx
     getattr(pins, pin)(mx)
+
+
+@pytest.mark.parametrize("pin", ["pin_decoder_equals_dense", "pin_decoder_brute", "pin_decoder_window_independence"])
+def test_decoder_window_attention(pin):
+    """Streaming decoder windows (project page 3.2): per-window routine and global-token routine
+    against a dense masked formulation, decimal brute force and window independence."""
+    from oracle.decoder import decoder_window_attention, decoder_global_attention
+    getattr(pins, pin)(oracle.StreamingCache, decoder_window_attention, decoder_global_attention)
+
+
+def test_set_bank():
+    pins.pin_set_bank(oracle.StreamingCache)
