@@ -16,7 +16,7 @@ __all__ = [
     "sr_chunk_attention", "sr_kvcache_gather", "sr_kvcache_ring", "sr_kvcache_destroy",
     "sr_attention_workspace_bytes", "sr_kvcache_set_workspace", "workspace_for",
     "sr_ring_create", "sr_ring_append", "sr_ring_evict", "sr_ring_segments", "sr_ring_destroy",
-    "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "SR_MX", "PAGE_TOKENS", "MAX_WINDOW",
+    "sr_status_string", "sr_last_error", "KVCache", "SR_BF16", "SR_F32", "SR_MX", "window_layout", "PAGE_TOKENS", "MAX_WINDOW",
     "MAX_VISIBLE_PAGES",
 ]
 
@@ -50,6 +50,23 @@ class sr_kvcache_config(ctypes.Structure):
 class sr_segment(ctypes.Structure):
     _fields_ = [("chunk_id", ctypes.c_int64), ("kind", ctypes.c_int32), ("slot", ctypes.c_int32),
                 ("page", ctypes.c_int32), ("length", ctypes.c_int32)]
+
+
+MAX_LAYOUT_WINDOWS = 64
+
+
+class sr_window_layout(ctypes.Structure):
+    _fields_ = [("num_windows", ctypes.c_int32), ("frames_per_chunk", ctypes.c_int32), ("window_pages", ctypes.c_int32),
+                ("window_tokens", ctypes.c_int32 * MAX_LAYOUT_WINDOWS)]
+
+
+def window_layout(window_tokens, frames_per_chunk, window_pages):
+    """sr_window_layout of windows holding window_tokens[w] tokens per latent frame."""
+    wt = list(window_tokens)
+    if len(wt) > MAX_LAYOUT_WINDOWS:
+        raise ValueError(f"at most {MAX_LAYOUT_WINDOWS} windows")
+    arr = (ctypes.c_int32 * MAX_LAYOUT_WINDOWS)(*(wt + [0] * (MAX_LAYOUT_WINDOWS - len(wt))))
+    return sr_window_layout(len(wt), frames_per_chunk, window_pages, arr)
 
 
 class sr_qk_prep(ctypes.Structure):
@@ -100,6 +117,11 @@ def load():
         "sr_ring_update": [P, I64, I32, ctypes.POINTER(I32)],
         "sr_ring_segments": [P, I32, ctypes.POINTER(sr_segment), I32, ctypes.POINTER(I32)],
         "sr_ring_destroy": [P],
+        "sr_kvcache_set_window_layout": [P, ctypes.POINTER(sr_window_layout)],
+        "sr_kvcache_set_bank": [P, I32, P, P, P],
+        "sr_kvcache_append_windows": [P, I64, P, P, P],
+        "sr_windows_attention": [P, I32, P, P, P, F32, P],
+        "sr_global_attention": [P, I32, P, I32, P, P, F32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -201,6 +223,28 @@ def sr_prefix_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=No
 def sr_kvcache_update_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
     n = k.shape[0] if n_tokens is None else n_tokens
     _check(load().sr_kvcache_update_chunk(h, chunk_id, _ptr(k), _ptr(v), n, _stream(stream)))
+
+
+def sr_kvcache_set_window_layout(h, layout):
+    _check(load().sr_kvcache_set_window_layout(h, ctypes.byref(layout)))
+
+
+def sr_kvcache_set_bank(h, bank, k, v, stream=None):
+    _check(load().sr_kvcache_set_bank(h, bank, _ptr(k), _ptr(v), _stream(stream)))
+
+
+def sr_kvcache_append_windows(h, chunk_id, k, v, stream=None):
+    _check(load().sr_kvcache_append_windows(h, chunk_id, _ptr(k), _ptr(v), _stream(stream)))
+
+
+def sr_windows_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    scale = softmax_scale if softmax_scale is not None else 1.0 / (q.shape[-1] ** 0.5)
+    _check(load().sr_windows_attention(h, bank, _ptr(q), _ptr(out), _ptr(lse), scale, _stream(stream)))
+
+
+def sr_global_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    scale = softmax_scale if softmax_scale is not None else 1.0 / (q.shape[-1] ** 0.5)
+    _check(load().sr_global_attention(h, bank, _ptr(q), q.shape[0], _ptr(out), _ptr(lse), scale, _stream(stream)))
 
 
 def sr_kvcache_gather(h, bank, k_out, v_out, stream=None):
@@ -376,6 +420,45 @@ class KVCache:
         """Prefix rows q [P][H][D] of bank `bank` over that bank only."""
         out = self._out_lse(q, out, lse)
         sr_prefix_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def set_window_layout(self, window_tokens, frames_per_chunk, window_pages):
+        """Window layout of a decoder cache (once, before the first append)."""
+        sr_kvcache_set_window_layout(self.h, window_layout(window_tokens, frames_per_chunk, window_pages))
+        self.layout = (list(window_tokens), frames_per_chunk, window_pages)
+        self.window_rows = frames_per_chunk * sum(window_tokens)
+
+    def _packed_rows(self):
+        """Rows of a chunk packed window by window (the library reads exactly that many)."""
+        rows = getattr(self, "window_rows", None)
+        if rows is None:
+            raise SrError(2, "no window layout: set one first")
+        return rows
+
+    def set_bank(self, bank, k, v, stream=None):
+        """Rewrite the persistent tokens of `bank` ([P][H][D])."""
+        shape = (self.cfg.persistent_tokens, self.cfg.num_heads, self.cfg.head_dim)
+        self._check_tensor(k, shape)
+        self._check_tensor(v, shape)
+        sr_kvcache_set_bank(self.h, bank, k, v, stream)
+
+    def append_windows(self, chunk_id, k, v, stream=None):
+        """Append a chunk packed window by window ([T][H][D])."""
+        self._check_tensor(k, (self._packed_rows(), self.cfg.num_heads, self.cfg.head_dim))
+        self._check_tensor(v, k.shape)
+        sr_kvcache_append_windows(self.h, chunk_id, k, v, stream)
+
+    def windows_attention(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        """Every window's rows of the current chunk (packed [T][H][D]) over the bank and the window's keys."""
+        self._check_tensor(q, (self._packed_rows(), self.cfg.num_heads, self.cfg.head_dim))
+        out = self._out_lse(q, out, lse)
+        sr_windows_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def global_attention(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        """Global-token queries [G][H][D] over the bank and every frame token of the current chunk."""
+        out = self._out_lse(q, out, lse)
+        sr_global_attention(self.h, bank, q, out, lse, softmax_scale, stream)
         return out
 
     def gather(self, bank=0, max_tokens=None, stream=None):

@@ -163,6 +163,7 @@ struct AttnArgs {
   float* rec;              // split: 4C partial records per XCD
   int32_t* cnt;            // split: C arrival counters per XCD (zero between calls)
   SegTable t;
+  WinView win;                              // window mode (win.n > 0): see WinView
   XcdPlan plan[8];                          // split: xcd_plan of each XCD
   int16_t left_tiles[8][kMaxCusPerXcd];     // split: key tiles of each XCD's split items
 };
@@ -739,7 +740,6 @@ constexpr int kFmtFp8 = 0, kFmtFp6 = 2;  // format codes of the scaled MX instru
 constexpr int kPShift = 6;
 constexpr float kMxRescale = 2.0f;
 constexpr int kScaleOne = 127;  // E8M0 byte of 1.0
-constexpr int kOnesFp8 = 0x38383838;  // four E4M3 1.0
 
 template <int FA, int FB, int OA, int OB>
 __device__ __forceinline__ f32x16_t mma_mx(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sa, int sb) {
@@ -1092,23 +1092,33 @@ __device__ __forceinline__ void mx_key_loop(const AttnArgs& a, char* smem, const
   st.l[0] = hl == 0 ? lacc[0] : 0.0f;
 }
 
+// Length and first page of segment s as window `win` sees it (win < 0: the table as is; else
+// the bank segments as is and, of every chunk, the window's pages and tokens).
+__device__ __forceinline__ int seg_len(const AttnArgs& a, int win, int s) {
+  return (win < 0 || s < a.win.bank_segs) ? a.t.s[s].len : a.win.frames * a.win.tok[win];
+}
+__device__ __forceinline__ int seg_page(const AttnArgs& a, int win, int s) {
+  return (win < 0 || s < a.win.bank_segs) ? a.t.s[s].page : a.t.s[s].page + win * a.win.pages;
+}
+
 // Pool page (relative to the head's first page) of tile t of the call's tile list: the
 // pages of the segments in visiting order.
-__device__ __forceinline__ int tile_page_index(const AttnArgs& a, int t) {
+__device__ __forceinline__ int tile_page_index(const AttnArgs& a, int win, int t) {
   int s = 0, first = 0;
   for (; s < a.t.n - 1; ++s) {
-    const int nt = (a.t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+    const int nt = (seg_len(a, win, s) + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
     if (t < first + nt) break;
     first += nt;
   }
-  return uniform(a.t.s[s].page + (t - first));
+  return uniform(seg_page(a, win, s) + (t - first));
 }
 
 // One piece of work: query tile qt of head h over tiles [tb, te) of its tile list.  slot < 0:
 // the whole list (write the output); else a sub-piece of split item `it` (record `slot`).
+// win >= 0: window mode, the rows and keys of that window (WinView).
 template <class G>
 __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* flag, int h, int qt, int tb, int te,
-                                          int slot, const SplitItem& it) {
+                                          int slot, const SplitItem& it, int win = -1) {
   using M = typename G::M;
   using Op = typename G::Op;
   using T = typename G::Elem;
@@ -1117,9 +1127,14 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   const int lane = tid & 63, wave = uniform(tid >> 6);
   const int c = lane & 31, hl = lane >> 5;
   const int q0 = qt * G::BM;
-  const int n_q = a.n_q, H = a.H, cb = a.causal_block;
+  const int H = a.H, cb = a.causal_block;
+  // Rows of this call (window mode: the window's), their first packed row, and the row count
+  // of the lse layout [H][rows of the whole call].
+  const int n_q = win < 0 ? a.n_q : uniform(a.win.frames * a.win.tok[win]);
+  const int row0 = win < 0 ? 0 : uniform(a.win.row0[win]);
+  const int lse_rows = a.n_q;
   const int cur = a.t.n - 1;
-  const int cur_len = a.t.s[cur].len;
+  const int cur_len = uniform(seg_len(a, win, cur));
   const int ntiles = te - tb;  // tiles [tb, te) of the item's tile list
   const size_t head_page = size_t(h) * a.total_pages;
   __syncthreads();  // the previous piece of this workgroup is done with LDS
@@ -1127,9 +1142,10 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   // The first pages (K and V of tile tb, K of tile tb+1) are requested first, their page
   // indices walked from the segment table in scalar code, so that their latency overlaps
   // the query loads and the tile-table build below.
-  issue_k<G>(a.kpool + (head_page + tile_page_index(a, tb)) * G::KPAGE, smem, wave, lane);
-  issue_v<G>(a.vpool + (head_page + tile_page_index(a, tb)) * G::VPAGE, smem + G::VBASE, wave, lane);
-  if (ntiles > 1) issue_k<G>(a.kpool + (head_page + tile_page_index(a, tb + 1)) * G::KPAGE, smem + G::KPAGE, wave, lane);
+  issue_k<G>(a.kpool + (head_page + tile_page_index(a, win, tb)) * G::KPAGE, smem, wave, lane);
+  issue_v<G>(a.vpool + (head_page + tile_page_index(a, win, tb)) * G::VPAGE, smem + G::VBASE, wave, lane);
+  if (ntiles > 1)
+    issue_k<G>(a.kpool + (head_page + tile_page_index(a, win, tb + 1)) * G::KPAGE, smem + G::KPAGE, wave, lane);
 
   // Query operands (B operand of K.Q^T), resident for the whole piece.
   typename G::QOps qo;
@@ -1140,9 +1156,9 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     const int qrow = q0 + (wave * G::QB + qb) * 32 + c;
     const bool ok = qrow < n_q;
     if constexpr (G::MX) {
-      mx_queries<G>(qo, qg + (size_t(ok ? qrow : 0) * H + h) * D, ok, hl);
+      mx_queries<G>(qo, qg + (size_t(row0 + (ok ? qrow : 0)) * H + h) * D, ok, hl);
     } else {
-      const T* src = qg + (size_t(ok ? qrow : 0) * H + h) * D + hl * M::EPL;
+      const T* src = qg + (size_t(row0 + (ok ? qrow : 0)) * H + h) * D + hl * M::EPL;
 #pragma unroll
       for (int ks = 0; ks < G::KSTEPS; ++ks) {
         Op v = M::load(reinterpret_cast<const char*>(src + ks * M::K));
@@ -1174,14 +1190,14 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   for (int t = tb + tid; t < te; t += G::NW * 64) {
     int s = 0, first = 0;
     for (; s < cur; ++s) {
-      const int nt = (a.t.s[s].len + BN - 1) / BN;
+      const int nt = (seg_len(a, win, s) + BN - 1) / BN;
       if (t < first + nt) break;
       first += nt;
     }
     const int k0 = (t - first) * BN;
     const bool is_cur = s == cur;
-    const int len = a.t.s[s].len;
-    tab[t - tb] = make_int4(a.t.s[s].page + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
+    const int len = seg_len(a, win, s);
+    tab[t - tb] = make_int4(seg_page(a, win, s) + k0 / SR_PAGE_TOKENS, is_cur ? k0 : -1, (is_cur ? cur_any : len) - k0,
                             (is_cur ? cur_all : len) - k0);
   }
   // V buffer 1 zeroed: iteration 0 multiplies it by all-zero probabilities, so it must not
@@ -1280,7 +1296,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     const float l = pair_sum(st.l[qb]);
     const float inv = 1.0f / l;
     if (qrow < n_q) {
-      T* orow = og + (size_t(qrow) * H + h) * D;
+      T* orow = og + (size_t(row0 + qrow) * H + h) * D;
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
@@ -1290,7 +1306,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
           for (int e = 0; e < 4; ++e) v[e] = st.acc[qb][db][4 * ig + e] * inv;
           M::store4(orow + db * 32 + 8 * ig + 4 * hl, v);
         }
-      if (a.lse && hl == 0) a.lse[size_t(h) * n_q + qrow] = (st.m[qb] + __log2f(l)) * kLn2;
+      if (a.lse && hl == 0) a.lse[size_t(h) * lse_rows + row0 + qrow] = (st.m[qb] + __log2f(l)) * kLn2;
     }
   }
 }
@@ -1324,6 +1340,25 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   bool band1 = false;
   XcdPlan p{};
   int r = 0, pos = 0, end = 0, base = 0;  // band-1 walk; base: layout offset of item r's piece
+  if (a.win.n > 0) {
+    // Window mode: items (window, head, query tile), window-major and head-major inside a
+    // window, renumbered per XCD as below; every item runs whole over its window's keys.
+    const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
+    const int g = local + xcd * per + (xcd < rem ? xcd : rem);
+    int w = 0;
+    while (w + 1 < a.win.n && g >= a.win.item0[w + 1]) ++w;
+    w = uniform(w);
+    const int rows = a.win.frames * a.win.tok[w];
+    const int qtw = (rows + G::BM - 1) / G::BM;
+    const int loc = g - a.win.item0[w];
+    h = uniform(loc / qtw);
+    qt = uniform(loc - h * qtw);
+    int fixed = 0;
+    for (int s = 0; s < a.t.n - 1; ++s) fixed += (seg_len(a, w, s) + G::BN - 1) / G::BN;
+    te = uniform(item_tiles(qt, fixed, rows, 0, seg_len(a, w, a.t.n - 1)));
+    run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, it, w);
+    return;
+  }
   if (!a.split) {
     // One workgroup per item, renumbered so each XCD gets a contiguous range of items: the
     // query tiles of a head then share that XCD's L2 while they stream the same keys.
@@ -1397,7 +1432,7 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
 
 template <class G>
 hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb, const void* q,
-                    void* o, float* lse, float scale, const SplitWorkspace& ws, hipStream_t st) {
+                    void* o, float* lse, float scale, const SplitWorkspace& ws, hipStream_t st, const WinView* win) {
   static_assert(SR_MAX_VISIBLE_PAGES <= 32767, "tile counts are stored as int16");
   AttnArgs a{};
   a.q = q;
@@ -1414,7 +1449,7 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
   a.fixed_tiles = 0;
   for (int s = 0; s + 1 < t.n; ++s) a.fixed_tiles += (t.s[s].len + G::BN - 1) / G::BN;
   a.n_items = a.q_tiles * L.H;
-  a.split = ws.cus_per_xcd > 0 ? 1 : 0;
+  a.split = ws.cus_per_xcd > 0 && !win ? 1 : 0;
   a.cus_per_xcd = ws.cus_per_xcd;
   a.rec = ws.records;
   a.cnt = ws.counters;
@@ -1430,8 +1465,9 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
     }
     a.num_wg = 8 * per;
   } else {
-    a.num_wg = a.n_items;
+    a.num_wg = win ? win->item0[win->n] : a.n_items;
   }
+  if (win) a.win = *win;
   a.t = t;
   hipLaunchKernelGGL((chunk_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
   return hipGetLastError();
@@ -1441,16 +1477,16 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
 
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
                             const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
-                            hipStream_t st) {
+                            hipStream_t st, const WinView* win) {
   if (L.dtype == SR_MX)
-    return L.D == 128 ? launch_t<GeoMx<128>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st)
-                      : launch_t<GeoMx<64>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
+    return L.D == 128 ? launch_t<GeoMx<128>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st, win)
+                      : launch_t<GeoMx<64>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st, win);
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st)
-                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
+    return L.D == 128 ? launch_t<Geo<uint16_t, 128, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st, win)
+                      : launch_t<Geo<uint16_t, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st, win);
   // fp32 caches are head_dim 64 only (validated on the host): a double-buffered 128-key
   // fp32 tile at head_dim 128 would need 256 KiB of LDS.
-  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st);
+  return launch_t<Geo<float, 64, 1, 8>>(L, pool, t, n_q, cb, q, o, lse, softmax_scale, ws, st, win);
 }
 
 }  // namespace sr

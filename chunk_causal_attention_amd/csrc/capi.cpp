@@ -1,5 +1,6 @@
 // C ABI of the KV cache and the attention call (declared in sr.h).  Host-side validation
 // happens before anything is enqueued; see the conventions at the top of sr.h.
+#include <algorithm>
 #include <cmath>
 #include <new>
 
@@ -14,6 +15,8 @@ struct sr_kvcache {
   int32_t num_cus = 0;        // compute units of the device the cache was created on
   sr::SplitWorkspace split;   // grid 0: no workspace attached
   size_t ws_bytes = 0;
+  bool windowed = false;      // a window layout is set (sr_kvcache_set_window_layout)
+  sr::WinView win;            // the layout with its prefix sums; bank_segs = (P > 0)
 };
 
 namespace {
@@ -63,6 +66,12 @@ sr_status check_attention_args(const sr_kvcache* c, int32_t bank, const void* q,
     return sr::fail(SR_E_INVALID, "softmax_scale must be finite and > 0");
   const sr::Layout& L = c->ring.L;
   if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  return SR_OK;
+}
+
+// Calls that treat a chunk as one contiguous run of tokens do not apply to a windowed cache.
+sr_status check_not_windowed(const sr_kvcache* c) {
+  if (c->windowed) return sr::fail(SR_E_STATE, "the cache has a window layout: use the window calls");
   return SR_OK;
 }
 
@@ -120,9 +129,11 @@ sr_status sr_kvcache_append_chunk(sr_kvcache* c, int64_t chunk_id, const void* k
   if (!c) return sr::fail(SR_E_INVALID, "null cache");
   if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
     return sr::fail(SR_E_INVALID, "chunk K/V must be non-null and 16-byte aligned");
+  sr_status st = check_not_windowed(c);
+  if (st != SR_OK) return st;
   int32_t slot;
   int64_t committed;
-  sr_status st = sr::plan_append(c->ring, chunk_id, n_tokens, &slot, &committed);
+  st = sr::plan_append(c->ring, chunk_id, n_tokens, &slot, &committed);
   if (st != SR_OK) return st;
   const sr::Layout& L = c->ring.L;
   st = device_status(sr::launch_append(L, c->pool, k, v, n_tokens, L.slot_page(slot), L.pages_per_slot,
@@ -145,6 +156,7 @@ sr_status sr_kvcache_append_qkv(sr_kvcache* c, int64_t chunk_id, const void* qkv
     return sr::fail(SR_E_INVALID, "positions and gains must be non-null and 4-byte aligned");
   const sr::Layout& L = c->ring.L;
   if (L.dtype == SR_MX) return sr::fail(SR_E_UNSUPPORTED, "the fused qkv append is not available for SR_MX caches");
+  if (c->windowed) return check_not_windowed(c);
   const int32_t pairs = L.D / 2;
   const int32_t* sec = prep->rope_sections;
   if (sec[0] < 0 || sec[1] < 0 || sec[2] < 0 || sec[0] + sec[1] + sec[2] != pairs)
@@ -192,6 +204,7 @@ sr_status sr_chunk_attention(sr_kvcache* c, int32_t bank, const void* q, void* o
                              void* stream) {
   sr::clear_error();
   sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st == SR_OK) st = check_not_windowed(c);
   if (st != SR_OK) return st;
   if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
   const sr::SegTable t = make_table(c->ring, bank, nullptr);
@@ -207,6 +220,7 @@ sr_status sr_window_attention(sr_kvcache* c, int32_t bank, const void* q, int32_
                               float softmax_scale, void* stream) {
   sr::clear_error();
   sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st == SR_OK) st = check_not_windowed(c);
   if (st != SR_OK) return st;
   if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
   const int32_t moving = sr::moving_tokens(c->ring);
@@ -225,6 +239,7 @@ sr_status sr_prefix_attention(sr_kvcache* c, int32_t bank, const void* q, void* 
                               void* stream) {
   sr::clear_error();
   sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st == SR_OK) st = check_not_windowed(c);
   if (st != SR_OK) return st;
   const sr::Layout& L = c->ring.L;
   if (L.P == 0) return sr::fail(SR_E_INVALID, "the cache has no persistent tokens");
@@ -244,8 +259,10 @@ sr_status sr_kvcache_update_chunk(sr_kvcache* c, int64_t chunk_id, const void* k
   if (!c) return sr::fail(SR_E_INVALID, "null cache");
   if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
     return sr::fail(SR_E_INVALID, "chunk K/V must be non-null and 16-byte aligned");
+  sr_status st = check_not_windowed(c);
+  if (st != SR_OK) return st;
   int32_t slot;
-  sr_status st = sr::plan_update(c->ring, chunk_id, n_tokens, &slot);
+  st = sr::plan_update(c->ring, chunk_id, n_tokens, &slot);
   if (st != SR_OK) return st;
   const sr::Layout& L = c->ring.L;
   st = device_status(sr::launch_append(L, c->pool, k, v, n_tokens, L.slot_page(slot), L.pages_per_slot,
@@ -308,8 +325,119 @@ sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void
   const sr::SegTable t = make_table(c->ring, bank, &total);
   if (total > max_tokens) return sr::fail(SR_E_INVALID, "sequence has %d tokens, room for %d", total, max_tokens);
   *n_tokens = total;
-  return device_status(sr::launch_gather(L, c->pool, t, total, k_out, v_out, static_cast<hipStream_t>(stream)),
+  return device_status(sr::launch_gather(L, c->pool, t, total, k_out, v_out, c->windowed ? &c->win : nullptr,
+                                         static_cast<hipStream_t>(stream)),
                        "gather");
+}
+
+sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* layout) {
+  sr::clear_error();
+  if (!c || !layout) return sr::fail(SR_E_INVALID, "null cache or layout");
+  const sr::Layout& L = c->ring.L;
+  if (L.dtype == SR_MX) return sr::fail(SR_E_UNSUPPORTED, "window layouts are available for SR_BF16 and SR_F32 caches");
+  if (c->windowed || c->ring.has_current || c->ring.hist_count > 0)
+    return sr::fail(SR_E_STATE, "the window layout is set once, before the first append");
+  const sr_window_layout& w = *layout;
+  if (w.num_windows < 1 || w.num_windows > SR_MAX_LAYOUT_WINDOWS)
+    return sr::fail(SR_E_INVALID, "num_windows %d outside [1, %d]", w.num_windows, SR_MAX_LAYOUT_WINDOWS);
+  if (w.frames_per_chunk < 1 || w.window_pages < 1)
+    return sr::fail(SR_E_INVALID, "frames_per_chunk and window_pages must be >= 1");
+  if (int64_t(w.num_windows) * w.window_pages > L.pages_per_slot)
+    return sr::fail(SR_E_INVALID, "%d windows x %d pages exceed the %d pages of a slot", w.num_windows, w.window_pages,
+                    L.pages_per_slot);
+  sr::WinView v{};
+  v.n = w.num_windows;
+  v.frames = w.frames_per_chunk;
+  v.pages = w.window_pages;
+  v.bank_segs = L.P > 0 ? 1 : 0;
+  for (int i = 0; i < v.n; ++i) {
+    const int32_t tok = w.window_tokens[i];
+    if (tok < 1 || int64_t(tok) * v.frames > int64_t(w.window_pages) * SR_PAGE_TOKENS)
+      return sr::fail(SR_E_INVALID, "window %d: %d tokens x %d frames do not fit %d pages", i, tok, v.frames,
+                      w.window_pages);
+    v.tok[i] = int16_t(tok);
+    v.row0[i + 1] = v.row0[i] + v.frames * tok;
+    v.item0[i + 1] = v.item0[i] + L.H * ((v.frames * tok + sr::kQueryTile - 1) / sr::kQueryTile);
+  }
+  c->win = v;
+  c->windowed = true;
+  return SR_OK;
+}
+
+sr_status sr_kvcache_set_bank(sr_kvcache* c, int32_t bank, const void* k, const void* v, void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  const sr::Layout& L = c->ring.L;
+  if (bank < 0 || bank >= L.banks) return sr::fail(SR_E_INVALID, "bank %d outside [0, %d)", bank, L.banks);
+  if (L.P == 0) return sr::fail(SR_E_INVALID, "the cache has no persistent tokens");
+  if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
+    return sr::fail(SR_E_INVALID, "bank K/V must be non-null and 16-byte aligned");
+  return device_status(sr::launch_append(L, c->pool, k, v, L.P, L.bank_page(bank), L.pages_per_bank,
+                                         static_cast<hipStream_t>(stream)),
+                       "bank write");
+}
+
+sr_status sr_kvcache_append_windows(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v, void* stream) {
+  sr::clear_error();
+  if (!c) return sr::fail(SR_E_INVALID, "null cache");
+  if (!c->windowed) return sr::fail(SR_E_STATE, "no window layout: set one first");
+  if (!k || !v || !sr::aligned16(k) || !sr::aligned16(v))
+    return sr::fail(SR_E_INVALID, "chunk K/V must be non-null and 16-byte aligned");
+  const int32_t T = c->win.row0[c->win.n];
+  int32_t slot;
+  int64_t committed;
+  sr_status st = sr::plan_append(c->ring, chunk_id, T, &slot, &committed);
+  if (st != SR_OK) return st;
+  const sr::Layout& L = c->ring.L;
+  st = device_status(sr::launch_append_windows(L, c->pool, k, v, c->win, L.slot_page(slot),
+                                               static_cast<hipStream_t>(stream)),
+                     "window append");
+  if (st != SR_OK) return st;
+  sr::commit_append(c->ring, chunk_id, T);
+  return SR_OK;
+}
+
+sr_status sr_windows_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse, float softmax_scale,
+                               void* stream) {
+  sr::clear_error();
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
+  if (!c->windowed) return sr::fail(SR_E_STATE, "no window layout: set one first");
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
+  const sr::SegTable t = make_table(c->ring, bank, nullptr);
+  const sr::Layout& L = c->ring.L;
+  // The largest window's key list: the bank pages and that window's pages of every chunk.
+  int32_t most = 0;
+  for (int w = 0; w < c->win.n; ++w) most = std::max(most, c->win.frames * int32_t(c->win.tok[w]));
+  sr::SegTable widest = t;
+  for (int s = c->win.bank_segs; s < widest.n; ++s) widest.s[s].len = most;
+  st = check_pages(widest);
+  if (st != SR_OK) return st;
+  return device_status(sr::launch_attention(L, c->pool, t, c->win.row0[c->win.n], 0, q, out, lse, softmax_scale,
+                                            sr::SplitWorkspace{}, static_cast<hipStream_t>(stream), &c->win),
+                       "windows attention");
+}
+
+sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
+                              float softmax_scale, void* stream) {
+  sr::clear_error();
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
+  if (!c->windowed) return sr::fail(SR_E_STATE, "no window layout: set one first");
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
+  if (n_rows < 1) return sr::fail(SR_E_INVALID, "n_rows %d < 1", n_rows);
+  const sr::Layout& L = c->ring.L;
+  // Keys: the bank, then every window's pages of the current chunk's slot.
+  sr::SegTable t{};
+  if (L.P > 0) t.s[t.n++] = sr::DevSeg{L.bank_page(bank), L.P};
+  const int32_t cur_page = L.slot_page(c->ring.slot_of(c->ring.cur_id));
+  for (int w = 0; w < c->win.n; ++w)
+    t.s[t.n++] = sr::DevSeg{cur_page + w * c->win.pages, c->win.frames * c->win.tok[w]};
+  st = check_pages(t);
+  if (st != SR_OK) return st;
+  return device_status(sr::launch_attention(L, c->pool, t, n_rows, 0, q, out, lse, softmax_scale, c->split,
+                                            static_cast<hipStream_t>(stream)),
+                       "global attention");
 }
 
 const sr_ring* sr_kvcache_ring(const sr_kvcache* c) { return c ? &c->ring : nullptr; }

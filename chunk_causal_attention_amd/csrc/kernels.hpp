@@ -8,7 +8,10 @@
 
 namespace sr {
 
-constexpr int kMaxSegs = SR_MAX_WINDOW + 2;
+// Segments of one call: the ring's (bank, up to SR_MAX_WINDOW history chunks, current) or, for the
+// global-token attention of a windowed cache, the bank and every window's part of the current chunk.
+constexpr int kMaxSegs = SR_MAX_LAYOUT_WINDOWS + 2;
+static_assert(kMaxSegs >= SR_MAX_WINDOW + 2, "ring segments fit");
 
 // One logical key segment as the kernels see it: first pool page and valid tokens.
 struct DevSeg {
@@ -27,6 +30,21 @@ struct SegTable {
 
 // Queries per workgroup of the attention kernel (8 waves x 32 queries).
 constexpr int kQueryTile = 256;
+
+// Window layout of a windowed cache as the kernels see it (sr_window_layout plus prefix sums).
+// In window mode an attention call runs every window as its own short sequence: window w's
+// rows are packed rows [row0[w], row0[w+1]) of q / out; its keys are the call's bank segments
+// unchanged and, of every other segment (a chunk), the window's pages (page + w * pages) holding
+// frames * tok[w] tokens.  Its (head, query tile) items are [item0[w], item0[w+1]) of the launch.
+struct WinView {
+  int32_t n = 0;          // windows; 0 = not window mode
+  int32_t frames = 0;     // latent frames per chunk
+  int32_t pages = 0;      // pages per window in a slot
+  int32_t bank_segs = 0;  // leading segments of the table that are banks (not window-split)
+  int16_t tok[SR_MAX_LAYOUT_WINDOWS] = {};
+  int32_t row0[SR_MAX_LAYOUT_WINDOWS + 1] = {};
+  int32_t item0[SR_MAX_LAYOUT_WINDOWS + 1] = {};
+};
 
 // Key tiles (cache pages) that query tile `qt` visits: every page of the segments before the
 // last (`fixed_tiles`) plus the last segment's pages up to the last causal block that one of
@@ -173,6 +191,10 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 // every head, K as rows and V transposed, and zeroes those pages past token n.
 hipError_t launch_append(const Layout& L, void* pool, const void* k, const void* v, int32_t n, int32_t page0,
                          int32_t npages, hipStream_t st);
+// The same for a chunk packed window by window: window w's rows [row0[w], row0[w+1]) go to pages
+// [page0 + w * pages, page0 + (w+1) * pages), zeroed past its tokens.  One launch.
+hipError_t launch_append_windows(const Layout& L, void* pool, const void* k, const void* v, const WinView& win,
+                                 int32_t page0, hipStream_t st);
 
 // Rotary table of one call: for rotation pair j (features 2j, 2j+1), the position axis it
 // follows (0 time, 1 y, 2 x) and its angle per unit of position.
@@ -188,15 +210,17 @@ hipError_t launch_prep_append(const Layout& L, void* pool, const void* qkv, cons
                               const float* gq, const float* gk, float eps, const RopeTable& rt, void* qout,
                               int32_t page0, int32_t npages, hipStream_t st);
 
-// Writes the logical sequence of `t` ([ntok][H][D], token-major) to kout / vout.
+// Writes the logical sequence of `t` ([ntok][H][D], token-major) to kout / vout.  win (or
+// nullptr): segments past win->bank_segs are chunks of a windowed cache, read window by window.
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
-                         hipStream_t st);
+                         const WinView* win, hipStream_t st);
 
 // Attention of n_q query rows q over the key segments of t (pages of `pool`), the last
 // segment seen per causal block of cb rows (cb == 0: whole; see item_tiles).  With
-// ws.cus_per_xcd > 0 the split schedule (xcd_plan) is used.
+// ws.cus_per_xcd > 0 the split schedule (xcd_plan) is used.  win (or nullptr): window mode
+// (WinView; n_q is then the packed row count, cb 0, no split).
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
                             const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
-                            hipStream_t st);
+                            hipStream_t st, const WinView* win = nullptr);
 
 }  // namespace sr

@@ -47,21 +47,20 @@ __device__ __forceinline__ u32x4_t column_piece(const float* p, int pitch) {
                  __float_as_uint(p[3 * pitch])};
 }
 
-// Workgroup (64-token half page, head).  Both K and V rows go through LDS (coalesced
-// 16-byte reads along the features), then are written piece by piece in page order
-// (coalesced 16-byte writes).  Tokens >= n are written as zeros.
+// One workgroup's share of an append: half page `half` (64 tokens) of head h.  Both K and V
+// rows go through LDS (coalesced 16-byte reads along the features), then are written piece by
+// piece in page order (coalesced 16-byte writes).  Tokens >= n are written as zeros.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v, int n, int H,
-                                                     T* __restrict__ kpool, T* __restrict__ vpool, int total_pages,
-                                                     int page0) {
+__device__ __forceinline__ void append_half_page(const T* __restrict__ k, const T* __restrict__ v, int n, int H,
+                                                 T* __restrict__ kpool, T* __restrict__ vpool, int total_pages,
+                                                 int page0, int half, int h) {
   constexpr int E = 16 / int(sizeof(T));  // elements per 16-byte piece
   constexpr int CPR = D / E;              // pieces per token row
   constexpr int PITCH = D + E;            // LDS row pitch (elements), padded by one piece
   __shared__ __align__(16) T ktile[kAppendTokens * PITCH];
   __shared__ __align__(16) T vtile[kAppendTokens * PITCH];
 
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * kAppendTokens;  // first token of this half page (slot-relative)
+  const int t0 = half * kAppendTokens;        // first token of this half page (slot-relative)
   const int tp = t0 % SR_PAGE_TOKENS;         // its position inside the page
   const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
   const u32x4_t z = {0, 0, 0, 0};
@@ -89,6 +88,27 @@ __global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, co
     const int g = ci / D, d = ci % D;
     *reinterpret_cast<u32x4_t*>(vpage + (size_t(tp / E + g) * D + d) * E) = column_piece(vtile + g * E * PITCH + d, PITCH);
   }
+}
+
+// Workgroup (64-token half page, head) of one contiguous run of tokens.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(const T* __restrict__ k, const T* __restrict__ v, int n, int H,
+                                                     T* __restrict__ kpool, T* __restrict__ vpool, int total_pages,
+                                                     int page0) {
+  append_half_page<T, D>(k, v, n, H, kpool, vpool, total_pages, page0, blockIdx.x, blockIdx.y);
+}
+
+// Workgroup (window, 64-token half page of its pages, head) of a chunk packed window by window
+// (WinView): window w's rows [row0[w], row0[w+1]) go to its pages page0 + w * pages ...
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_windows_kernel(const T* __restrict__ k, const T* __restrict__ v, int H,
+                                                             T* __restrict__ kpool, T* __restrict__ vpool,
+                                                             int total_pages, int page0, WinView win) {
+  const int halves = win.pages * (SR_PAGE_TOKENS / kAppendTokens);
+  const int w = blockIdx.x / halves, half = blockIdx.x % halves;
+  const size_t off = size_t(win.row0[w]) * H * D;
+  append_half_page<T, D>(k + off, v + off, win.row0[w + 1] - win.row0[w], H, kpool, vpool, total_pages,
+                         page0 + w * win.pages, half, blockIdx.y);
 }
 
 // ---- fused qk-RMSNorm + rotary embedding + cache write ---------------------------------
@@ -229,10 +249,23 @@ __global__ __launch_bounds__(256) void prep_append_kernel(const T* __restrict__ 
   }
 }
 
+// Page (relative to the head's first page) and in-page token of token `off` of segment s; for a
+// windowed chunk segment (s >= win.bank_segs in window mode) `off` is a packed row.
+__device__ __forceinline__ int2 seg_token(const SegTable& tab, const WinView& win, int s, int off) {
+  int page = tab.s[s].page;
+  if (win.n > 0 && s >= win.bank_segs) {
+    int w = 0;
+    while (w + 1 < win.n && off >= win.row0[w + 1]) ++w;
+    off -= win.row0[w];
+    page += w * win.pages;
+  }
+  return make_int2(page + off / SR_PAGE_TOKENS, off % SR_PAGE_TOKENS);
+}
+
 // Thread per (token, feature).  Test/debug path; not tuned.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool, const T* __restrict__ vpool,
-                                                     SegTable tab, int total_pages, int H, int ntok,
+                                                     SegTable tab, WinView win, int total_pages, int H, int ntok,
                                                      T* __restrict__ kout, T* __restrict__ vout) {
   constexpr int E = 16 / int(sizeof(T));
   const int h = blockIdx.y;
@@ -245,8 +278,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ kpool
       off -= tab.s[s].len;
       ++s;
     }
-    const size_t page = size_t(h) * total_pages + tab.s[s].page + off / SR_PAGE_TOKENS;
-    const int tp = off % SR_PAGE_TOKENS;
+    const int2 pt = seg_token(tab, win, s, off);
+    const size_t page = size_t(h) * total_pages + pt.x;
+    const int tp = pt.y;
     const T* kpage = kpool + page * SR_PAGE_TOKENS * D;
     const T* vpage = vpool + page * SR_PAGE_TOKENS * D;
     kout[(size_t(t) * H + h) * D + d] = kpage[(size_t(d / E) * SR_PAGE_TOKENS + row_pos<T>(tp)) * E + d % E];
@@ -437,12 +471,23 @@ hipError_t prep_append_t(const Layout& L, void* pool, const void* qkv, const int
 
 template <typename T, int D>
 hipError_t gather_t(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
-                    hipStream_t st) {
+                    const WinView& win, hipStream_t st) {
   const T* kpool = static_cast<const T*>(pool);
   const T* vpool = reinterpret_cast<const T*>(static_cast<const char*>(pool) + L.half_bytes);
   dim3 grid((ntok + 63) / 64, L.H);
-  hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(256), 0, st, kpool, vpool, t, L.total_pages, L.H, ntok,
+  hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(256), 0, st, kpool, vpool, t, win, L.total_pages, L.H, ntok,
                      static_cast<T*>(kout), static_cast<T*>(vout));
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t append_windows_t(const Layout& L, void* pool, const void* k, const void* v, const WinView& win,
+                            int32_t page0, hipStream_t st) {
+  T* kpool = static_cast<T*>(pool);
+  T* vpool = reinterpret_cast<T*>(static_cast<char*>(pool) + L.half_bytes);
+  dim3 grid(win.n * win.pages * (SR_PAGE_TOKENS / kAppendTokens), L.H);
+  hipLaunchKernelGGL((append_windows_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(k),
+                     static_cast<const T*>(v), L.H, kpool, vpool, L.total_pages, page0, win);
   return hipGetLastError();
 }
 
@@ -480,14 +525,24 @@ hipError_t launch_prep_append(const Layout& L, void* pool, const void* qkv, cons
 }
 
 hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, int32_t ntok, void* kout, void* vout,
-                         hipStream_t st) {
+                         const WinView* win, hipStream_t st) {
   if (ntok == 0) return hipSuccess;
-  if (L.dtype == SR_MX)
+  if (L.dtype == SR_MX)  // windowed caches are bf16 / fp32 only (checked by the caller)
     return L.D == 128 ? mx_gather_t<128>(L, pool, t, ntok, kout, vout, st) : mx_gather_t<64>(L, pool, t, ntok, kout, vout, st);
+  const WinView none{};
+  const WinView& wv = win ? *win : none;
   if (L.dtype == SR_BF16)
-    return L.D == 128 ? gather_t<uint16_t, 128>(L, pool, t, ntok, kout, vout, st)
-                      : gather_t<uint16_t, 64>(L, pool, t, ntok, kout, vout, st);
-  return gather_t<float, 64>(L, pool, t, ntok, kout, vout, st);
+    return L.D == 128 ? gather_t<uint16_t, 128>(L, pool, t, ntok, kout, vout, wv, st)
+                      : gather_t<uint16_t, 64>(L, pool, t, ntok, kout, vout, wv, st);
+  return gather_t<float, 64>(L, pool, t, ntok, kout, vout, wv, st);
+}
+
+hipError_t launch_append_windows(const Layout& L, void* pool, const void* k, const void* v, const WinView& win,
+                                 int32_t page0, hipStream_t st) {
+  if (L.dtype == SR_BF16)
+    return L.D == 128 ? append_windows_t<uint16_t, 128>(L, pool, k, v, win, page0, st)
+                      : append_windows_t<uint16_t, 64>(L, pool, k, v, win, page0, st);
+  return append_windows_t<float, 64>(L, pool, k, v, win, page0, st);
 }
 
 }  // namespace sr

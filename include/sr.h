@@ -292,10 +292,74 @@ sr_status sr_attention_workspace_bytes(const sr_kvcache_config* cfg, int32_t num
  * it alive while calls that use it are queued. */
 sr_status sr_kvcache_set_workspace(sr_kvcache* c, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Windowed caches: the streaming decoder ("3.2 Fast Causal H3 VAE").
+ *
+ * Iteration 2: the decoder takes chunks of two latent frames; each chunk's attention sees its
+ * own latent frames and the cached K/V of the four before it (a window of W = 2 chunks), and
+ * attention runs inside non-overlapping windows of 16 x 16 tokens.  Iteration 3, item 4: each
+ * window is one short sequence (about 512 queries against 1,541 keys at 720p), padding left
+ * out, empty slots hidden.  Iterations 4 and 6: four register tokens and one class token attend
+ * to the whole frame, are rebuilt for every chunk and never cached; every window also attends
+ * to them.
+ *
+ * A cache with a window layout stores every chunk's frame tokens window by window: window w
+ * owns window_pages pages of each ring slot, from page w * window_pages of the slot, and holds
+ * frames_per_chunk * window_tokens[w] tokens (its tokens of the chunk's first latent frame,
+ * then of the second, ...).  The chunk's K/V, queries and outputs are packed the same way,
+ * windows in order, with no padding: T = frames_per_chunk * sum(window_tokens) rows.  The
+ * global tokens live in a persistent bank (persistent_tokens = their count), rewritten for
+ * every chunk with sr_kvcache_set_bank.  On such a cache sr_kvcache_append_chunk,
+ * sr_kvcache_update_chunk, sr_kvcache_append_qkv, sr_chunk_attention, sr_window_attention and
+ * sr_prefix_attention return SR_E_STATE; sr_kvcache_gather returns the packed sequence.
+ * ------------------------------------------------------------------------------------------ */
+#define SR_MAX_LAYOUT_WINDOWS 64
+
+typedef struct sr_window_layout {
+  int32_t num_windows;       /* 1 .. SR_MAX_LAYOUT_WINDOWS */
+  int32_t frames_per_chunk;  /* >= 1: latent frames per chunk */
+  int32_t window_pages;      /* >= 1: pages per window in a ring slot;
+                                num_windows * window_pages <= pages of a slot (ceil(capacity / 128)) */
+  int32_t window_tokens[SR_MAX_LAYOUT_WINDOWS]; /* 1 .. 128 * window_pages / frames_per_chunk each
+                                                   (entries past num_windows are ignored) */
+} sr_window_layout;
+
+/* Sets the window layout (host only).  Allowed once, before the first append; SR_E_STATE after
+ * it, SR_E_INVALID for a layout that does not fit the slots. */
+sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* layout);
+
+/* Rewrites the persistent tokens of `bank` in place: k, v device [P][H][D] (any cache; the
+ * decoder's global tokens, rebuilt for every chunk).  SR_E_INVALID when P == 0.  The caller may
+ * reuse k / v once the stream has passed the call. */
+sr_status sr_kvcache_set_bank(sr_kvcache* c, int32_t bank, const void* k, const void* v, void* stream);
+
+/* Appends one chunk of a windowed cache: k, v device [T][H][D] packed window by window (see
+ * above).  Ring rules and errors of sr_kvcache_append_chunk with n_tokens = T; each window's
+ * pages are zeroed past its tokens. */
+sr_status sr_kvcache_append_windows(sr_kvcache* c, int64_t chunk_id, const void* k, const void* v, void* stream);
+
+/* Window attention of the current chunk: q device [T][H][D] packed like the chunk; the rows of
+ * window w attend to the persistent tokens of `bank` (the global tokens), window w's tokens of
+ * the history chunks (oldest first) and of the current chunk, every row seeing every one of
+ * them.  out [T][H][D] in the cache dtype, lse fp32 [H][T] or NULL, softmax_scale > 0.  One
+ * launch for all windows, heads and query tiles (the workspace is not used).  SR_E_STATE
+ * without a window layout or a current chunk; q must not alias out. */
+sr_status sr_windows_attention(sr_kvcache* c, int32_t bank, const void* q, void* out, float* lse,
+                               float softmax_scale, void* stream);
+
+/* Global-token attention: n_rows >= 1 queries q (device [n_rows][H][D], the global tokens)
+ * attend to the persistent tokens of `bank` and to every window's tokens of the current chunk
+ * (the whole frame), all visible.  out [n_rows][H][D], lse [H][n_rows] or NULL.  With a
+ * workspace attached the few (head, query tile) items are split over the device's compute units
+ * by key tiles (split-K) and merged as in sr_chunk_attention.  SR_E_STATE without a window
+ * layout or a current chunk. */
+sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
+                              float softmax_scale, void* stream);
+
 /* Copies the logical key/value sequence of a call on `bank` (persistent, history oldest
  * first, current) into k_out / v_out (device, [max_tokens][H][D]), bit-exact.  *n_tokens
  * receives the length; SR_E_INVALID if it exceeds max_tokens (nothing enqueued).  For tests
- * and debugging. */
+ * and debugging.  A windowed cache's chunks come out packed window by window. */
 sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void* v_out,
                             int32_t max_tokens, int32_t* n_tokens, void* stream);
 

@@ -43,7 +43,8 @@ def _mix_scalar(x):
 
 # stream tags (top 16 bits of the sub-stream key)
 TAGS = {"Q": 1, "K": 2, "V": 3, "K_STEP0": 4, "V_STEP0": 5, "PK": 6, "PV": 7, "X30": 8, "KSTAR": 9, "VSTAR": 10,
-        "KH": 11, "VH": 12, "QM": 13, "QP": 14, "QKV": 15, "GQ": 16, "GK": 17}
+        "KH": 11, "VH": 12, "QM": 13, "QP": 14, "QKV": 15, "GQ": 16, "GK": 17,
+        "DK": 18, "DV": 19, "DQ": 20, "DGK": 21, "DGV": 22, "DGQ": 23}
 
 
 def substream_seed(base, tag, chunk=0, step=0, bank=0):

@@ -280,3 +280,123 @@ def single_step_inputs(w):
         else:
             cur = (ev["k"], ev["v"], ev["q"])
     return pk, pv, hist[-w.window:] if w.window else [], cur
+
+
+# ---------------------------------------------------------------- streaming decoder windows
+# Project page, "3.2 Fast Causal H3 VAE": chunks of two latent frames, each attending to itself and
+# the cached four before it, inside non-overlapping 16 x 16-token windows (every other layer
+# shifted by half a window), plus five global (register and class) tokens rebuilt per chunk.  The
+# latent grid of a 720p frame is 45 x 80 tokens (16x downsampling per side, as for the renderer's
+# frames); head count and width are stand-ins (the pages give none for the decoder).
+
+@dataclass(frozen=True)
+class DecoderWorkload:
+    name: str
+    index: int            # seed offset: base seed = 20261012 + index
+    heads: int
+    head_dim: int
+    grid_h: int           # latent tokens per frame: grid_h x grid_w
+    grid_w: int
+    window: int           # window side in tokens
+    shift: int            # window offset (0, or half a window on shifted layers)
+    frames: int           # latent frames per chunk
+    window_chunks: int    # cached chunks (W)
+    global_tokens: int
+    chunks: int
+    qk_std: float = 1.0
+    v_std: float = 1.0
+    dtype: str = "bf16"
+
+    @property
+    def seed(self):
+        return 20261012 + self.index
+
+    def partition(self):
+        return window_partition(self.grid_h, self.grid_w, self.window, self.shift)
+
+    @property
+    def window_tokens(self):
+        return [len(ix) for ix in self.partition()]
+
+    @property
+    def window_pages(self):
+        return -(-self.frames * max(self.window_tokens) // 128)
+
+    @property
+    def chunk_tokens(self):
+        return self.frames * self.grid_h * self.grid_w
+
+    @property
+    def capacity(self):
+        """Slot capacity (tokens) of a cache holding every window's pages."""
+        return len(self.window_tokens) * self.window_pages * 128
+
+    def scaled(self, **kw):
+        return replace(self, **kw)
+
+
+def _cuts(n, window, shift):
+    """Window boundaries along one axis: multiples of `window` moved back by `shift`."""
+    inner = [k * window - shift for k in range(1, n // window + 2) if 0 < k * window - shift < n]
+    return [0] + inner + [n]
+
+
+def window_partition(grid_h, grid_w, window, shift):
+    """Windows of one latent frame, row-major: a list of int arrays of the frame's token indices
+    (row-major inside each window)."""
+    rows, cols = _cuts(grid_h, window, shift), _cuts(grid_w, window, shift)
+    out = []
+    for r0, r1 in zip(rows[:-1], rows[1:]):
+        for c0, c1 in zip(cols[:-1], cols[1:]):
+            rr, cc = np.meshgrid(np.arange(r0, r1), np.arange(c0, c1), indexing="ij")
+            out.append((rr * grid_w + cc).ravel())
+    return out
+
+
+def pack_windows(x, partition, frames, frame_tokens):
+    """Frame-major chunk rows [frames * frame_tokens][...] -> packed window by window (window w:
+    its tokens of frame 0, then frame 1, ...)."""
+    order = np.concatenate([np.concatenate([f * frame_tokens + ix for f in range(frames)]) for ix in partition])
+    return x[order]
+
+
+DECODER_WORKLOADS = {
+    # 720p decoder layer: 45 x 80 latent tokens per frame, 15 windows (10 of 16 x 16, 5 of 13 x 16)
+    "d1": DecoderWorkload("d1", 41, 16, 128, 45, 80, 16, 0, 2, 2, 5, 4),
+    # the shifted layer: 24 windows (edges of 8, 16, 16, 5 rows and 8, 16, 16, 16, 16, 8 columns)
+    "d1s": DecoderWorkload("d1s", 42, 16, 128, 45, 80, 16, 8, 2, 2, 5, 4),
+    # parity cases: several windows of two sizes, a shifted layout, a one-window multi-page layout
+    "t_dec": DecoderWorkload("t_dec", 43, 3, 128, 20, 24, 8, 0, 2, 2, 5, 5),
+    "t_dec_s": DecoderWorkload("t_dec_s", 44, 2, 128, 20, 24, 8, 4, 2, 2, 5, 5),
+    "t_dec64": DecoderWorkload("t_dec64", 45, 2, 64, 16, 16, 16, 0, 2, 2, 5, 4),
+    "t_decf32": DecoderWorkload("t_decf32", 46, 2, 64, 12, 12, 8, 0, 2, 1, 3, 4, dtype="f32"),
+}
+
+
+def get_decoder_workload(name):
+    return DECODER_WORKLOADS[name]
+
+
+class DecoderStream:
+    """Seeded chunks of a decoder workload.  Yields per chunk {"chunk", "evict_before", "gk", "gv",
+    "gq" [G][H][D] (the global tokens, rebuilt per chunk), "k", "v", "q" [T][H][D] packed window by
+    window}.  Frame tokens are drawn frame-major (tags DK/DV/DQ) and packed with pack_windows."""
+
+    def __init__(self, w):
+        self.w = w
+
+    def __iter__(self):
+        w = self.w
+        part = w.partition()
+        ft = w.grid_h * w.grid_w
+        shape = (w.frames * ft, w.heads, w.head_dim)
+        gshape = (w.global_tokens, w.heads, w.head_dim)
+        st = _store if w.dtype == "bf16" else (lambda _w, x: np.asarray(x, dtype=np.float32))
+        for c in range(w.chunks):
+            evict = w.window_chunks > 0 and c >= w.window_chunks + 1
+            ev = {"chunk": c, "evict_before": evict}
+            for tag, key, std in (("DGK", "gk", w.qk_std), ("DGV", "gv", w.v_std), ("DGQ", "gq", w.qk_std)):
+                ev[key] = st(w, _draw(w, tag, gshape, std, chunk=c))
+            for tag, key, std in (("DK", "k", w.qk_std), ("DV", "v", w.v_std), ("DQ", "q", w.qk_std)):
+                ev[key] = st(w, pack_windows(_draw(w, tag, shape, std, chunk=c), part, w.frames, ft))
+            yield ev

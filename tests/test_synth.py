@@ -105,3 +105,55 @@ def test_closed_forms_golden():
         # a few ulps: the logits themselves are rounded decimal expansions of ln 2, ln 3, ln 4
         assert np.abs(o[0] - np.array(case["weights"])).max() <= 4e-15
         assert abs(lse[0] - case["lse"]) <= 4e-15
+
+
+def test_decoder_windows():
+    """Window partition of a latent frame: every token in exactly one window, windows row-major,
+    the shifted layout cut half a window earlier; the 720p decoder window's shape as the project
+    page gives it (queries and keys per window, the global tokens)."""
+    g = json.load(open(os.path.join(GOLDEN, "workload_shapes.json")))["decoder"]
+    w = synth.get_decoder_workload("d1")
+    assert [w.grid_h, w.grid_w] == g["grid_720p"] and w.window == g["window"]
+    assert w.frames == g["frames_per_chunk"] and w.frames * w.window_chunks == g["cached_frames"]
+    assert w.global_tokens == g["global_tokens"]
+    assert w.frames * max(w.window_tokens) == g["queries_per_window"]
+    assert w.global_tokens + (w.window_chunks + 1) * w.frames * max(w.window_tokens) == g["keys_per_window"]
+    for name in ("d1", "d1s", "t_dec", "t_dec_s", "t_dec64", "t_decf32"):
+        d = synth.get_decoder_workload(name)
+        part = d.partition()
+        ix = np.concatenate(part)
+        assert np.array_equal(np.sort(ix), np.arange(d.grid_h * d.grid_w)), name
+        assert d.frames * sum(d.window_tokens) == d.chunk_tokens
+        for p in part:   # a window is a rectangle of the grid, row-major inside
+            r, c = p // d.grid_w, p % d.grid_w
+            rect = ((r.min() + np.arange(r.max() - r.min() + 1))[:, None] * d.grid_w
+                    + c.min() + np.arange(c.max() - c.min() + 1)[None, :]).ravel()
+            assert np.array_equal(p, rect), name
+            assert len(p) == (r.max() - r.min() + 1) * (c.max() - c.min() + 1)
+            assert np.array_equal(p, np.sort(p))
+            assert r.max() - r.min() < d.window and c.max() - c.min() < d.window
+    assert synth.get_decoder_workload("d1").window_tokens == [256] * 10 + [208] * 5
+    s = synth.get_decoder_workload("d1s")
+    assert len(s.window_tokens) == 4 * 6 and s.window_tokens[0] == 8 * 8 and s.window_tokens[-1] == 5 * 8
+    # pack_windows: window by window, frames in order inside a window
+    x = np.arange(2 * 6)
+    assert pack_list(synth.pack_windows(x, [np.array([0, 1, 3]), np.array([2, 4, 5])], 2, 6)) == \
+        [0, 1, 3, 6, 7, 9, 2, 4, 5, 8, 10, 11]
+
+
+def pack_list(a):
+    return [int(v) for v in a]
+
+
+def test_decoder_stream():
+    """Seeded decoder chunks: packed shapes, eviction from chunk W + 1 on, fresh global tokens."""
+    w = synth.get_decoder_workload("t_dec")
+    evs = list(synth.DecoderStream(w))
+    assert [e["evict_before"] for e in evs] == [c >= w.window_chunks + 1 for c in range(w.chunks)]
+    T = w.chunk_tokens
+    for e in evs:
+        assert e["k"].shape == e["v"].shape == e["q"].shape == (T, w.heads, w.head_dim)
+        assert e["gk"].shape == (w.global_tokens, w.heads, w.head_dim) and e["k"].dtype == np.uint16
+    assert not np.array_equal(evs[0]["gk"], evs[1]["gk"])
+    again = next(iter(synth.DecoderStream(w)))
+    assert np.array_equal(again["k"], evs[0]["k"]) and np.array_equal(again["gq"], evs[0]["gq"])
