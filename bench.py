@@ -17,6 +17,10 @@ Consistency", prefix cache).
 queries, FP8 values: "The road to the fastest, cheapest H3", Accelerating the denoiser,
 item 2); its roofline peak is the MFMA peak of that mix (below).
 
+`--workload d1` (or d1s, the shifted layer) times one layer of the streaming decoder at 720p
+("3.2 Fast Causal H3 VAE"): per step, evict, rewrite the five global tokens, append the chunk
+window by window, every window's attention in one launch and the global tokens' attention.
+
 `--workload c1p` runs c1 chunk-steps whose chunk enters through the fused append
 (sr_kvcache_append_qkv: qk-RMSNorm, rotary embedding at stream-absolute positions and the
 cache write in one kernel, "3.2 Fast Causal H3 VAE", iteration 6) and reports that kernel's
@@ -56,20 +60,23 @@ MX_WORKLOADS = {"c1x": "c1"}
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 220096.4, "write_kib": 103835.4,
-           "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
-    "c1p": {"fetch_kib": 221461.8, "write_kib": 103832.9,
-            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
-    "c1w": {"fetch_kib": 320248.3, "write_kib": 125267.3,
-            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
-    "c1x": {"fetch_kib": 108768.5, "write_kib": 148875.6,
-            "attention_sha256": "b033f379033847358df1bf73e1dcee15a1cbca1cae6f5d49555686a1d810348c"},
+    "c1": {"fetch_kib": 219860.3, "write_kib": 103828.4,
+           "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    "c1p": {"fetch_kib": 220558.8, "write_kib": 103844.3,
+            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    "c1w": {"fetch_kib": 320251.5, "write_kib": 125272.8,
+            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    "c1x": {"fetch_kib": 108773.7, "write_kib": 148872.4,
+            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    # the decoder layer's dominant kernel: windows_attention_kernel
+    "d1": {"fetch_kib": 115756.3, "write_kib": 32170.6,
+           "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
 PREP_TRAFFIC = {
-    "c1p": {"fetch_kib": 42279.7, "write_kib": 84912.0,
-            "kv_sha256": "5eb0934b2d5d47985be424a13a54054439a4d72ddeaccfa894411b2f88ebb577"},
+    "c1p": {"fetch_kib": 42280.0, "write_kib": 84912.0,
+            "kv_sha256": "e3effd5a17e9922ea96b7527006304fd446d54a7922c56e90b390b58904ece1e"},
 }
 KV_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "kv_kernels.hip")
 
@@ -493,12 +500,224 @@ def run_prep(args, w):
     return res
 
 
+# Decoder layers: the streaming decoder's window attention ("3.2 Fast Causal H3 VAE").
+DECODER_WORKLOADS = ("d1", "d1s")
+
+
+def decoder_flops(w):
+    """Algorithmic flops of one decoder layer's attention at full ring: every window's rows over
+    the global tokens and the window's tokens of W + 1 chunks, and the global tokens over the
+    global tokens and the whole chunk.  Returns (windows, global)."""
+    r = w.frames * np.asarray(w.window_tokens, dtype=np.float64)
+    f_win = 4.0 * w.heads * w.head_dim * float((r * (w.global_tokens + (w.window_chunks + 1) * r)).sum())
+    f_glob = 4.0 * w.heads * w.head_dim * w.global_tokens * float(w.global_tokens + w.chunk_tokens)
+    return f_win, f_glob
+
+
+def global_bytes(w):
+    """Algorithmic bytes of one global-token call: the K/V of the global tokens and of every frame
+    token of the chunk, read once; the queries read and the outputs written once."""
+    es = 2 if w.dtype == "bf16" else 4
+    G = w.global_tokens
+    return es * w.heads * w.head_dim * (2 * (G + w.chunk_tokens) + 2 * G)
+
+
+# Bytes past L2 per launch of the few-row split-K kernel (few_attention_kernel), as TRAFFIC.
+FEW_TRAFFIC = {
+    "d1": {"fetch_kib": 30546.9, "write_kib": 1307.5,
+           "few_sha256": "fa20788a3e2c7f86260e946df07eb20baa138bd197b344c81f48a9827915d382"},
+}
+FEW_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "few_attention.hip")
+
+
+def measured_few_traffic(workload):
+    import hashlib
+    t = FEW_TRAFFIC.get(workload)
+    if not t or t["few_sha256"] != hashlib.sha256(open(FEW_SRC, "rb").read()).hexdigest():
+        return None
+    return (2.0 * t["fetch_kib"] + 1.0 * t["write_kib"]) * 1024.0
+
+
+def cpu_baseline_decoder(w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on whole heads of the decoder layer's full-ring chunk."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    z = np.zeros((1, w.global_tokens, w.heads, w.head_dim), dtype=np.uint16)
+    m = oracle.StreamingCache(z, z, w.window_chunks)
+    ev = None
+    for ev in synth.DecoderStream(w):
+        if ev["evict_before"]:
+            m.evict()
+        m.set_bank(0, ev["gk"], ev["gv"])
+        m.append(ev["chunk"], ev["k"], ev["v"])
+    scale = 1.0 / math.sqrt(w.head_dim)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        oracle.decoder_window_attention(m, w.window_tokens, w.frames, ev["q"], scale, w.dtype, heads=[heads])
+        oracle.decoder_global_attention(m, ev["gq"], scale, w.dtype, heads=[heads])
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = sum(decoder_flops(w)) * heads / w.heads
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads of {w.name}: every window's rows and the global rows of the "
+                      f"full-ring chunk, fp64 numpy oracle, {dt:.1f} s wall"}
+
+
+def run_decoder(args, w):
+    """Decoder-layer step: evict the oldest chunk, rewrite the global tokens, append the chunk
+    window by window, every window's attention (one launch) and the global tokens' attention."""
+    import torch
+    import synth
+    import chunk_causal_attention_amd as sr
+    from synth.torch_io import to_dev
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    evs = list(synth.DecoderStream(w))
+    sets = [tuple(to_dev(ev[x], w.dtype) for x in ("gk", "gv", "k", "v", "q", "gq")) for ev in evs]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    G, T = w.global_tokens, w.chunk_tokens
+    cfg = sr.config_for(w.heads, w.head_dim, G, w.capacity, w.window_chunks, w.capacity, 1,
+                        sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32)
+    zero = torch.zeros((1, G, w.heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
+    t_init = time.perf_counter()
+    layers = []
+    ws = None if args.no_split else sr.workspace_for(cfg)
+    for _ in range(args.layers):
+        c = sr.KVCache(cfg, zero, zero, workspace=ws)
+        c.set_window_layout(w.window_tokens, w.frames, w.window_pages)
+        for j in range(w.window_chunks + 1):
+            gk, gv, k, v, _, _ = sets[j % len(sets)]
+            c.set_bank(0, gk, gv)
+            c.append_windows(j, k, v)
+        layers.append({"cache": c, "next": w.window_chunks + 1})
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t_init
+    out = torch.empty((T, w.heads, w.head_dim), dtype=zero.dtype, device=dev)
+    lse = torch.empty((w.heads, T), dtype=torch.float32, device=dev)
+    gout = torch.empty((G, w.heads, w.head_dim), dtype=zero.dtype, device=dev)
+    glse = torch.empty((w.heads, G), dtype=torch.float32, device=dev)
+    ev_sets = []
+
+    def step(i, timed):
+        L = layers[i % len(layers)]
+        c = L["cache"]
+        cid = L["next"]
+        L["next"] += 1
+        gk, gv, k, v, q, gq = sets[cid % len(sets)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if w.window_chunks > 0:
+            c.evict()
+        if timed:
+            e[0].record()
+        c.set_bank(0, gk, gv)
+        c.append_windows(cid, k, v)
+        if timed:
+            e[1].record()
+        c.windows_attention(0, q, out=out, lse=lse, softmax_scale=scale)
+        if timed:
+            e[2].record()
+        c.global_attention(0, gq, out=gout, lse=glse, softmax_scale=scale)
+        if timed:
+            e[3].record()
+            ev_sets.append(e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in ev_sets])
+    t_win = np.array([e[1].elapsed_time(e[2]) for e in ev_sets])
+    t_glob = np.array([e[2].elapsed_time(e[3]) for e in ev_sets])
+    ms_step = elapsed * 1e3 / args.steps
+    f_win, f_glob = decoder_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    win_tflops = f_win / (t_win.mean() * 1e-3) / 1e12
+    glob_gbps = global_bytes(w) / (t_glob.mean() * 1e-3) / 1e9
+    stock = w == synth.get_decoder_workload(w.name)   # counters were taken on the stock shapes
+    traffic = measured_traffic(w.name) if stock else None
+    if args.traffic_kib is not None:
+        traffic = args.traffic_kib * 1024.0
+    es = 2 if w.dtype == "bf16" else 4
+    # K and V read once, their pages (zero tails included) written once: the bank's, then every window's.
+    write_bytes = es * w.heads * w.head_dim * 2 * (G + 128 * math.ceil(G / 128) + T + w.capacity)
+    rmax = w.frames * max(w.window_tokens)
+    res = {
+        "metric": "decoder-layer attention TFLOP/s per chunk (frac of bf16 MFMA peak), 1 MI355X",
+        "value": round((f_win + f_glob) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: decoder layer at {w.grid_h}x{w.grid_w} latent tokens, {len(w.window_tokens)} "
+                        f"windows of {w.window}x{w.window} tokens (offset {w.shift}), {w.frames} frames per chunk, "
+                        f"{w.window_chunks} cached chunks, {G} global tokens, {w.heads} heads x {w.head_dim}",
+            "heads": w.heads, "head_dim": w.head_dim, "windows": len(w.window_tokens), "queries_per_chunk": T,
+            "largest_window": f"{rmax} queries x {G + (w.window_chunks + 1) * rmax} keys",
+            "layers_cycled": args.layers,
+            "step": "evict + set_bank + append_windows + windows_attention + global_attention",
+            "global_schedule": "whole items" if args.no_split else "key tiles split evenly over the CUs",
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(win_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(win_tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "global_roofline": {
+            "bound": "hbm",
+            "achieved": round(glob_gbps, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(glob_gbps / PEAK_HBM_GBS, 4),
+            "traffic": measured_few_traffic(w.name) if stock else None,
+        },
+        "ms_windows_attention": round(float(t_win.mean()), 4),
+        "ms_windows_attention_p10_p50_p90": [round(float(np.percentile(t_win, p)), 4) for p in (10, 50, 90)],
+        "ms_global_attention": round(float(t_glob.mean()), 4),
+        "global_attention_TFLOPs": round(f_glob / (t_glob.mean() * 1e-3) / 1e12, 3),
+        "ms_kv_writes": round(float(t_write.mean()), 4),
+        "kv_writes_GBps": round(write_bytes / (t_write.mean() * 1e-3) / 1e9, 1),
+        "windows_gflop_per_call": round(f_win / 1e9, 3),
+        "global_gflop_per_call": round(f_glob / 1e9, 4),
+        "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
+    }
+    for L in layers:
+        L["cache"].close()
+    if args.copy_calibration:
+        copy_calibration(res, torch, dev)
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decoder(w, args.cpu_budget)
+    return res
+
+
 def run(args):
     import torch
     import synth
     import chunk_causal_attention_amd as sr
 
     sr.load()
+    if args.workload in DECODER_WORKLOADS:
+        w = synth.get_decoder_workload(args.workload)
+        if args.window_chunks is not None:
+            w = w.scaled(window_chunks=args.window_chunks, chunks=args.window_chunks + 2)
+        return run_decoder(args, w)
     mx = args.workload in MX_WORKLOADS
     w = synth.get_workload(MX_WORKLOADS.get(args.workload, args.workload))
     if w.name in WINDOW_WORKLOADS:
@@ -624,8 +843,11 @@ def main():
     ap.add_argument("--workload", default="c1",
                     help="c1 (default), c3, c4, c1s, c4s; c1w: the page-literal window variant at c1 shapes; "
                          "c1p: c1 chunk-steps entering through the fused qk-RMSNorm + rotary append; "
-                         "c1x: c1 chunk-steps on the reduced-precision (MXFP6/FP8) cache")
+                         "c1x: c1 chunk-steps on the reduced-precision (MXFP6/FP8) cache; "
+                         "d1, d1s: a 720p streaming-decoder layer (plain or shifted windows)")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
+    ap.add_argument("--window-chunks", type=int, default=None,
+                    help="decoder workloads: cached chunks W (default: the workload's, 2 = four latent frames)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-split", action="store_true",
                     help="run attention without a workspace (one workgroup per head and query tile)")
@@ -636,7 +858,7 @@ def main():
                     help="override: scaled KiB per attention launch from rocprofv3 FETCH/WRITE runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU: the multi-GPU path is not implemented",
                           "n_gpus": args.gpus}))
         raise SystemExit(2)
     res = run(args)

@@ -1340,25 +1340,6 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   bool band1 = false;
   XcdPlan p{};
   int r = 0, pos = 0, end = 0, base = 0;  // band-1 walk; base: layout offset of item r's piece
-  if (a.win.n > 0) {
-    // Window mode: items (window, head, query tile), window-major and head-major inside a
-    // window, renumbered per XCD as below; every item runs whole over its window's keys.
-    const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
-    const int g = local + xcd * per + (xcd < rem ? xcd : rem);
-    int w = 0;
-    while (w + 1 < a.win.n && g >= a.win.item0[w + 1]) ++w;
-    w = uniform(w);
-    const int rows = a.win.frames * a.win.tok[w];
-    const int qtw = (rows + G::BM - 1) / G::BM;
-    const int loc = g - a.win.item0[w];
-    h = uniform(loc / qtw);
-    qt = uniform(loc - h * qtw);
-    int fixed = 0;
-    for (int s = 0; s < a.t.n - 1; ++s) fixed += (seg_len(a, w, s) + G::BN - 1) / G::BN;
-    te = uniform(item_tiles(qt, fixed, rows, 0, seg_len(a, w, a.t.n - 1)));
-    run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, it, w);
-    return;
-  }
   if (!a.split) {
     // One workgroup per item, renumbered so each XCD gets a contiguous range of items: the
     // query tiles of a head then share that XCD's L2 while they stream the same keys.
@@ -1430,6 +1411,32 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   }
 }
 
+// Window mode (a.win.n > 0): one workgroup per item (window, head, query tile), window-major
+// and head-major inside a window, renumbered so each XCD gets a contiguous range of items (the
+// query tiles of a window and head share that XCD's L2); every item runs whole over its
+// window's keys.
+template <class G>
+__global__ __launch_bounds__(G::NW * 64, G::NW / 4) void windows_attention_kernel(const AttnArgs a) {
+  __shared__ __align__(1024) char smem[G::LDS_BYTES];
+  __shared__ int flag;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
+  const int g = local + xcd * per + (xcd < rem ? xcd : rem);
+  int w = 0;
+  while (w + 1 < a.win.n && g >= a.win.item0[w + 1]) ++w;
+  w = uniform(w);
+  const int rows = a.win.frames * a.win.tok[w];
+  const int qtw = (rows + G::BM - 1) / G::BM;
+  const int loc = g - a.win.item0[w];
+  const int h = uniform(loc / qtw);
+  const int qt = uniform(loc - h * qtw);
+  int fixed = 0;
+  for (int s = 0; s < a.t.n - 1; ++s) fixed += (seg_len(a, w, s) + G::BN - 1) / G::BN;
+  const int te = uniform(item_tiles(qt, fixed, rows, 0, seg_len(a, w, a.t.n - 1)));
+  run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{}, w);
+}
+
 template <class G>
 hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb, const void* q,
                     void* o, float* lse, float scale, const SplitWorkspace& ws, hipStream_t st, const WinView* win) {
@@ -1469,7 +1476,12 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
   }
   if (win) a.win = *win;
   a.t = t;
-  hipLaunchKernelGGL((chunk_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
+  if (win) {
+    if constexpr (G::MX) return hipErrorNotSupported;  // refused on the host: no windowed SR_MX caches
+    else hipLaunchKernelGGL((windows_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((chunk_attention_kernel<G>), dim3(a.num_wg), dim3(G::NW * 64), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -435,6 +435,10 @@ sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_
     t.s[t.n++] = sr::DevSeg{cur_page + w * c->win.pages, c->win.frames * c->win.tok[w]};
   st = check_pages(t);
   if (st != SR_OK) return st;
+  if (sr::few_attention_fits(L, t, n_rows, c->split))
+    return device_status(sr::launch_few_attention(L, c->pool, t, n_rows, q, out, lse, softmax_scale, c->split,
+                                                  static_cast<hipStream_t>(stream)),
+                         "global attention");
   return device_status(sr::launch_attention(L, c->pool, t, n_rows, 0, q, out, lse, softmax_scale, c->split,
                                             static_cast<hipStream_t>(stream)),
                        "global attention");

@@ -223,4 +223,12 @@ hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t
                             const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,
                             hipStream_t st, const WinView* win = nullptr);
 
+// Split-K attention of at most kFewRows query rows (bf16 caches, head_dim 64 or 128, a
+// workspace attached): every segment of t visible to every row, one workgroup per (head, two
+// pages), records merged by each head's last workgroup (few_attention.hip).
+constexpr int32_t kFewRows = 32;
+bool few_attention_fits(const Layout& L, const SegTable& t, int32_t n_q, const SplitWorkspace& ws);
+hipError_t launch_few_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, const void* q,
+                                void* o, float* lse, float softmax_scale, const SplitWorkspace& ws, hipStream_t st);
+
 }  // namespace sr

@@ -230,3 +230,37 @@ def test_decoder_without_global_tokens(sr):
         gates.assert_gates(harness.widen_host(harness.to_host(go, "bf16"), "bf16"), g_ref, "bf16", f"global {c}")
         assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-2
     cache.close()
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_global_attention_row_counts(sr, head_dim):
+    """Global-token attention for 1 to 33 query rows (32 is the most the few-row split-K kernel
+    takes; 33 runs the chunk-attention kernel), with and without a workspace, against the oracle;
+    a second call gives the same bits (the arrival counters are left at zero)."""
+    import torch
+    rng = np.random.default_rng(13 + head_dim)
+    H, G, tok, frames = 3, 5, [64, 100, 7, 64], 2
+    cap = len(tok) * 2 * 128
+    T = frames * sum(tok)
+    bf = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    gk, gv = bf(1, G, H, head_dim), bf(1, G, H, head_dim)
+    model = oracle.StreamingCache(gk, gv, 1)
+    k, v = bf(T, H, head_dim), bf(T, H, head_dim)
+    model.append(0, k, v)
+    scale = 1.0 / np.sqrt(head_dim)
+    for ws in ("own", None):
+        cache = sr.KVCache(sr.config_for(H, head_dim, G, cap, 1, cap, 1, sr.SR_BF16),
+                           harness.to_dev(gk, "bf16"), harness.to_dev(gv, "bf16"), workspace=ws)
+        cache.set_window_layout(tok, frames, 2)
+        cache.append_windows(0, harness.to_dev(k, "bf16"), harness.to_dev(v, "bf16"))
+        for n in (1, 5, 31, 32, 33):
+            gq = bf(n, H, head_dim)
+            lse = torch.full((H, n), float("nan"), dtype=torch.float32, device="cuda")
+            o = cache.global_attention(0, harness.to_dev(gq, "bf16"), lse=lse, softmax_scale=scale)
+            o2 = cache.global_attention(0, harness.to_dev(gq, "bf16"), softmax_scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o2), (ws, n)
+            g_ref, l_ref = oracle.decoder_global_attention(model, gq, scale, "bf16")
+            gates.assert_gates(harness.widen_host(harness.to_host(o, "bf16"), "bf16"), g_ref, "bf16", f"{ws} {n}")
+            assert np.abs(lse.cpu().numpy() - l_ref).max() <= 2e-2, (ws, n)
+        cache.close()
