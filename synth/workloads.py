@@ -370,6 +370,8 @@ DECODER_WORKLOADS = {
     "t_dec_s": DecoderWorkload("t_dec_s", 44, 2, 128, 20, 24, 8, 4, 2, 2, 5, 5),
     "t_dec64": DecoderWorkload("t_dec64", 45, 2, 64, 16, 16, 16, 0, 2, 2, 5, 4),
     "t_decf32": DecoderWorkload("t_decf32", 46, 2, 64, 12, 12, 8, 0, 2, 1, 3, 4, dtype="f32"),
+    # the most windows a layout takes (64), each one token per frame: every key tile nearly empty
+    "t_decmax": DecoderWorkload("t_decmax", 47, 2, 128, 8, 8, 1, 0, 2, 2, 5, 4),
 }
 
 

@@ -89,7 +89,7 @@ def check_stats(w, stats):
 
 
 @pytest.mark.parametrize("schedule", ["split", "whole"])
-@pytest.mark.parametrize("name", ["t_dec", "t_dec_s", "t_dec64", "t_decf32"])
+@pytest.mark.parametrize("name", ["t_dec", "t_dec_s", "t_dec64", "t_decf32", "t_decmax"])
 def test_decoder_parity_every_element(sr, name, schedule):
     w = synth.get_decoder_workload(name)
     say(f"[decoder] {name} ({schedule}): H={w.heads} D={w.head_dim} windows={len(w.window_tokens)} "

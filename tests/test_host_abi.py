@@ -38,6 +38,21 @@ def test_binding_constants_match_header(sr):
     assert defs["SR_PAGE_TOKENS"] == sr.PAGE_TOKENS
     assert defs["SR_MAX_WINDOW"] == sr.MAX_WINDOW
     assert defs["SR_MAX_VISIBLE_PAGES"] == sr.MAX_VISIBLE_PAGES
+    assert defs["SR_MAX_LAYOUT_WINDOWS"] == sr.MAX_LAYOUT_WINDOWS
+
+
+def test_window_layout_struct(sr):
+    """sr_window_layout as the header declares it: three int32 and SR_MAX_LAYOUT_WINDOWS token
+    counts, unused entries zero; the binding refuses more windows than the struct holds."""
+    import ctypes
+    assert ctypes.sizeof(sr.sr_window_layout) == 4 * (3 + sr.MAX_LAYOUT_WINDOWS)
+    lay = sr.window_layout([256] * 10 + [208] * 5, 2, 4)
+    assert (lay.num_windows, lay.frames_per_chunk, lay.window_pages) == (15, 2, 4)
+    assert list(lay.window_tokens) == [256] * 10 + [208] * 5 + [0] * (sr.MAX_LAYOUT_WINDOWS - 15)
+    full = sr.window_layout([1] * sr.MAX_LAYOUT_WINDOWS, 2, 1)
+    assert full.num_windows == sr.MAX_LAYOUT_WINDOWS
+    with pytest.raises(ValueError):
+        sr.window_layout([1] * (sr.MAX_LAYOUT_WINDOWS + 1), 2, 1)
 
 
 def test_status_strings(sr):

@@ -118,7 +118,7 @@ def test_decoder_windows():
     assert w.global_tokens == g["global_tokens"]
     assert w.frames * max(w.window_tokens) == g["queries_per_window"]
     assert w.global_tokens + (w.window_chunks + 1) * w.frames * max(w.window_tokens) == g["keys_per_window"]
-    for name in ("d1", "d1s", "t_dec", "t_dec_s", "t_dec64", "t_decf32"):
+    for name in synth.DECODER_WORKLOADS:
         d = synth.get_decoder_workload(name)
         part = d.partition()
         ix = np.concatenate(part)
