@@ -204,15 +204,17 @@ def test_decoder_call_errors(sr):
     nog.close()
 
 
-def test_decoder_without_global_tokens(sr):
+@pytest.mark.parametrize("workspace", ["own", None])
+def test_decoder_without_global_tokens(sr, workspace):
     """A windowed cache with no persistent tokens: each window over its own keys only, the
-    global call over the current chunk only; every element against the oracle."""
+    global call over the current chunk only (the few-row kernel with a workspace, the chunk
+    kernel without); every element against the oracle."""
     import torch
     rng = np.random.default_rng(12)
     H, D, cap, tok, frames = 2, 128, 6 * 128, [64, 100, 7], 2
     T = frames * sum(tok)
     bf = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
-    cache = sr.KVCache(sr.config_for(H, D, 0, cap, 2, cap, 1, sr.SR_BF16), workspace=None)
+    cache = sr.KVCache(sr.config_for(H, D, 0, cap, 2, cap, 1, sr.SR_BF16), workspace=workspace)
     cache.set_window_layout(tok, frames, 2)
     z = np.zeros((1, 0, H, D), dtype=np.uint16)
     model = oracle.StreamingCache(z, z, 2)
