@@ -349,10 +349,13 @@ sr_status sr_windows_attention(sr_kvcache* c, int32_t bank, const void* q, void*
 
 /* Global-token attention: n_rows >= 1 queries q (device [n_rows][H][D], the global tokens)
  * attend to the persistent tokens of `bank` and to every window's tokens of the current chunk
- * (the whole frame), all visible.  out [n_rows][H][D], lse [H][n_rows] or NULL.  With a
- * workspace attached the few (head, query tile) items are split over the device's compute units
- * by key tiles (split-K) and merged as in sr_chunk_attention.  SR_E_STATE without a window
- * layout or a current chunk. */
+ * (the whole frame), all visible.  out [n_rows][H][D], lse [H][n_rows] or NULL.  Iteration 6:
+ * split-K.  On a bf16 cache with a workspace attached and n_rows <= 32, every head's keys are
+ * split two pages per workgroup over the device and each head's partial results are merged by
+ * its last workgroup (in a fixed order: repeated calls give the same bits); otherwise the call
+ * runs on the chunk-attention kernel (with its split schedule when a workspace is attached).
+ * The workspace must not be in use by a call on another stream.  SR_E_STATE without a window
+ * layout or a current chunk; SR_E_INVALID for n_rows < 1. */
 sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
                               float softmax_scale, void* stream);
 
