@@ -310,7 +310,7 @@ def run_window(args, w):
     F = window_flops(w)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    traffic = (measured_traffic(w.name) if w == synth.get_workload(w.name) else None)
     if args.traffic_kib is not None:
         traffic = args.traffic_kib * 1024.0
     res = {
@@ -473,7 +473,7 @@ def run_prep(args, w):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / peak, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": (measured_traffic(w.name) if w == synth.get_workload(w.name) else None),
         },
         "prep_roofline": {
             "bound": "hbm",
@@ -481,7 +481,7 @@ def run_prep(args, w):
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(prep_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": measured_prep_traffic(w.name),
+            "traffic": (measured_prep_traffic(w.name) if w == synth.get_workload(w.name) else None),
         },
         "ms_attention": round(float(t_attn.mean()), 4),
         "ms_attention_p10_p50_p90": [round(float(np.percentile(t_attn, p)), 4) for p in (10, 50, 90)],
@@ -720,6 +720,9 @@ def run(args):
         return run_decoder(args, w)
     mx = args.workload in MX_WORKLOADS
     w = synth.get_workload(MX_WORKLOADS.get(args.workload, args.workload))
+    if args.heads is not None:
+        # one GPU's share of a run whose heads are sharded over several GPUs (same shapes, fewer heads)
+        w = w.scaled(heads=args.heads)
     if w.name in WINDOW_WORKLOADS:
         return run_window(args, w)
     if w.name in PREP_WORKLOADS:
@@ -785,7 +788,7 @@ def run(args):
     peak = PEAK_MX_TFLOPS if mx else (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS)
     attn_tflops = F / (t_attn.mean() * 1e-3) / 1e12
     name = args.workload
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name) if args.heads is None else None
     if args.traffic_kib is not None:
         traffic = args.traffic_kib * 1024.0
     res = {
@@ -846,6 +849,8 @@ def main():
                          "c1x: c1 chunk-steps on the reduced-precision (MXFP6/FP8) cache; "
                          "d1, d1s: a 720p streaming-decoder layer (plain or shifted windows)")
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches cycled over")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="chunk workloads: heads of one GPU's share of a head-sharded run (e.g. 3 = 24 over 8)")
     ap.add_argument("--window-chunks", type=int, default=None,
                     help="decoder workloads: cached chunks W (default: the workload's, 2 = four latent frames)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")

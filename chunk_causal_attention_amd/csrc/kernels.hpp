@@ -164,6 +164,24 @@ inline XcdPlan xcd_plan(int32_t x, int32_t n_items, int32_t q_tiles, int32_t fix
   return p;
 }
 
+// Even ("fan") split for launches with fewer (head, query tile) items than compute units, where
+// the two-band plan above would leave most units idle (a one-GPU share of a head-sharded run):
+// each item's key tiles are cut into P equal pieces, P at most the units per item, every piece
+// at least kFanMinTiles long (twice the measured start-and-finish cost of a piece), and P at
+// most kFanMaxPieces (the merging piece reads the records one after the other, about a
+// quarter tile-time each).  Piece p of item i leaves its record in slot i P + p; the item's
+// last piece to arrive (counter i) merges them in slot order.  Returns P, or 1 for no fan split.
+constexpr int32_t kFanMinTiles = 8;
+constexpr int32_t kFanMaxPieces = 32;
+inline int32_t fan_pieces(int32_t n_items, int32_t min_tiles, int32_t C) {
+  const int32_t units = 8 * C;
+  if (n_items <= 0 || n_items >= units) return 1;
+  int32_t p = units / n_items;
+  if (p > min_tiles / kFanMinTiles) p = min_tiles / kFanMinTiles;
+  if (p > kFanMaxPieces) p = kFanMaxPieces;
+  return p < 2 ? 1 : p;
+}
+
 // C of the split schedule for a device with num_cus compute units.
 inline int32_t split_cus_per_xcd(int32_t num_cus) {
   const int32_t C = num_cus / 8;

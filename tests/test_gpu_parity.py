@@ -126,8 +126,8 @@ def test_parity_full_size_sampled(sr, name, schedule):
 
 
 def test_one_gpu_share_of_sharded_run(sr):
-    """c1 shapes with 3 heads (one GPU's share when 24 heads are sharded over 8): about 7
-    items per XCD, for which the split plan runs the items whole on the split workgroups."""
+    """c1 shapes with 3 heads (one GPU's share when 24 heads are sharded over 8): 57 items,
+    fewer than the compute units, so the workspace runs each as 4 equal pieces (fan split)."""
     w = synth.get_workload("c1").scaled(heads=3)
     rows = harness.sample_rows(w.chunk)
     say(f"[share] c1 x 3 heads: {len(rows)} sampled rows")
@@ -319,6 +319,10 @@ EDGE = [  # H, D, P, cap, W, cb, dtype, chunks
     ("short chunk in a large slot", 2, 128, 300, 1000, 2, 1000, "bf16", [1000, 1000, 3]),
     ("one-token history chunks", 3, 128, 7, 40, 3, 17, "bf16", [1, 1, 1, 40]),
     ("no prefix, full window", 2, 64, 0, 256, 3, 64, "bf16", [256] * 6),
+    # fewer items than compute units: the workspace runs each item as P equal pieces (fan split)
+    ("fan split, long prefix", 2, 128, 8000, 300, 1, 300, "bf16", [300, 300]),
+    ("fan split, causal blocks", 3, 128, 4000, 700, 1, 100, "bf16", [700, 700]),
+    ("fan split, fp32", 2, 64, 3000, 200, 1, 200, "f32", [200, 200]),
 ]
 
 
