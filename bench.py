@@ -60,17 +60,17 @@ MX_WORKLOADS = {"c1x": "c1"}
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 219860.3, "write_kib": 103828.4,
-           "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
-    "c1p": {"fetch_kib": 220558.8, "write_kib": 103844.3,
-            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
-    "c1w": {"fetch_kib": 320251.5, "write_kib": 125272.8,
-            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
-    "c1x": {"fetch_kib": 108773.7, "write_kib": 148872.4,
-            "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    "c1": {"fetch_kib": 220806.4, "write_kib": 103851.7,
+           "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
+    "c1p": {"fetch_kib": 222259.8, "write_kib": 103827.6,
+            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
+    "c1w": {"fetch_kib": 320252.2, "write_kib": 125268.2,
+            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
+    "c1x": {"fetch_kib": 106744.0, "write_kib": 146810.5,
+            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
     # the decoder layer's dominant kernel: windows_attention_kernel
-    "d1": {"fetch_kib": 115756.3, "write_kib": 32170.6,
-           "attention_sha256": "ecc51bf6f1df53e29ca386b10feb139f029bb74f4ba0b11bbfe4bfdcecd2ec75"},
+    "d1": {"fetch_kib": 115755.9, "write_kib": 32166.4,
+           "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
