@@ -78,6 +78,36 @@ def test_prep_every_element(sr, dtype, D, n, first_frame):
     cache.close()
 
 
+def test_prep_full_size_every_element(sr):
+    """The benchmark's c1p call: a 4680-token chunk (three 52 x 30 latent frames from stream frame
+    300 on) x 24 heads x 128 into a c1 cache, rotation sections 16/24/24, base 10^4, eps 10^-6;
+    every element of the prepared q and k against the oracle, V bit for bit."""
+    import torch
+    w = synth.get_workload("c1p")
+    n, H, D = w.chunk, w.heads, w.head_dim
+    say(f"[prep full] c1p: {n} tokens x {H} heads x {D}")
+    qkv = synth.qkv_inputs(w, n, chunk=100)
+    pos = synth.latent_positions(n, 1560, 52, 300)
+    gq, gk = synth.prep_gains(w)
+    sec = _sections(D)
+    cfg = harness.cfg_of(sr, w)
+    pk, pv = synth.SessionStream(w).persistent()   # storage arrays [1][P][H][D]
+    cache = sr.KVCache(cfg, harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype))
+    dq = cache.append_qkv(0, harness.to_dev(qkv, w.dtype), torch.from_numpy(pos).cuda(), torch.from_numpy(gq).cuda(),
+                          torch.from_numpy(gk).cuda(), sr.qk_prep(sec, 10000.0, 1e-6))
+    kg, vg = cache.gather(0)
+    torch.cuda.synchronize()
+    q_ref, k_ref, _ = oracle.prep_qkv(qkv, pos, gq.astype(np.float64), gk.astype(np.float64), 1e-6, sec, 10000.0,
+                                      w.dtype)
+    P = w.persistent
+    eq = _ulp_check(harness.widen_host(harness.to_host(dq, w.dtype), w.dtype), q_ref, w.dtype, "q")
+    ek = _ulp_check(harness.widen_host(harness.to_host(kg, w.dtype), w.dtype)[P:], k_ref, w.dtype, "k")
+    assert (harness.to_host(vg, w.dtype)[P:] == qkv[:, 2]).all()
+    assert (harness.to_host(kg, w.dtype)[:P] == pk[0]).all()
+    say(f"[prep full] max |err| q {eq:.3g} k {ek:.3g}")
+    cache.close()
+
+
 def test_prep_stream_attention(sr):
     """Chunks appended with the fused call, then chunk attention of the prepared queries:
     the oracle runs the same pipeline (prep_qkv, its cache model, chunk_attention) in fp64."""
