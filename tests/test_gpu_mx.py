@@ -231,11 +231,13 @@ def test_mx_window_and_prefix(sr):
 
 def test_mx_degenerate_shapes(sr):
     """One-token chunks without persistent tokens and W = 0; a chunk of exactly one page at
-    head_dim 64; ragged pages with causal blocks of half a sub-tile."""
+    head_dim 64; ragged pages with causal blocks of half a sub-tile; a long prefix with few items
+    (4 items of 69 key tiles: the fan split runs each as 8 pieces)."""
     import torch
     rng = np.random.default_rng(23)
     mk = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
-    for H, D, P, n, W, cb in [(2, 128, 0, 1, 0, 1), (1, 64, 5, 128, 1, 128), (3, 128, 129, 257, 2, 32)]:
+    for H, D, P, n, W, cb in [(2, 128, 0, 1, 0, 1), (1, 64, 5, 128, 1, 128), (3, 128, 129, 257, 2, 32),
+                              (2, 128, 8000, 300, 1, 300)]:
         say(f"[mx degenerate] H={H} D={D} P={P} n={n} W={W} cb={cb}")
         pkb, pvb = mk(1, P, H, D), mk(1, P, H, D)
         cache = sr.KVCache(sr.config_for(H, D, P, n, W, cb, 1, sr.SR_MX),
