@@ -118,6 +118,7 @@ def load():
         "sr_ring_segments": [P, I32, ctypes.POINTER(sr_segment), I32, ctypes.POINTER(I32)],
         "sr_ring_destroy": [P],
         "sr_kvcache_set_window_layout": [P, ctypes.POINTER(sr_window_layout)],
+        "sr_window_layout_check": [cfgp, ctypes.POINTER(sr_window_layout)],
         "sr_kvcache_set_bank": [P, I32, P, P, P],
         "sr_kvcache_append_windows": [P, I64, P, P, P],
         "sr_windows_attention": [P, I32, P, P, P, F32, P],
@@ -227,6 +228,10 @@ def sr_kvcache_update_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
 
 def sr_kvcache_set_window_layout(h, layout):
     _check(load().sr_kvcache_set_window_layout(h, ctypes.byref(layout)))
+
+
+def sr_window_layout_check(cfg, layout):
+    _check(load().sr_window_layout_check(ctypes.byref(cfg), ctypes.byref(layout)))
 
 
 def sr_kvcache_set_bank(h, bank, k, v, stream=None):

@@ -330,14 +330,13 @@ sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void
                        "gather");
 }
 
-sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* layout) {
-  sr::clear_error();
-  if (!c || !layout) return sr::fail(SR_E_INVALID, "null cache or layout");
-  const sr::Layout& L = c->ring.L;
+}  // extern "C"
+
+namespace {
+
+// Validates a window layout against a cache geometry (host only) and fills the kernels' view.
+sr_status window_view(const sr::Layout& L, const sr_window_layout& w, sr::WinView* out) {
   if (L.dtype == SR_MX) return sr::fail(SR_E_UNSUPPORTED, "window layouts are available for SR_BF16 and SR_F32 caches");
-  if (c->windowed || c->ring.has_current || c->ring.hist_count > 0)
-    return sr::fail(SR_E_STATE, "the window layout is set once, before the first append");
-  const sr_window_layout& w = *layout;
   if (w.num_windows < 1 || w.num_windows > SR_MAX_LAYOUT_WINDOWS)
     return sr::fail(SR_E_INVALID, "num_windows %d outside [1, %d]", w.num_windows, SR_MAX_LAYOUT_WINDOWS);
   if (w.frames_per_chunk < 1 || w.window_pages < 1)
@@ -355,10 +354,40 @@ sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* la
     if (tok < 1 || int64_t(tok) * v.frames > int64_t(w.window_pages) * SR_PAGE_TOKENS)
       return sr::fail(SR_E_INVALID, "window %d: %d tokens x %d frames do not fit %d pages", i, tok, v.frames,
                       w.window_pages);
-    v.tok[i] = int16_t(tok);
+    // A window's keys of one chunk must fit the attention kernel's tile table on their own.
+    if (int64_t(tok) * v.frames > int64_t(SR_MAX_VISIBLE_PAGES) * SR_PAGE_TOKENS)
+      return sr::fail(SR_E_INVALID, "window %d: %d tokens x %d frames exceed the %d pages one call can visit", i, tok,
+                      v.frames, SR_MAX_VISIBLE_PAGES);
+    v.tok[i] = tok;
     v.row0[i + 1] = v.row0[i] + v.frames * tok;
     v.item0[i + 1] = v.item0[i] + L.H * ((v.frames * tok + sr::kQueryTile - 1) / sr::kQueryTile);
   }
+  *out = v;
+  return SR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sr_status sr_window_layout_check(const sr_kvcache_config* cfg, const sr_window_layout* layout) {
+  sr::clear_error();
+  if (!cfg || !layout) return sr::fail(SR_E_INVALID, "null config or layout");
+  sr::Layout L;
+  sr_status st = sr::make_layout(cfg, &L);
+  if (st != SR_OK) return st;
+  sr::WinView v;
+  return window_view(L, *layout, &v);
+}
+
+sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* layout) {
+  sr::clear_error();
+  if (!c || !layout) return sr::fail(SR_E_INVALID, "null cache or layout");
+  if (c->windowed || c->ring.has_current || c->ring.hist_count > 0)
+    return sr::fail(SR_E_STATE, "the window layout is set once, before the first append");
+  sr::WinView v;
+  const sr_status st = window_view(c->ring.L, *layout, &v);
+  if (st != SR_OK) return st;
   c->win = v;
   c->windowed = true;
   return SR_OK;

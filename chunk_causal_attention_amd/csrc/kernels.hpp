@@ -41,7 +41,7 @@ struct WinView {
   int32_t frames = 0;     // latent frames per chunk
   int32_t pages = 0;      // pages per window in a slot
   int32_t bank_segs = 0;  // leading segments of the table that are banks (not window-split)
-  int16_t tok[SR_MAX_LAYOUT_WINDOWS] = {};
+  int32_t tok[SR_MAX_LAYOUT_WINDOWS] = {};  // tokens per frame of each window
   int32_t row0[SR_MAX_LAYOUT_WINDOWS + 1] = {};
   int32_t item0[SR_MAX_LAYOUT_WINDOWS + 1] = {};
 };

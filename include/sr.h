@@ -297,11 +297,12 @@ sr_status sr_kvcache_set_workspace(sr_kvcache* c, void* ws, size_t ws_bytes, voi
  *
  * Iteration 2: the decoder takes chunks of two latent frames; each chunk's attention sees its
  * own latent frames and the cached K/V of the four before it (a window of W = 2 chunks), and
- * attention runs inside non-overlapping windows of 16 x 16 tokens.  Iteration 3, item 4: each
- * window is one short sequence (about 512 queries against 1,541 keys at 720p), padding left
- * out, empty slots hidden.  Iterations 4 and 6: four register tokens and one class token attend
- * to the whole frame, are rebuilt for every chunk and never cached; every window also attends
- * to them.
+ * attention runs inside non-overlapping windows of 16 x 16 tokens.  Iteration 3, item 4: a
+ * window's attention is an independent sequence of its own (at 720p: 512 query rows, 1,541
+ * keys) without padded rows, and ring slots that hold nothing yet are left out of its keys.
+ * Iterations 4 and 6: five global tokens (four register tokens, one class token) see the
+ * whole frame and are recomputed for each chunk instead of being cached; every window's rows
+ * see them as well.
  *
  * A cache with a window layout stores every chunk's frame tokens window by window: window w
  * owns window_pages pages of each ring slot, from page w * window_pages of the slot, and holds
@@ -325,8 +326,15 @@ typedef struct sr_window_layout {
 } sr_window_layout;
 
 /* Sets the window layout (host only).  Allowed once, before the first append; SR_E_STATE after
- * it, SR_E_INVALID for a layout that does not fit the slots. */
+ * it, otherwise the errors of sr_window_layout_check. */
 sr_status sr_kvcache_set_window_layout(sr_kvcache* c, const sr_window_layout* layout);
+
+/* Checks a window layout against a cache config without a cache (host only, no device work):
+ * SR_E_INVALID for a config or layout that does not fit (windows beyond a slot's pages, a
+ * window's frames_per_chunk * window_tokens[w] tokens beyond its window_pages pages or beyond
+ * the SR_MAX_VISIBLE_PAGES pages one attention call can visit), SR_E_UNSUPPORTED for an SR_MX
+ * cache. */
+sr_status sr_window_layout_check(const sr_kvcache_config* cfg, const sr_window_layout* layout);
 
 /* Rewrites the persistent tokens of `bank` in place: k, v device [P][H][D] (any cache; the
  * decoder's global tokens, rebuilt for every chunk).  SR_E_INVALID when P == 0.  The caller may

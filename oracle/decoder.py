@@ -7,8 +7,9 @@ What the step computes (project page, "3.2 Fast Causal H3 VAE"):
   * iteration 2 (space): attention runs inside non-overlapping windows of 16 x 16 tokens (every
     other layer shifts the windows by half a window), so a window's tokens attend to the same
     window's tokens only;
-  * iteration 3, item 4: each window is one short sequence (about 512 queries against 1,541 keys
-    at 720p), padding left out, cache slots that are still empty at stream start hidden;
+  * iteration 3, item 4: the attention of a window is computed as an independent sequence of
+    its own (at 720p: 512 query rows, 1,541 keys), with no padded rows and with ring slots that
+    hold nothing yet (the first chunks of a stream) left out of the key list;
   * iterations 4 and 6: four register tokens and one class token ("global tokens") attend to the
     whole frame, are rebuilt for every chunk and never cached; every window's attention also sees
     them (the 1,541 keys are 6 x 256 frame tokens + 5 global tokens).

@@ -2,8 +2,8 @@
 
 What the step does (project page, "3.2 Fast Causal H3 VAE", iteration 6: after the qkv
 projection, qk-norm, the rotary embedding and the K/V cache write run as one fused kernel;
-iteration 3, inference item 2: each new latent frame receives its rotary position once,
-when it is written into its ring slot; iteration 4: frame tokens take the absolute
+iteration 3, inference item 2: the rotary position of a latent frame is applied a single
+time, as the frame is written into its ring slot; iteration 4: frame tokens take the absolute
 latent-frame index of the stream, so that every attention score depends only on time
 differences).
 

@@ -55,6 +55,33 @@ def test_window_layout_struct(sr):
         sr.window_layout([1] * (sr.MAX_LAYOUT_WINDOWS + 1), 2, 1)
 
 
+def test_window_layout_check(sr):
+    """A layout is refused on the host when a window's tokens of one chunk do not fit its pages
+    or exceed the pages one attention call can visit, whatever fits the slot; token counts
+    above the int16 range are kept whole (no truncation to a negative count)."""
+    cap = 60 * 128  # the decoder's 720p slot: 15 windows x 4 pages
+    d1 = sr.config_for(16, 128, 5, cap, 2, cap, 1, sr.SR_BF16)
+    sr.sr_window_layout_check(d1, sr.window_layout([256] * 10 + [208] * 5, 2, 4))
+
+    def refused(cfg, lay, status=sr.SR_E_INVALID):
+        with pytest.raises(sr.SrError) as e:
+            sr.sr_window_layout_check(cfg, lay)
+        assert e.value.status == status
+
+    # 40,000 tokens x 4 frames in one window of 1250 pages fits the slot, but it is 1250 pages of
+    # keys of a single chunk: more than one call can visit (40,000 would also wrap an int16).
+    big = sr.config_for(1, 128, 0, 160000, 0, 160000, 1, sr.SR_BF16)
+    refused(big, sr.window_layout([40000], 4, 1250))
+    # above the int16 range but within the kernel's reach: accepted whole
+    ok = sr.config_for(1, 128, 0, 40064, 0, 40064, 1, sr.SR_BF16)
+    sr.sr_window_layout_check(ok, sr.window_layout([40000], 1, 313))
+    refused(d1, sr.window_layout([129], 1, 1))          # 129 tokens in one page
+    refused(d1, sr.window_layout([65], 2, 1))           # 2 frames x 65 tokens in one page
+    refused(d1, sr.window_layout([1] * 16, 2, 4))       # 64 pages of a 60-page slot
+    refused(sr.config_for(16, 128, 5, cap, 2, cap, 1, sr.SR_MX), sr.window_layout([256], 2, 4),
+            sr.SR_E_UNSUPPORTED)
+
+
 def test_status_strings(sr):
     assert sr.sr_status_string(0) == "SR_OK"
     assert sr.sr_status_string(2) == "SR_E_STATE"
