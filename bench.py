@@ -125,57 +125,77 @@ def append_bytes(w, mx=False):
     return es * w.heads * w.head_dim * 2 * (w.chunk + pages * 128)
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The fp64 oracle, as it stands, on whole heads of the workload's last chunk-step."""
-    import oracle
-    import synth
-    from threadpoolctl import threadpool_info
-    pk, pv, hist, cur = synth.single_step_inputs(w)
-    m = oracle.StreamingCache(pk, pv, w.window)
+def _native_cache(w, pk, pv, hist, cur, conv=None):
+    """The C++ oracle's cache holding the workload's last chunk-step (conv maps storage values)."""
+    from oracle import native
+    conv = conv or (lambda a: a)
+    m = native.StreamingCache(conv(pk), conv(pv), w.window)
     for i, (k, v) in enumerate(hist):
-        m.append(i, k, v)
-    m.append(len(hist), cur[0], cur[1])
+        m.append(i, conv(k), conv(v))
+    m.append(len(hist), conv(cur[0]), conv(cur[1]))
+    return m
+
+
+def _timed_heads(w, run, budget_s, group):
+    """Runs run(heads) on groups of heads until every head is done or budget_s has passed."""
+    done, t0 = 0, time.perf_counter()
+    while done < w.heads and time.perf_counter() - t0 < budget_s:
+        hs = list(range(done, min(w.heads, done + group)))
+        run(hs)
+        done += len(hs)
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The plain C++ fp64 oracle, as it stands, on whole heads of the workload's last chunk-step,
+    with every hardware thread (std::thread over head x 64-row blocks)."""
+    import synth
+    from oracle import native
+    pk, pv, hist, cur = synth.single_step_inputs(w)
+    m = _native_cache(w, pk, pv, hist, cur)
     scale = 1.0 / math.sqrt(w.head_dim)
-    heads, t0 = 0, time.perf_counter()
-    while heads < w.heads and time.perf_counter() - t0 < budget_s:
-        oracle.chunk_attention(m, 0, cur[2], scale, w.causal_block, w.dtype, heads=[heads])
-        heads += 1
-    dt = time.perf_counter() - t0
+    threads = native.load().orc_hardware_threads()
+    heads, dt = _timed_heads(w, lambda hs: native.chunk_attention(m, 0, cur[2], scale, w.causal_block, w.dtype,
+                                                                  heads=hs), budget_s, 4)
     flops = attention_flops(w) * heads / w.heads
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    model, _ = native.cpu_model()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{heads} of {w.heads} heads x all {w.chunk} query rows of {w.name} "
-                      f"({w.visible_keys} keys), fp64 numpy oracle, {dt:.1f} s wall"}
+                      f"({w.visible_keys} keys), C++ fp64 oracle on {threads} threads, {dt:.1f} s wall"}
 
 
-def cpu_baseline_mx(w, budget_s=10.0):
-    """The oracle on whole heads of the reduced-precision chunk-step: quantize that head's
-    queries, keys and values (oracle.mx) and run its attention over the dequantized values."""
+def cpu_baseline_mx(w, budget_s=20.0):
+    """The C++ oracle on whole heads of the reduced-precision chunk-step: the heads' queries, keys
+    and values quantized by oracle.mx (MXFP6 q/k, FP8 v; exact in fp32), then the fp64 attention
+    over the dequantized values.  The quantization is timed with the attention."""
     import oracle
     import synth
     from oracle import mx as omx
-    from threadpoolctl import threadpool_info
+    from oracle import native
     pk, pv, hist, cur = synth.single_step_inputs(w)
     wid = lambda a: oracle.widen(a, "bf16")
     scale = 1.0 / math.sqrt(w.head_dim)
-    heads, t0 = 0, time.perf_counter()
-    while heads < w.heads and time.perf_counter() - t0 < budget_s:
-        h = slice(heads, heads + 1)
+    threads = native.load().orc_hardware_threads()
+
+    def run(hs):
+        h = slice(hs[0], hs[-1] + 1)
         dk = lambda a: omx.mxfp6_values(wid(a[..., h, :])).astype(np.float32)
         dv = lambda a: omx.fp8_values(wid(a[..., h, :])).astype(np.float32)
-        m = oracle.StreamingCache(dk(pk), dv(pv), w.window)
+        m = native.StreamingCache(dk(pk), dv(pv), w.window)
         for i, (k, v) in enumerate(hist):
             m.append(i, dk(k), dv(v))
         m.append(len(hist), dk(cur[0]), dv(cur[1]))
-        oracle.chunk_attention(m, 0, dk(cur[2]), scale, w.causal_block, "f32")
-        heads += 1
-    dt = time.perf_counter() - t0
+        native.chunk_attention(m, 0, dk(cur[2]), scale, w.causal_block, "f32")
+
+    heads, dt = _timed_heads(w, run, budget_s, 4)
     flops = attention_flops(w) * heads / w.heads
-    threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    model, _ = native.cpu_model()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{heads} of {w.heads} heads x all {w.chunk} query rows of {w.name} ({w.visible_keys} keys): "
-                      f"MXFP6/FP8 quantization of that head's inputs + fp64 attention over the dequantized "
-                      f"values, numpy oracle, {dt:.1f} s wall"}
+                      f"MXFP6/FP8 quantization of those heads' inputs (numpy) + fp64 attention over the "
+                      f"dequantized values (C++ oracle, {threads} threads), {dt:.1f} s wall"}
 
 
 def make_inputs(sr, w, n_sets, torch):

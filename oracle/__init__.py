@@ -16,7 +16,11 @@ reaches the plain masked softmax-attention result exactly (the online softmax
 only reorders the rounding), so the oracle is that definition written out.
 
 Modules
-  attention      masked scaled-dot-product attention, the definition (fp64)
+  native         the plain C++17 fp64 oracle (cpp/attention_oracle.cpp): the definition, its own
+                 std::deque cache model and the dense full-sequence route, on std::thread
+                 workers; the reference of the GPU parity tests, the smoke check and the
+                 benchmark's CPU baseline (loaded on demand: `from oracle import native`)
+  attention      masked scaled-dot-product attention, the definition (fp64, numpy)
   cache_model    the streaming cache: persistent banks, rolling window, current chunk
   chunk_attention  one attention call of the current chunk over the cache model
   full_sequence  an independent dense path over the whole stream with an explicit mask
@@ -41,11 +45,11 @@ from .full_sequence import full_sequence_attention, window_full_attention
 from .window_attention import window_attention, prefix_attention
 from .qk_prep import rms_norm, rope, rope_angles, prep_qkv
 from .brute import brute_attention
-from .mx import mxfp6_values, fp8_values, mx_attention_values
+from .mx import mxfp6_values, fp8_values
 from .decoder import decoder_window_attention, decoder_global_attention, window_offsets
 
 __all__ = ["masked_attention", "widen", "StreamingCache", "CacheStateError", "chunk_attention",
            "current_block_mask", "full_sequence_attention", "window_full_attention", "window_attention",
            "prefix_attention", "rms_norm", "rope", "rope_angles", "prep_qkv", "brute_attention",
-           "mxfp6_values", "fp8_values", "mx_attention_values",
+           "mxfp6_values", "fp8_values",
            "decoder_window_attention", "decoder_global_attention", "window_offsets"]

@@ -127,9 +127,3 @@ def fp8_values(x):
     """x [...] -> the FP8 E4M3-dequantized values (fp64)."""
     return decode(encode(x, E4M3), E4M3)
 
-
-def mx_attention_values(q, k, v):
-    """The operands of the reduced-precision attention: MXFP6 queries and keys (blocks along
-    the last axis), FP8 values, as fp64.  The attention over them is the unchanged
-    definition (masked_attention) on the same visible sets."""
-    return mxfp6_values(q), mxfp6_values(k), fp8_values(v)

@@ -1,8 +1,11 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
 
-Element-by-element on reduced workloads that span several query and key tiles with ragged
-tails; on sampled rows (and all-finite checks) at the full workload sizes, with the same
-launch configuration the benchmark times.  Gates: tests/gates.py.
+The reference is the plain C++ fp64 oracle (oracle/native.py; cross-checked against the numpy
+oracle on the CPU).  Every element on reduced workloads that span several query and key tiles
+with ragged tails, and every element at the full workload sizes in the launch configuration
+the benchmark times (the split schedule; c1 and c4 also with whole items).  The 64-step c2
+session is checked whole on its first six and last two chunk-steps, on sampled rows in
+between, with a bit-exact gather of both banks after every step.  Gates: tests/gates.py.
 """
 import sys
 
@@ -11,8 +14,8 @@ import pytest
 
 import gates
 import harness
-import oracle
 import synth
+from oracle import native
 
 pytestmark = pytest.mark.gpu
 
@@ -29,16 +32,19 @@ def sr():
     return harness.lib_module()
 
 
-def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on_step=None, workspace="own"):
-    """Streams workload `w` through the library and the oracle model; returns per-step stats.
-    workspace "own": the split schedule (the default a KVCache runs); None: one workgroup per item."""
+def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on_step=None, workspace="own",
+               whole_steps=None):
+    """Streams workload `w` through the library and the oracle's cache model; returns per-step
+    stats (step index, output stats, lse stats).  workspace "own": the split schedule (the
+    default a KVCache runs); None: one workgroup per item.  rows: rows checked (None: all);
+    whole_steps: step indices checked on every row whatever `rows` says."""
     import torch
     scale = 1.0 / np.sqrt(w.head_dim)
     stream = synth.SessionStream(w)
     pk, pv = stream.persistent()
     cache = sr.KVCache(harness.cfg_of(sr, w), harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype),
                        workspace=workspace)
-    model = oracle.StreamingCache(pk, pv, w.window)
+    model = native.StreamingCache(pk, pv, w.window)
     stats = []
     for idx, ev in enumerate(stream):
         cid = ev["chunk"] + phase
@@ -63,8 +69,8 @@ def run_stream(sr, w, phase=0, rows=None, check_gather=False, oracle_every=1, on
             on_step(idx, ev, out_h, lse_h)
         if idx % oracle_every and not (w.single_step):
             continue
-        r = np.arange(w.chunk) if rows is None else rows
-        o_ref, l_ref = oracle.chunk_attention(model, ev["bank"], ev["q"], scale, w.causal_block, w.dtype, rows=r)
+        r = np.arange(w.chunk) if rows is None or (whole_steps and idx in whole_steps) else rows
+        o_ref, l_ref = native.chunk_attention(model, ev["bank"], ev["q"], scale, w.causal_block, w.dtype, rows=r)
         o_dev = harness.widen_host(out_h[r], w.dtype)
         st = gates.error_stats(o_dev, o_ref)
         st_l = gates.error_stats(lse_h[:, r], l_ref)
@@ -115,14 +121,45 @@ def test_ring_phase_bit_identical(sr, name):
 FULL = ["c1", "c3", "c4", "c1s", "c4s"]
 
 
-@pytest.mark.parametrize("name,schedule", [(n, "split") for n in FULL] + [("c1", "whole"), ("c4", "whole")])
-def test_parity_full_size_sampled(sr, name, schedule):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size_every_element(sr, name):
+    """One chunk-step at the workload's full size, every row of every head (O and LSE), in the
+    benchmark's launch configuration (split schedule) and, for c1 and c4, with whole items too.
+    The oracle's result is computed once and serves both schedules."""
+    import time
+    import torch
     w = synth.get_workload(name)
-    rows = harness.sample_rows(w.chunk, block=w.causal_block if w.causal_block < w.chunk else None)
-    say(f"[full] {name} ({schedule}): {len(rows)} sampled rows x {w.heads} heads, {w.visible_keys} keys")
-    stats = run_stream(sr, w, rows=rows, workspace=SCHEDULES[schedule])
-    check_stats(w, stats)
-    say(f"[full] {name}:", stats[-1][1], "lse", stats[-1][2]["max_abs"])
+    scale = 1.0 / np.sqrt(w.head_dim)
+    pk, pv, hist, cur = synth.single_step_inputs(w)
+    schedules = ["split", "whole"] if name in ("c1", "c4") else ["split"]
+    say(f"[full] {name}: {w.chunk} rows x {w.heads} heads over {w.visible_keys} keys, schedules {schedules}")
+    outs = {}
+    for sch in schedules:
+        cache = sr.KVCache(harness.cfg_of(sr, w), harness.to_dev(pk, w.dtype), harness.to_dev(pv, w.dtype),
+                           workspace=SCHEDULES[sch])
+        for i, (k, v) in enumerate(hist):
+            cache.append(i, harness.to_dev(k, w.dtype), harness.to_dev(v, w.dtype))
+        cache.append(len(hist), harness.to_dev(cur[0], w.dtype), harness.to_dev(cur[1], w.dtype))
+        lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device="cuda")
+        out = cache.attention(0, harness.to_dev(cur[2], w.dtype), lse=lse, softmax_scale=scale)
+        outs[sch] = (harness.widen_host(harness.to_host(out, w.dtype), w.dtype), lse.cpu().numpy())
+        cache.close()
+    model = native.StreamingCache(pk, pv, w.window)
+    for i, (k, v) in enumerate(hist):
+        model.append(i, k, v)
+    model.append(len(hist), cur[0], cur[1])
+    t0 = time.perf_counter()
+    o_ref, l_ref = native.chunk_attention(model, 0, cur[2], scale, w.causal_block, w.dtype)
+    say(f"[full] {name}: oracle {time.perf_counter() - t0:.1f} s")
+    g = gates.gates_for(w.dtype)
+    for sch, (o, l) in outs.items():
+        assert np.isfinite(o).all() and np.isfinite(l).all()
+        st, st_l = gates.error_stats(o, o_ref), gates.error_stats(l, l_ref)
+        say(f"[full] {name} ({sch}): max {st['max_abs']:.3g} mean {st['mean_abs']:.3g} rel {st['rel_fro']:.3g} "
+            f"lse max {st_l['max_abs']:.3g}")
+        assert gates.passes(st, g), (name, sch, st)
+        assert st_l["max_abs"] <= 2e-2, (name, sch, st_l)
 
 
 def test_one_gpu_share_of_sharded_run(sr):
@@ -169,12 +206,16 @@ def test_split_schedule_is_deterministic_and_leaves_counters_zero(sr):
         c.close()
 
 
-def test_session_c2_sampled(sr):
-    """32 chunks x 2 steps with per-step banks and evictions; sampled rows of every step."""
+@pytest.mark.timeout(900)
+def test_session_c2(sr):
+    """32 chunks x 2 steps with per-step banks and evictions: every element of the first six
+    chunk-steps (the window filling, the first eviction) and of the last two, sampled rows of
+    the others, and after every step a bit-exact gather of both banks' logical sequences."""
     w = synth.get_workload("c2")
     rows = harness.sample_rows(w.chunk, stride=211)
-    say(f"[c2] 64 chunk-steps, {len(rows)} rows each")
-    stats = run_stream(sr, w, rows=rows, check_gather=False)
+    whole = {0, 1, 2, 3, 4, 5, 62, 63}
+    say(f"[c2] 64 chunk-steps: whole outputs at {sorted(whole)}, {len(rows)} rows at the others, gather every step")
+    stats = run_stream(sr, w, rows=rows, check_gather=True, whole_steps=whole)
     assert len(stats) == 64
     check_stats(w, stats)
     errs = [s[1]["rel_fro"] for s in stats]
@@ -291,7 +332,7 @@ def _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, seed, chunks, workspace, r
     pk_t, pk = draw(1, P, H, D)
     pv_t, pv = draw(1, P, H, D)
     cache = sr.KVCache(cfg, pk_t.cuda() if P else None, pv_t.cuda() if P else None, workspace=workspace)
-    model = oracle.StreamingCache(pk, pv, W)
+    model = native.StreamingCache(pk, pv, W)
     for cid, n in enumerate(chunks):
         if W > 0 and cid >= W + 1:
             assert cache.evict() == model.evict()
@@ -303,7 +344,7 @@ def _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, seed, chunks, workspace, r
     lse = torch.empty((H, chunks[-1]), dtype=torch.float32, device="cuda")
     out = cache.attention(0, q_t.cuda(), lse=lse, softmax_scale=scale)
     r = np.arange(chunks[-1]) if rows is None else rows
-    o_ref, l_ref = oracle.chunk_attention(model, 0, q, scale, cb, dtype, rows=r)
+    o_ref, l_ref = native.chunk_attention(model, 0, q, scale, cb, dtype, rows=r)
     st = gates.error_stats(harness.widen_host(harness.to_host(out, dtype)[r], dtype), o_ref)
     assert gates.passes(st, gates.gates_for(dtype)), st
     assert np.abs(lse.cpu().numpy()[:, r] - l_ref).max() <= (2e-2 if dtype == "bf16" else 1e-4)
