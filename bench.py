@@ -727,6 +727,93 @@ def run_decoder(args, w):
     return res
 
 
+def time_chunk_steps(sr, torch, w, mx, n_layers, steps, warmup, no_split):
+    """Cold chunk-steps of workload w: n_layers independent layer caches (each larger than the
+    last-level cache for the full-size workloads) visited in turn, every step evict + append +
+    chunk attention, HIP events on the launch stream around the append and the attention."""
+    dev = torch.device("cuda:0")
+    pk, pv, sets = make_inputs(sr, w, w.window + 2, torch)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
+                        sr.SR_MX if mx else (sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32))
+    t_init = time.perf_counter()
+    layers = []
+    # One attention workspace serves every layer cache: their calls are ordered on one stream.
+    ws = None if no_split else sr.workspace_for(cfg)
+    for _ in range(n_layers):
+        c = sr.KVCache(cfg, pk, pv, workspace=ws)
+        for j in range(w.window + 1):
+            k, v, _ = sets[j % len(sets)]
+            c.append(j, k, v)
+        layers.append({"cache": c, "next": w.window + 1})
+    torch.cuda.synchronize()
+    t_init = time.perf_counter() - t_init
+    out = torch.empty((w.chunk, w.heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
+    lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device=dev)
+    ev_pairs = []
+
+    def step(i, timed):
+        L = layers[i % len(layers)]
+        c = L["cache"]
+        cid = L["next"]
+        L["next"] += 1
+        if w.window > 0:
+            c.evict()
+        k, v, q = sets[cid % len(sets)]
+        if timed:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            c.append(cid, k, v)
+            e1.record()
+            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+            e2.record()
+            ev_pairs.append((e0, e1, e2))
+        else:
+            c.append(cid, k, v)
+            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    res = {"elapsed": elapsed, "init_s": t_init,
+           "append_ms": np.array([a.elapsed_time(b) for a, b, _ in ev_pairs]),
+           "attention_ms": np.array([b.elapsed_time(c) for _, b, c in ev_pairs])}
+    for L in layers:
+        L["cache"].close()
+    del layers, out, lse, sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def mfma_probe(sr, torch, dev, iters=8000, reps=5):
+    """The dense bf16 MFMA rate the device sustains (sr_probe_mfma_bf16: two workgroups of eight
+    waves per compute unit, four independent MFMA chains per wave, register operands), best of
+    `reps` launches, and the shader clock it implies at 4096 flop per clock and compute unit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 2 * cus
+    out = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    flops = wgs * 8 * 4 * 32768.0 * iters
+    sr.sr_probe_mfma_bf16(out, wgs, 100)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sr.sr_probe_mfma_bf16(out, wgs, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None or ms < best else best
+    tf = flops / (best * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4),
+            "clock_mhz_implied": round(tf * 1e12 / (cus * 4096.0) / 1e6, 0), "ms": round(best, 4),
+            "method": f"{wgs} workgroups x 8 waves x 4 MFMA chains x {iters} v_mfma_f32_32x32x16_bf16, best of {reps}"}
+
+
 def run(args):
     import torch
     import synth
@@ -751,58 +838,8 @@ def run(args):
         raise SystemExit(f"workload {w.name} is a parity case, not a bench workload")
     torch.cuda.init()
     dev = torch.device("cuda:0")
-    pk, pv, sets = make_inputs(sr, w, w.window + 2, torch)
-    scale = 1.0 / math.sqrt(w.head_dim)
-    cfg = sr.config_for(w.heads, w.head_dim, w.persistent, w.chunk, w.window, w.causal_block, w.banks,
-                        sr.SR_MX if mx else (sr.SR_BF16 if w.dtype == "bf16" else sr.SR_F32))
-
-    t_init = time.perf_counter()
-    layers = []
-    # One attention workspace serves every layer cache: their calls are ordered on one stream.
-    ws = None if args.no_split else sr.workspace_for(cfg)
-    for _ in range(args.layers):
-        c = sr.KVCache(cfg, pk, pv, workspace=ws)
-        for j in range(w.window + 1):
-            k, v, _ = sets[j % len(sets)]
-            c.append(j, k, v)
-        layers.append({"cache": c, "next": w.window + 1})
-    torch.cuda.synchronize()
-    t_init = time.perf_counter() - t_init
-    out = torch.empty((w.chunk, w.heads, w.head_dim), dtype=sets[0][0].dtype, device=dev)
-    lse = torch.empty((w.heads, w.chunk), dtype=torch.float32, device=dev)
-
-    ev_pairs = []
-
-    def step(i, timed):
-        L = layers[i % len(layers)]
-        c = L["cache"]
-        cid = L["next"]
-        L["next"] += 1
-        if w.window > 0:
-            c.evict()
-        k, v, q = sets[cid % len(sets)]
-        if timed:
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record()
-            c.append(cid, k, v)
-            e1.record()
-            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
-            e2.record()
-            ev_pairs.append((e0, e1, e2))
-        else:
-            c.append(cid, k, v)
-            c.attention(cid % w.banks, q, out=out, lse=lse, softmax_scale=scale)
-
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    t_append = np.array([a.elapsed_time(b) for a, b, _ in ev_pairs])
-    t_attn = np.array([b.elapsed_time(c) for _, b, c in ev_pairs])
+    t = time_chunk_steps(sr, torch, w, mx, args.layers, args.steps, args.warmup, args.no_split)
+    elapsed, t_append, t_attn, t_init = t["elapsed"], t["append_ms"], t["attention_ms"], t["init_s"]
     ms_step = elapsed * 1e3 / args.steps
     F = attention_flops(w)
     peak = PEAK_MX_TFLOPS if mx else (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS)
@@ -849,8 +886,23 @@ def run(args):
         "attention_gflop_per_call": round(F / 1e9, 3),
         "session_init_ms_per_layer": round(t_init * 1e3 / args.layers, 3),
     }
-    for L in layers:
-        L["cache"].close()
+    if name == "c1" and args.heads is None and not args.no_split and args.extra_c3:
+        # the second configuration of the target, timed the same way (cold, split schedule)
+        w3 = synth.get_workload("c3")
+        t3 = time_chunk_steps(sr, torch, w3, False, args.layers, max(10, args.steps // 2), args.warmup, False)
+        a3 = t3["attention_ms"]
+        tf3 = attention_flops(w3) / (a3.mean() * 1e-3) / 1e12
+        res["c3_ms_attention"] = round(float(a3.mean()), 4)
+        res["c3_ms_attention_p10_p50_p90"] = [round(float(np.percentile(a3, p)), 4) for p in (10, 50, 90)]
+        res["c3_attention_tflops"] = round(tf3, 3)
+        res["c3_frac"] = round(tf3 / PEAK_BF16_TFLOPS, 4)
+        res["c3_steps"] = len(a3)
+    if args.probe and not mx and w.dtype == "bf16":
+        probe = mfma_probe(sr, torch, dev)
+        probe["attention_frac_of_probe"] = round(attn_tflops / probe["tflops"], 4)
+        if "c3_attention_tflops" in res:
+            probe["c3_frac_of_probe"] = round(res["c3_attention_tflops"] / probe["tflops"], 4)
+        res["mfma_probe"] = probe
     if args.copy_calibration:
         copy_calibration(res, torch, dev)
     if args.cpu_baseline:
@@ -876,7 +928,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-split", action="store_true",
                     help="run attention without a workspace (one workgroup per head and query tile)")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (whole heads)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work (whole heads)")
+    ap.add_argument("--no-extra-c3", dest="extra_c3", action="store_false",
+                    help="c1: do not also time the 720p workload c3's attention (reported as c3_* keys)")
+    ap.add_argument("--no-probe", dest="probe", action="store_false",
+                    help="do not run the dense bf16 MFMA probe (reported as mfma_probe)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference for the profiler's byte counters)")
     ap.add_argument("--traffic-kib", type=float, default=None,

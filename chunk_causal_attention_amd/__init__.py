@@ -123,6 +123,7 @@ def load():
         "sr_kvcache_append_windows": [P, I64, P, P, P],
         "sr_windows_attention": [P, I32, P, P, P, F32, P],
         "sr_global_attention": [P, I32, P, I32, P, P, F32, P],
+        "sr_probe_mfma_bf16": [P, I32, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -228,6 +229,13 @@ def sr_kvcache_update_chunk(h, chunk_id, k, v, n_tokens=None, stream=None):
 
 def sr_kvcache_set_window_layout(h, layout):
     _check(load().sr_kvcache_set_window_layout(h, ctypes.byref(layout)))
+
+
+def sr_probe_mfma_bf16(out, workgroups, iters, stream=None):
+    """Dense bf16 MFMA probe: out a device float tensor of >= workgroups * 512 elements."""
+    if out.numel() < workgroups * 512:
+        raise ValueError("out holds fewer than workgroups * 512 floats")
+    _check(load().sr_probe_mfma_bf16(_ptr(out), workgroups, iters, _stream(stream)))
 
 
 def sr_window_layout_check(cfg, layout):

@@ -44,8 +44,9 @@
 // Softmax in the exp2 domain with a lazily updated running max: O and l are rescaled only
 // when some row's max grows by more than 2^8, otherwise the stale max is kept (exact in real
 // arithmetic; probabilities stay below 2^8, far from fp32/bf16 overflow).  The row sums are
-// taken from the bf16-rounded probabilities that the P.V instruction multiplies, with
-// v_dot2_f32_bf16 against (1, 1).
+// plain fp32 adds of the probabilities before their bf16 rounding (two chains per lane): a
+// dot-product instruction on the rounded pairs stalls the matrix unit when it sits between
+// MFMAs (measured), and the rounding of P is then one relative 2^-9 error per weight either way.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -477,6 +478,7 @@ __device__ __forceinline__ void block_a(RowState<G>& st, Scores<G>& sc, Probs<G>
     for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(vpage, vsub, r, c, hl);
   }
   float mx = -INFINITY, mneg = 0.0f;
+  float lpart[2] = {0.0f, 0.0f};  // row sums of the fp32 probabilities, two chains
   fence();
 #pragma unroll
   for (int r = 0; r < NP; ++r) {
@@ -505,17 +507,17 @@ __device__ __forceinline__ void block_a(RowState<G>& st, Scores<G>& sc, Probs<G>
         for (int e = (r - H1) * EPR; e < (r - H1 + 1) * EPR && e < kEarlyProbs; ++e) {
           sc[e / 16][0][e % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][0][e % 16], sl2, mneg));
           pin(sc[e / 16][0][e % 16]);
+          lpart[e & 1] += sc[e / 16][0][e % 16];
           if ((e & 7) == 7) {
             pop[e / 16][0][(e % 16) / 8] = M::pack(sc[e / 16][0], (e % 16) / 8);
-            lsum = M::row_sum(pop[e / 16][0][(e % 16) / 8], lsum);
             pin(pop[e / 16][0][(e % 16) / 8]);
-            pin(lsum);
           }
         }
       }
     }
     fence();
   }
+  lsum = lpart[0] + lpart[1];
 }
 
 // Block B: S^T = K Q^T of sub-tile i+1 alongside the probabilities of sub-tile i that block A
@@ -535,7 +537,7 @@ __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>
 #pragma unroll
   for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
   const float mneg = -st.m[0];
-  float lsum = 0.0f;
+  float lpart[2] = {0.0f, 0.0f};  // row sums of the fp32 probabilities, two chains
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
     const int ks = r / G::NKB, kb = r % G::NKB;
@@ -549,16 +551,15 @@ __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>
       const int ekb = e / 16, ei = e % 16;
       sc[ekb][0][ei] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ekb][0][ei], sl2, mneg));
       pin(sc[ekb][0][ei]);
-      if ((e & 7) == 7) {  // a group of 8 probabilities is complete: round and sum them
+      lpart[e & 1] += sc[ekb][0][ei];
+      if ((e & 7) == 7) {  // a group of 8 probabilities is complete: round them for the P.V product
         pop[ekb][0][ei / 8] = M::pack(sc[ekb][0], ei / 8);
-        lsum = M::row_sum(pop[ekb][0][ei / 8], lsum);
         pin(pop[ekb][0][ei / 8]);
-        pin(lsum);
       }
     }
     fence();
   }
-  st.l[0] += lsum;
+  st.l[0] += lpart[0] + lpart[1];
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {

@@ -473,6 +473,14 @@ sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_
                        "global attention");
 }
 
+sr_status sr_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, void* stream) {
+  sr::clear_error();
+  if (!out) return sr::fail(SR_E_INVALID, "null output");
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return sr::fail(SR_E_INVALID, "workgroups %d or iters %d out of range", workgroups, iters);
+  return device_status(sr::launch_mfma_probe(out, workgroups, iters, static_cast<hipStream_t>(stream)), "mfma probe");
+}
+
 const sr_ring* sr_kvcache_ring(const sr_kvcache* c) { return c ? &c->ring : nullptr; }
 
 sr_status sr_kvcache_destroy(sr_kvcache* c) {

@@ -249,4 +249,10 @@ bool few_attention_fits(const Layout& L, const SegTable& t, int32_t n_q, const S
 hipError_t launch_few_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, const void* q,
                                 void* o, float* lse, float softmax_scale, const SplitWorkspace& ws, hipStream_t st);
 
+// Dense bf16 MFMA probe (probe.hip): `workgroups` workgroups of kProbeThreads threads, each
+// running 4 chains of `iters` 32x32x16 MFMAs; writes one float per thread to out.
+constexpr int32_t kProbeThreads = 512;
+constexpr int32_t kProbeChains = 4;
+hipError_t launch_mfma_probe(float* out, int32_t workgroups, int32_t iters, hipStream_t st);
+
 }  // namespace sr

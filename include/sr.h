@@ -374,6 +374,15 @@ sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_
 sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void* v_out,
                             int32_t max_tokens, int32_t* n_tokens, void* stream);
 
+/* Measurement aid (not part of the attention path): the dense bf16 MFMA rate of the device.
+ * Launches `workgroups` workgroups of 512 threads; every wave runs 4 independent chains of
+ * `iters` v_mfma_f32_32x32x16_bf16 instructions on register operands, 4 * 32768 * iters flops
+ * per wave, and each thread writes one float to out (device, >= workgroups * 512 floats, owned by
+ * the caller).  Two workgroups per compute unit keep every SIMD busy; the flops over the launch's
+ * duration are the sustained peak at the running clock.  SR_E_INVALID for a null out,
+ * workgroups outside [1, 2^20] or iters outside [1, 2^24]; SR_E_DEVICE for a launch failure. */
+sr_status sr_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, void* stream);
+
 /* The handle's ring state, for inspection (owned by the cache). */
 const sr_ring* sr_kvcache_ring(const sr_kvcache* c);
 
