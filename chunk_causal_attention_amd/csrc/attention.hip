@@ -19,13 +19,13 @@
 //
 // Schedule.  Iteration i of the key loop works on 64-key sub-tiles of the cache pages:
 //   [mask sub-tile i if partial]
-//   { O^T += V^T P^T for sub-tile i-1  ||  row max of sub-tile i }
-//   [rescale O and l if some row max grew by more than 2^8]
-//   { S^T = K Q^T for sub-tile i+1     ||  exp2, rounding and row sums of sub-tile i }
-// Each {..} block mixes MFMAs, their LDS operand reads and vector-ALU work, and is
-// scheduled to keep several LDS reads in flight and to slot the vector work between the
-// MFMAs; two waves per SIMD run the same stream.  A sub-tile past every query's visible
-// keys is simply fully masked (its probabilities are zero), so the loop has no other
+//   { O^T += V^T P^T for sub-tile i-1  ||  exp2, rounding and row sums of half of sub-tile i }
+//   { S^T = K Q^T for sub-tile i+1     ||  the other half }
+//   [rare: sub-tile i's row max, rescale of O and l, its probabilities again]
+// Each {..} block mixes MFMAs, their LDS operand reads and vector-ALU work (one probability
+// per MFMA), and is scheduled to keep several LDS reads in flight and to slot the vector work
+// between the MFMAs; two waves per SIMD run the same stream.  A sub-tile past every query's
+// visible keys is simply fully masked (its probabilities are zero), so the loop has no other
 // branches.  The loop runs one page (two iterations) per trip, the two sub-tiles' score
 // registers alternating; a closing step adds the last sub-tile's P.V.  K and V pages have
 // separate double buffers in LDS; the pages of tile t+2 (K) and t+1 (V) are requested at
@@ -41,12 +41,16 @@
 // registers of a lane come out exactly in the operand order the P.V instruction expects,
 // and V transposed, so its operand is one contiguous LDS read per lane.
 //
-// Softmax in the exp2 domain with a lazily updated running max: O and l are rescaled only
-// when some row's max grows by more than 2^8, otherwise the stale max is kept (exact in real
-// arithmetic; probabilities stay below 2^8, far from fp32/bf16 overflow).  The row sums are
-// plain fp32 adds of the probabilities before their bf16 rounding (two chains per lane): a
-// dot-product instruction on the rounded pairs stalls the matrix unit when it sits between
-// MFMAs (measured), and the rounding of P is then one relative 2^-9 error per weight either way.
+// Softmax in the exp2 domain with a lazily updated running max (exact in real arithmetic): a
+// sub-tile's probabilities are taken against the running max as it stands, and the sub-tile's
+// own row max is computed only when some lane's sum of its 32 probabilities exceeds 2^12 (a
+// probability may be that large or have overflowed); then the running max moves, O and l are
+// rescaled and the probabilities are taken again.  So every probability that reaches the P.V
+// product is at most 2^12, far from fp32/bf16 overflow, and the row max costs nothing on the
+// common path.  The row sums are plain fp32 adds of the probabilities before their bf16
+// rounding (two chains per lane): a dot-product instruction on the rounded pairs stalls the
+// matrix unit when it sits between MFMAs (measured), and the rounding of P is one relative
+// 2^-9 error per weight either way.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -68,7 +72,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));  // operand of the scal
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kRescaleThreshold = 8.0f;  // log2 units (generic path: fp32, head_dim 64 with QB > 1)
 constexpr float kMaxInit = -1.0e30f;       // finite: keeps exp2(x - max) defined on masked rows
 constexpr int kMaxTiles = SR_MAX_VISIBLE_PAGES;  // tile-table capacity (pages of visible keys)
 
@@ -447,38 +451,55 @@ __device__ __forceinline__ typename G::Op qk_operand(const char* kpage, int sub,
   return G::M::load(kpage + k_addr<G>(sub * G::SUB + kb * 32 + c, ks * 16 + hl * 8));
 }
 
-// Probabilities of sub-tile i computed in block A (one operand group of 8); block B computes
-// the others.
-constexpr int kEarlyProbs = 8;
+// Probabilities of a sub-tile are computed against the running max as it stands, without the
+// sub-tile's own row max: a lane's 32 probabilities and their sum are taken first, and only if
+// that sum exceeds 2^kSumLimit in some lane (some probability may be that large, or have
+// overflowed) does the wave take the slow path (rescale_and_redo): the sub-tile's row max,
+// the rescale of O and l to the new running max, and the probabilities again.  Every
+// probability of the fast path is at most 2^kSumLimit, far from fp32/bf16 overflow.  The
+// running max starts at kMaxInit, so a piece's first sub-tile always takes the slow path.
+constexpr float kSumLimit = 4096.0f;  // 2^12
 
-// Block A: O^T += V^T P^T of sub-tile i-1, with, in the shadow of its MFMAs, the row max of
-// sub-tile i and the lazy-rescale decision (first half of the regions) and the first
-// kEarlyProbs probabilities of sub-tile i with their row sum (second half), so that the
-// vector work is spread over both blocks.  Outputs: `grow` (uniform) tells whether the
-// running max moves to `mnew`; the caller rescales the accumulators after the block, once
-// its MFMAs are issued.  The probabilities here already use the new max.
-// LOADED: the ring already holds the first AH V operands (read during the previous block B);
-// else they are read here.  SOFTMAX: false for the closing step (no sub-tile i).  With
-// SOFTMAX, the last AH regions also read the first AH score operands of sub-tile i+1
-// (block B) into the ring.
+// Probability e of sub-tile `sc` (score register e % 16 of key block e / 16): exp2(s * sl2 - m)
+// into grp[e % 8] and the row sum (two chains, by parity of e); a complete group of 8 is
+// rounded to bf16 into its P.V operand.  The raw score stays in sc for the slow path.
+template <class G>
+__device__ __forceinline__ void prob(const Scores<G>& sc, Probs<G>& pop, float (&grp)[8], float (&lpart)[2], int e,
+                                     float sl2, float mneg) {
+  using M = typename G::M;
+  const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][0][e % 16], sl2, mneg));
+  grp[e % 8] = p;
+  pin(grp[e % 8]);
+  lpart[e & 1] += p;
+  if ((e & 7) == 7) {
+    f32x16_t t{};
+#pragma unroll
+    for (int x = 0; x < 8; ++x) t[8 * ((e % 16) / 8) + x] = grp[x];
+    pop[e / 16][0][(e % 16) / 8] = M::pack(t, (e % 16) / 8);
+    pin(pop[e / 16][0][(e % 16) / 8]);
+  }
+}
+
+// Block A: O^T += V^T P^T of sub-tile i-1, with the first half of sub-tile i's probabilities
+// (one per MFMA) in the shadow of its MFMAs.  LOADED: the ring already holds the first AH V
+// operands (read during the previous block B); else they are read here.  SOFTMAX: false for
+// the closing step (no sub-tile i).  With SOFTMAX, the last AH regions also read the first AH
+// score operands of sub-tile i+1 (block B) into the ring.
 template <class G, bool LOADED, bool SOFTMAX>
-__device__ __forceinline__ void block_a(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, float& lsum, bool& grow,
-                                        float& mnew, float sl2, const char* vpage, int vsub, const char* kpage,
+__device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, Probs<G>& pop, float (&lpart)[2],
+                                        float sl2, float mneg, const char* vpage, int vsub, const char* kpage,
                                         int ksub, typename G::Op (&ring)[AH], int c, int hl) {
   using M = typename G::M;
   constexpr int NP = G::NDB * G::NKB * G::PSTEPS;
+  constexpr int NE = 16 * G::NKB;  // probabilities per lane
   static_assert(NP % AH == 0, "ring slots must line up across blocks");
-  constexpr int H1 = NP / 2;                        // regions of the row max
-  constexpr int NE = 16 * G::NKB;                   // scores per lane
-  constexpr int MPR = NE / H1;                      // scores per region of the max
-  constexpr int EPR = (kEarlyProbs + (NP - H1) - 1) / (NP - H1);
-  static_assert(MPR % 2 == 0 && kEarlyProbs % 8 == 0, "max pairs, whole operand groups");
+  static_assert(NE % 2 == 0 && (NE / 2) % 8 == 0, "whole operand groups per block");
+  constexpr int EA = NE / 2;  // probabilities computed here
   if constexpr (!LOADED) {
 #pragma unroll
     for (int r = 0; r < AH; ++r) ring[r] = pv_operand<G>(vpage, vsub, r, c, hl);
   }
-  float mx = -INFINITY, mneg = 0.0f;
-  float lpart[2] = {0.0f, 0.0f};  // row sums of the fp32 probabilities, two chains
+  float grp[8];
   fence();
 #pragma unroll
   for (int r = 0; r < NP; ++r) {
@@ -489,55 +510,29 @@ __device__ __forceinline__ void block_a(RowState<G>& st, Scores<G>& sc, Probs<G>
     else if (SOFTMAX)
       ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH - NP, c, hl);
     if constexpr (SOFTMAX) {
-      if (r < H1) {
 #pragma unroll
-        for (int e = r * MPR; e < (r + 1) * MPR; e += 2) {
-          mx = fmaxf(mx, fmaxf(sc[e / 16][0][e % 16], sc[(e + 1) / 16][0][(e + 1) % 16]));
-          pin(mx);
-        }
-      }
-      if (r == H1 - 1) {
-        const float m_old = st.m[0];
-        mnew = fmaxf(m_old, pair_max(mx) * sl2);
-        grow = __any(mnew > m_old + kRescaleThreshold);
-        mneg = -(grow ? mnew : m_old);
-      }
-      if (r >= H1) {
-#pragma unroll
-        for (int e = (r - H1) * EPR; e < (r - H1 + 1) * EPR && e < kEarlyProbs; ++e) {
-          sc[e / 16][0][e % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / 16][0][e % 16], sl2, mneg));
-          pin(sc[e / 16][0][e % 16]);
-          lpart[e & 1] += sc[e / 16][0][e % 16];
-          if ((e & 7) == 7) {
-            pop[e / 16][0][(e % 16) / 8] = M::pack(sc[e / 16][0], (e % 16) / 8);
-            pin(pop[e / 16][0][(e % 16) / 8]);
-          }
-        }
-      }
+      for (int e = r * EA / NP; e < (r + 1) * EA / NP; ++e) prob<G>(sc, pop, grp, lpart, e, sl2, mneg);
     }
     fence();
   }
-  lsum = lpart[0] + lpart[1];
 }
 
-// Block B: S^T = K Q^T of sub-tile i+1 alongside the probabilities of sub-tile i that block A
-// left (from kEarlyProbs on), spread evenly over the regions.  The ring holds the first AH
-// score operands on entry.  NEXT_V: the last AH regions read the first AH
-// V operands of the next block A (half `vsub_next` of the V page at `vnext`) into the ring.
+// Block B: S^T = K Q^T of sub-tile i+1 alongside the second half of sub-tile i's
+// probabilities.  The ring holds the first AH score operands on entry.  NEXT_V: the last AH
+// regions read the first AH V operands of the next block A (half `vsub_next` of the V page at
+// `vnext`) into the ring.
 template <class G, bool NEXT_V>
-__device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>& pop, Scores<G>& sn,
+__device__ __forceinline__ void block_b(const Scores<G>& sc, Probs<G>& pop, float (&lpart)[2], Scores<G>& sn,
                                         const typename G::Op (&qop)[1][G::KSTEPS], const char* kpage, int ksub,
                                         const char* vnext, int vsub_next, typename G::Op (&ring)[AH], float sl2,
-                                        int c, int hl) {
+                                        float mneg, int c, int hl) {
   using M = typename G::M;
   constexpr int NS = G::KSTEPS * G::NKB;
   static_assert(NS % AH == 0, "ring slots must line up across blocks");
-  constexpr int NE = 16 * G::NKB;  // probabilities per lane
-  constexpr int NB = NE - kEarlyProbs;
+  constexpr int NE = 16 * G::NKB, EA = NE / 2, NB = NE - EA;
 #pragma unroll
   for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
-  const float mneg = -st.m[0];
-  float lpart[2] = {0.0f, 0.0f};  // row sums of the fp32 probabilities, two chains
+  float grp[8];
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
     const int ks = r / G::NKB, kb = r % G::NKB;
@@ -547,19 +542,30 @@ __device__ __forceinline__ void block_b(RowState<G>& st, Scores<G>& sc, Probs<G>
     else if (NEXT_V)
       ring[r % AH] = pv_operand<G>(vnext, vsub_next, r + AH - NS, c, hl);
 #pragma unroll
-    for (int e = kEarlyProbs + r * NB / NS; e < kEarlyProbs + (r + 1) * NB / NS; ++e) {
-      const int ekb = e / 16, ei = e % 16;
-      sc[ekb][0][ei] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ekb][0][ei], sl2, mneg));
-      pin(sc[ekb][0][ei]);
-      lpart[e & 1] += sc[ekb][0][ei];
-      if ((e & 7) == 7) {  // a group of 8 probabilities is complete: round them for the P.V product
-        pop[ekb][0][ei / 8] = M::pack(sc[ekb][0], ei / 8);
-        pin(pop[ekb][0][ei / 8]);
-      }
-    }
+    for (int e = EA + r * NB / NS; e < EA + (r + 1) * NB / NS; ++e) prob<G>(sc, pop, grp, lpart, e, sl2, mneg);
     fence();
   }
-  st.l[0] += lpart[0] + lpart[1];
+}
+
+// The slow path of a sub-tile whose probabilities may exceed 2^kSumLimit: its row max moves the
+// running max (where it is larger), O and l are rescaled to the new max, and the sub-tile's
+// probabilities and row sum are computed again.  Exact in real arithmetic, like the fast path.
+template <class G>
+__device__ __forceinline__ float rescale_and_redo(RowState<G>& st, const Scores<G>& sc, Probs<G>& pop, float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16 * G::NKB; ++e) mx = fmaxf(mx, sc[e / 16][0][e % 16]);
+  const float m_old = st.m[0];
+  const float mnew = fmaxf(m_old, pair_max(mx) * sl2);
+  const float alpha = __builtin_amdgcn_exp2f(m_old - mnew);
+  st.l[0] *= alpha;
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) st.acc[0][db] *= alpha;
+  st.m[0] = mnew;
+  float grp[8], lpart[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int e = 0; e < 16 * G::NKB; ++e) prob<G>(sc, pop, grp, lpart, e, sl2, -mnew);
+  return lpart[0] + lpart[1];
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
@@ -706,22 +712,18 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
   const char* kpage = smem + (((i + 1) >> 1) & 1) * G::KPAGE;             // sub-tile i+1
   float rmax[G::QB];
   if constexpr (G::ES == 2 && G::QB == 1) {
-    float lsum = 0.0f, mnew = 0.0f;
-    bool grow = false;
-    block_a<G, !ODD, !CLOSING>(st, sc, pop, lsum, grow, mnew, sl2, vpage, NEXT, kpage, NEXT, ring, c, hl);
+    float lpart[2] = {0.0f, 0.0f};
+    const float mneg = -st.m[0];
+    block_a<G, !ODD, !CLOSING>(st, sc, pop, lpart, sl2, mneg, vpage, NEXT, kpage, NEXT, ring, c, hl);
     if (CLOSING) return;  // nothing follows the last sub-tile's P.V
-    if (grow) {  // lazy rescale: the running max grew by more than 2^8 in some row
-      const float alpha = __builtin_amdgcn_exp2f(st.m[0] - mnew);
-      st.l[0] *= alpha;
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) st.acc[0][db] *= alpha;
-      st.m[0] = mnew;
-    }
-    st.l[0] += lsum;
     mid();
     // Odd i: the next iteration's P.V reads sub-tile i, the second half of V page i / 2.
     const char* vnext = smem + G::VBASE + ((i >> 1) & 1) * G::VPAGE;
-    block_b<G, ODD == 1>(st, sc, pop, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, c, hl);
+    block_b<G, ODD == 1>(sc, pop, lpart, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, mneg, c, hl);
+    float lsum = lpart[0] + lpart[1];
+    // Some probability of the sub-tile may exceed 2^kSumLimit: take its row max (rare).
+    if (__any(!(lsum <= kSumLimit))) lsum = rescale_and_redo<G>(st, sc, pop, sl2);
+    st.l[0] += lsum;
   } else {
     accumulate<G>(st, pop, vpage, NEXT, c, hl);
     if (CLOSING) return;
