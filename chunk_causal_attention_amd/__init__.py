@@ -124,6 +124,7 @@ def load():
         "sr_windows_attention": [P, I32, P, P, P, F32, P],
         "sr_global_attention": [P, I32, P, I32, P, P, F32, P],
         "sr_probe_mfma_bf16": [P, I32, I32, P],
+        "sr_global_attention_static": [P, I32, P, I32, P, P, F32, P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -258,6 +259,12 @@ def sr_windows_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=N
 def sr_global_attention(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
     scale = softmax_scale if softmax_scale is not None else 1.0 / (q.shape[-1] ** 0.5)
     _check(load().sr_global_attention(h, bank, _ptr(q), q.shape[0], _ptr(out), _ptr(lse), scale, _stream(stream)))
+
+
+def sr_global_attention_static(h, bank, q, out, lse=None, softmax_scale=None, stream=None):
+    scale = softmax_scale if softmax_scale is not None else 1.0 / (q.shape[-1] ** 0.5)
+    _check(load().sr_global_attention_static(h, bank, _ptr(q), q.shape[0], _ptr(out), _ptr(lse), scale,
+                                             _stream(stream)))
 
 
 def sr_kvcache_gather(h, bank, k_out, v_out, stream=None):
@@ -472,6 +479,12 @@ class KVCache:
         """Global-token queries [G][H][D] over the bank and every frame token of the current chunk."""
         out = self._out_lse(q, out, lse)
         sr_global_attention(self.h, bank, q, out, lse, softmax_scale, stream)
+        return out
+
+    def global_attention_static(self, bank, q, out=None, lse=None, softmax_scale=None, stream=None):
+        """global_attention with its records in the library's static scratch (allocates nothing)."""
+        out = self._out_lse(q, out, lse)
+        sr_global_attention_static(self.h, bank, q, out, lse, softmax_scale, stream)
         return out
 
     def gather(self, bank=0, max_tokens=None, stream=None):

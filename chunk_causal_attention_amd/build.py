@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsr.so")
-SOURCES = ["core.cpp", "capi.cpp", "kv_kernels.hip", "attention.hip", "few_attention.hip", "probe.hip"]
+SOURCES = ["core.cpp", "capi.cpp", "kv_kernels.hip", "attention.hip", "few_attention.hip", "probe.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -481,6 +481,38 @@ sr_status sr_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, void
   return device_status(sr::launch_mfma_probe(out, workgroups, iters, static_cast<hipStream_t>(stream)), "mfma probe");
 }
 
+sr_status sr_global_attention_static(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out,
+                                     float* lse, float softmax_scale, void* stream) {
+  sr::clear_error();
+  sr_status st = check_attention_args(c, bank, q, out, lse, softmax_scale);
+  if (st != SR_OK) return st;
+  if (!c->windowed) return sr::fail(SR_E_STATE, "no window layout: set one first");
+  if (!c->ring.has_current) return sr::fail(SR_E_STATE, "no current chunk: append one first");
+  if (n_rows < 1) return sr::fail(SR_E_INVALID, "n_rows %d < 1", n_rows);
+  const sr::Layout& L = c->ring.L;
+  sr::SegTable t{};
+  if (L.P > 0) t.s[t.n++] = sr::DevSeg{L.bank_page(bank), L.P};
+  const int32_t cur_page = L.slot_page(c->ring.slot_of(c->ring.cur_id));
+  for (int w = 0; w < c->win.n; ++w)
+    t.s[t.n++] = sr::DevSeg{cur_page + w * c->win.pages, c->win.frames * c->win.tok[w]};
+  st = check_pages(t);
+  if (st != SR_OK) return st;
+  if (!sr::few_attention_shape_ok(L, t, n_rows))
+    return sr::fail(SR_E_UNSUPPORTED, "the static-scratch call takes bf16 caches, head_dim 64 or 128 and 1..%d rows",
+                    sr::kFewRows);
+  const int64_t need = sr::few_attention_record_floats(L, t, n_rows);
+  if (need > sr::kStaticRecordFloats || L.H > sr::kStaticCounters)
+    return sr::fail(SR_E_UNSUPPORTED,
+                    "the call needs %lld floats of records for %d heads; the static scratch holds %d floats and %d heads",
+                    (long long)need, L.H, sr::kStaticRecordFloats, sr::kStaticCounters);
+  sr::SplitWorkspace ws;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = device_status(sr::static_scratch_workspace(&ws, s), "static scratch");
+  if (st != SR_OK) return st;
+  return device_status(sr::launch_few_attention(L, c->pool, t, n_rows, q, out, lse, softmax_scale, ws, s),
+                       "global attention (static scratch)");
+}
+
 const sr_ring* sr_kvcache_ring(const sr_kvcache* c) { return c ? &c->ring : nullptr; }
 
 sr_status sr_kvcache_destroy(sr_kvcache* c) {

@@ -271,15 +271,25 @@ __global__ __launch_bounds__(kWaves * 64) void few_attention_kernel(const FewArg
 
 }  // namespace
 
-bool few_attention_fits(const Layout& L, const SegTable& t, int32_t n_q, const SplitWorkspace& ws) {
-  if (L.dtype != SR_BF16 || (L.D != 64 && L.D != 128) || n_q < 1 || n_q > kFewRows || ws.cus_per_xcd <= 0) return false;
+int64_t few_attention_record_floats(const Layout& L, const SegTable& t, int32_t n_q) {
   int64_t npages = 0;
   for (int s = 0; s < t.n; ++s) npages += (t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
   const int64_t pieces = (npages + 1) / 2;
-  const int64_t rec_floats = int64_t(L.H) * pieces * (64 + int64_t(n_q) * L.D);
+  return int64_t(L.H) * pieces * (64 + int64_t(n_q) * L.D);
+}
+
+bool few_attention_shape_ok(const Layout& L, const SegTable& t, int32_t n_q) {
+  if (L.dtype != SR_BF16 || (L.D != 64 && L.D != 128) || n_q < 1 || n_q > kFewRows) return false;
+  int64_t npages = 0;
+  for (int s = 0; s < t.n; ++s) npages += (t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
+  const int64_t pieces = (npages + 1) / 2;
+  return npages > 0 && 2 * pieces * n_q <= int64_t(kWaves) * L.D * kPad;
+}
+
+bool few_attention_fits(const Layout& L, const SegTable& t, int32_t n_q, const SplitWorkspace& ws) {
+  if (ws.cus_per_xcd <= 0 || !few_attention_shape_ok(L, t, n_q)) return false;
   const int64_t have = int64_t(8) * 4 * ws.cus_per_xcd * attn_record_floats(L.D);
-  return npages > 0 && L.H <= 8 * ws.cus_per_xcd && rec_floats <= have &&
-         2 * pieces * n_q <= int64_t(kWaves) * L.D * kPad;
+  return L.H <= 8 * ws.cus_per_xcd && few_attention_record_floats(L, t, n_q) <= have;
 }
 
 hipError_t launch_few_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, const void* q,

@@ -255,4 +255,17 @@ constexpr int32_t kProbeThreads = 512;
 constexpr int32_t kProbeChains = 4;
 hipError_t launch_mfma_probe(float* out, int32_t workgroups, int32_t iters, hipStream_t st);
 
+// Library-owned scratch of sr_global_attention_static (static_scratch.hip): records of the
+// split-K global-token kernel (at most kStaticRecordFloats floats: 4 MiB) and kStaticCounters
+// arrival counters.  Fills *ws with this device's copy (looked up, and its counters zeroed on
+// stream st, on the device's first call).
+constexpr int32_t kStaticRecordFloats = 1 << 20;
+constexpr int32_t kStaticCounters = 4096;
+hipError_t static_scratch_workspace(SplitWorkspace* ws, hipStream_t st);
+// Records (floats) and counters the few-row kernel needs for n_q rows over the pages of t.
+int64_t few_attention_record_floats(const Layout& L, const SegTable& t, int32_t n_q);
+// The few-row kernel can take the call at all (bf16, head_dim 64 or 128, 1..kFewRows rows, the
+// wave-merge buffer holds the rows), whatever workspace it gets.
+bool few_attention_shape_ok(const Layout& L, const SegTable& t, int32_t n_q);
+
 }  // namespace sr

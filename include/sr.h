@@ -367,6 +367,23 @@ sr_status sr_windows_attention(sr_kvcache* c, int32_t bank, const void* q, void*
 sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
                               float softmax_scale, void* stream);
 
+/* sr_global_attention for callers that cannot allocate device memory (code under graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the same split-K call, with its
+ * records and arrival counters in a scratch array the library owns -- 4 MiB of records
+ * (2^20 floats) and 4096 counters, one copy per GPU held until the process ends -- instead of
+ * the cache's workspace; no device memory is allocated by this call or by the library.  The
+ * result equals sr_global_attention's with a workspace attached, bit for bit.  All calls on one
+ * GPU share its copy: calls that overlap on one GPU (other streams, other threads) race and
+ * must be ordered by the caller.  The first call on a GPU looks up that GPU's copy and enqueues
+ * one small kernel on `stream` that zeroes its counters; every call leaves them at zero.
+ * Same arguments and errors as sr_global_attention, plus SR_E_UNSUPPORTED when the call does
+ * not fit the few-row kernel (a cache other than SR_BF16, head_dim other than 64 or 128, more
+ * than 32 rows) or needs more scratch than the array holds (H * ceil(pages / 2) * (64 + n_rows *
+ * head_dim) floats of records, pages = the call's key pages; H <= 4096); nothing is enqueued
+ * then. */
+sr_status sr_global_attention_static(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,
+                                     float softmax_scale, void* stream);
+
 /* Copies the logical key/value sequence of a call on `bank` (persistent, history oldest
  * first, current) into k_out / v_out (device, [max_tokens][H][D]), bit-exact.  *n_tokens
  * receives the length; SR_E_INVALID if it exceeds max_tokens (nothing enqueued).  For tests
