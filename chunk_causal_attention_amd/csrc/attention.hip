@@ -201,7 +201,7 @@ struct Geo {
     Op op[QB][KSTEPS];  // query operands, resident for the whole piece
   };
   static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
-  static constexpr int RPL = QB * (NDB * 16 + 2);  // record floats per lane: O^T, max, sum
+  static constexpr int RPL = QB * (NDB * 16 + 4);  // record floats per lane: O^T, max, sum, 2 pad
   static constexpr int REC = NW * 64 * RPL;        // record floats per workgroup
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
 };
@@ -226,7 +226,7 @@ struct GeoMx {
   static constexpr int TABLE = VBASE + 2 * VPAGE;
   static constexpr int LIMS = TABLE + kMaxTiles * 16;  // per-lane causal limits (int), read on partial tiles
   static constexpr int LDS_BYTES = LIMS + NW * 64 * 4;
-  static constexpr int RPL = QB * (NDB * 16 + 2);
+  static constexpr int RPL = QB * (NDB * 16 + 4);
   static constexpr int REC = NW * 64 * RPL;
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
   static_assert(SC + NB * BN <= KPAGE && KPAGE % 1024 == 0 && VPAGE % 1024 == 0, "page layout");
@@ -609,34 +609,42 @@ __device__ __forceinline__ int for_each_subpiece(const AttnArgs& a, const SplitI
   return 2;
 }
 
-// Records are written and read with device-scope (agent) relaxed atomic stores and loads,
-// which gfx950 performs at the device's coherence point without touching other data in the
-// XCD's L2.  Ordering: every wave waits for its record stores to complete (vmcnt 0) before
-// the workgroup barrier that precedes the arrival counter update, and the merging workgroup
-// loads records only after its counter update returned.  Release/acquire fences at device
-// scope would instead write back and invalidate the whole L2 of the XCD, dropping the key
-// pages every other workgroup there is streaming.
-__device__ __forceinline__ void rec_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float rec_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Records are written and read with 16-byte buffer stores and loads carrying the device-scope
+// coherence bit (sc1: what a relaxed atomic access at agent scope compiles to, here four
+// dwords per lane at once), which gfx950 performs at the device's coherence point without
+// touching other data in the XCD's L2.  Ordering: every wave waits for its record stores to
+// complete (vmcnt 0) before the workgroup barrier that precedes the arrival counter update,
+// and the merging workgroup loads records only after its counter update returned.
+// Release/acquire fences at device scope would instead write back and invalidate the whole L2
+// of the XCD, dropping the key pages every other workgroup there is streaming.
+constexpr int kCoherentAux = 16;  // cache-policy operand of the buffer builtins: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const float* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
 }
 
-// Record layout: lane-major, float j of lane (wave, lane) at (wave * RPL + j) * 64 + lane,
-// so every store and load of a record is a coalesced 256-byte row per wave.
+// Record layout: 16-byte chunks, lane-major: chunk j of lane (wave, lane) at byte
+// ((wave * RPL / 4 + j) * 64 + lane) * 16, so every store and load of a record is a coalesced
+// 1 KiB row per wave.  Per query block: O^T in chunks 4 db + ig (registers 4 ig .. 4 ig + 3 of
+// output block db), then one chunk (max, sum, 0, 0).
 template <class G>
 __device__ __forceinline__ void store_record(float* rec, const RowState<G>& st, int wave, int lane) {
-  float* p = rec + size_t(wave) * G::RPL * 64 + lane;
+  static_assert(G::RPL % 4 == 0, "records in 16-byte chunks");
+  const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec, G::REC * 4);
+  const int off = (wave * (G::RPL / 4) * 64 + lane) * 16;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
-    float* q = p + qb * (G::NDB * 16 + 2) * 64;
+    const int j0 = qb * (G::NDB * 4 + 1);
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) rec_store(q + (db * 16 + e) * 64, st.acc[qb][db][e]);
-    rec_store(q + (G::NDB * 16) * 64, st.m[qb]);
-    rec_store(q + (G::NDB * 16 + 1) * 64, st.l[qb]);
+      for (int ig = 0; ig < 4; ++ig) {
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = st.acc[qb][db][4 * ig + e];
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off + (j0 + 4 * db + ig) * 1024, 0, kCoherentAux);
+      }
+    const f32x4_t ml = {st.m[qb], st.l[qb], 0.0f, 0.0f};
+    __builtin_amdgcn_raw_buffer_store_b128(ml, r, off + (j0 + 4 * G::NDB) * 1024, 0, kCoherentAux);
   }
 }
 
@@ -647,7 +655,7 @@ __device__ __forceinline__ void store_record(float* rec, const RowState<G>& st, 
 template <class G>
 __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int own,
                                               int wave, int lane) {
-  const size_t lane_off = size_t(wave) * G::RPL * 64 + lane;
+  const int off = (wave * (G::RPL / 4) * 64 + lane) * 16;
   RowState<G> mg;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
@@ -657,13 +665,14 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
     for (int db = 0; db < G::NDB; ++db) mg.acc[qb][db] = f32x16_t{};
   }
   for_each_subpiece(a, it, a.cus_per_xcd, [&](int slot) {
-    const float* p = a.rec + size_t(slot) * G::REC + lane_off;
+    const __amdgpu_buffer_rsrc_t r = rec_rsrc(a.rec + size_t(slot) * G::REC, G::REC * 4);
     const bool mine = slot == own;
 #pragma unroll
     for (int qb = 0; qb < G::QB; ++qb) {
-      const float* q = p + qb * (G::NDB * 16 + 2) * 64;
-      const float mk = mine ? st.m[qb] : rec_load(q + (G::NDB * 16) * 64);
-      const float lk = mine ? st.l[qb] : rec_load(q + (G::NDB * 16 + 1) * 64);
+      const int j0 = qb * (G::NDB * 4 + 1);
+      f32x4_t ml = {st.m[qb], st.l[qb], 0.0f, 0.0f};
+      if (!mine) ml = __builtin_amdgcn_raw_buffer_load_b128(r, off + (j0 + 4 * G::NDB) * 1024, 0, kCoherentAux);
+      const float mk = ml[0], lk = ml[1];
       const float mn = fmaxf(mg.m[qb], mk);
       const float a0 = __builtin_amdgcn_exp2f(mg.m[qb] - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
       mg.m[qb] = mn;
@@ -671,9 +680,13 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float x = mine ? st.acc[qb][db][e] : rec_load(q + (db * 16 + e) * 64);
-          mg.acc[qb][db][e] = mg.acc[qb][db][e] * a0 + x * a1;
+        for (int ig = 0; ig < 4; ++ig) {
+          f32x4_t x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = st.acc[qb][db][4 * ig + e];
+          if (!mine) x = __builtin_amdgcn_raw_buffer_load_b128(r, off + (j0 + 4 * db + ig) * 1024, 0, kCoherentAux);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mg.acc[qb][db][4 * ig + e] = mg.acc[qb][db][4 * ig + e] * a0 + x[e] * a1;
         }
     }
   });
@@ -1103,6 +1116,27 @@ __device__ __forceinline__ void mx_key_loop(const AttnArgs& a, char* smem, const
   st.l[0] = hl == 0 ? lacc[0] : 0.0f;
 }
 
+// The page requests and barriers of the key loop without its compute, for a wave none of
+// whose query rows exist (the last, partial query tile of a head): the wave still moves its
+// share of every page and meets every barrier, in the order of the bf16 and reduced-precision
+// loops (V of tile t+1 into buffer (t+1) % 2 after the barrier of page t, K of tile t+2 into
+// buffer t % 2), but leaves the matrix unit and the LDS reads to the waves that have rows.
+template <class G>
+__device__ __forceinline__ void idle_key_loop(const AttnArgs& a, char* smem, const int4* tab, int ntiles,
+                                              size_t head_page, int wave, int lane) {
+  for (int t = 0; t < ntiles; ++t) {
+    const int vpage_next = uniform(tab[min(t + 1, ntiles - 1)].x);
+    const int kpage_next = uniform(tab[min(t + 2, ntiles - 1)].x);
+    if (t >= 1) wait_loads<0>();
+    __syncthreads();
+    if (t + 1 < ntiles)
+      issue_v<G>(a.vpool + (head_page + vpage_next) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE, wave,
+                 lane);
+    if (t + 2 < ntiles)
+      issue_k<G>(a.kpool + (head_page + kpage_next) * G::KPAGE, smem + (t & 1) * G::KPAGE, wave, lane);
+  }
+}
+
 // Length and first page of segment s as window `win` sees it (win < 0: the table as is; else
 // the bank segments as is and, of every chunk, the window's pages and tokens).
 __device__ __forceinline__ int seg_len(const AttnArgs& a, int win, int s) {
@@ -1220,7 +1254,9 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
 
   const float sl2 = a.scale_log2;
   const int nsub = 2 * ntiles;  // sub-tiles j = 2t, 2t+1 of tile t
-  if constexpr (G::MX) {
+  if (uniform(q0 + wave * G::QB * 32) >= n_q) {
+    idle_key_loop<G>(a, smem, tab, ntiles, head_page, wave, lane);
+  } else if constexpr (G::MX) {
     mx_key_loop<G>(a, smem, tab, st, qo, lim_cur, ntiles, head_page, sl2, wave, lane);
   } else {
   const auto& qop = qo.op;

@@ -64,8 +64,9 @@ __host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, i
 }
 
 // Floats of one workgroup's partial result in the split schedule: per lane of the 8 waves,
-// the head_dim/2 output accumulators it holds plus its running max and sum.
-__host__ __device__ constexpr int32_t attn_record_floats(int32_t head_dim) { return 8 * 64 * (head_dim / 2 + 2); }
+// the head_dim/2 output accumulators it holds plus its running max and sum, padded to
+// whole 16-byte chunks.
+__host__ __device__ constexpr int32_t attn_record_floats(int32_t head_dim) { return 8 * 64 * (head_dim / 2 + 4); }
 
 // Split schedule.  Workgroup i of a launch runs on XCD i % 8 as that XCD's (i / 8)-th
 // workgroup, and each XCD (own L2, C compute units) gets a contiguous range of the head-major

@@ -274,7 +274,7 @@ sr_status sr_prefix_attention(sr_kvcache* c, int32_t bank, const void* q, void* 
  * ("3.3 Inference Acceleration and End-to-End Deployment", attention kernel tuning); this
  * split is the MI355X choice.
  *
- * Layout: 32 C records of 8 x 64 x (head_dim / 2 + 2) floats, then 8 C int32 arrival
+ * Layout: 32 C records of 8 x 64 x (head_dim / 2 + 4) floats, then 8 C int32 arrival
  * counters (rounded up to 256 bytes).  The counters must be zero when a call starts;
  * sr_kvcache_set_workspace zeroes them and every call leaves them zero.  Results with and
  * without a workspace agree within rounding (different summation order); with a workspace
