@@ -8,7 +8,7 @@
 //
 // Work decomposition.  An item is (head, tile of BM = NW*QB*32 = 256 queries); each wave
 // owns QB blocks of 32 queries.  A piece of work is an item's query tile over a range of
-// its key tiles: the whole range, or, in the split schedule (kernels.hpp, xcd_plan), part
+// its key tiles: the whole range, or, in the split schedule (kernels.hpp: queues of units), part
 // of it, with the partial results merged by the item's last piece.  A piece walks the key
 // tiles of its segments in visiting order; tiles past the last visible causal block are
 // never loaded.  Each tile (BN = 128 keys, one cache page) is copied unchanged from HBM
@@ -161,17 +161,19 @@ struct AttnArgs {
   int32_t n_q, H, total_pages, causal_block;
   int32_t q_tiles, num_wg;
   float scale_log2;
-  int32_t split;           // 0: one workgroup per item; 1: the split schedule (xcd_plan)
-  int32_t fan;             // > 1: the fan split (fan_pieces), used instead of xcd_plan
+  int32_t split;           // 0: one workgroup per item; 1: the split schedule (queues of units)
+  int32_t fan;             // > 1: the fan split (fan_pieces), used instead of the queues
   int32_t fixed_tiles;     // pages of the bank and history segments
   int32_t n_items;         // H * q_tiles (head, query tile) items, head-major
   int32_t cus_per_xcd;     // split: C, compute units per XCD
   float* rec;              // split: 4C partial records per XCD
   int32_t* cnt;            // split: C arrival counters per XCD (zero between calls)
+  int32_t* qctr;           // split: queue counter of each XCD, then the exit counter (zero between calls)
   SegTable t;
   WinView win;                              // window mode (win.n > 0): see WinView
-  XcdPlan plan[8];                          // split: xcd_plan of each XCD
-  int16_t left_tiles[8][kMaxCusPerXcd];     // split: key tiles of each XCD's split items
+  int32_t q_first[8], q_whole[8], q_left[8];  // split: each XCD's first item, whole items, split items
+  int32_t q_share[8];                         // split: each XCD's split tiles per compute unit
+  int16_t left_tiles[8][kMaxCusPerXcd];       // split: key tiles of each XCD's split items
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
@@ -203,6 +205,7 @@ struct Geo {
   static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
   static constexpr int RPL = QB * (NDB * 16 + 4);  // record floats per lane: O^T, max, sum, 2 pad
   static constexpr int REC = NW * 64 * RPL;        // record floats per workgroup
+  static constexpr bool REC16 = ES == 2;           // O^T kept as bf16 in the record (bf16 caches)
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
 };
 
@@ -228,6 +231,7 @@ struct GeoMx {
   static constexpr int LDS_BYTES = LIMS + NW * 64 * 4;
   static constexpr int RPL = QB * (NDB * 16 + 4);
   static constexpr int REC = NW * 64 * RPL;
+  static constexpr bool REC16 = true;
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
   static_assert(SC + NB * BN <= KPAGE && KPAGE % 1024 == 0 && VPAGE % 1024 == 0, "page layout");
   // Score register i of lane half hl holds key 8*(i/4) + 4*hl + i%4 of its 32-key block (the
@@ -573,124 +577,142 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return int64_t((uint64_t(uint32_t(uniform(int(u >> 32)))) << 32) | uint32_t(uniform(int(uint32_t(u)))));
 }
 
-// A split item as the merge sees it: XCD x, index r among the XCD's split items, its tile
-// count, and the XCD's plan (xcd_plan in kernels.hpp).
+// A split item as the merge sees it: XCD x, index r among the XCD's split items and its tile
+// count (queue split), or its pieces, first record slot and arrival counter (fan split).
 struct SplitItem {
-  int x, r, tiles;
-  XcdPlan plan;
-  int fan = 0;    // fan split: pieces of the item (0: two-band split)
+  int x = 0, r = 0, tiles = 0, share = 0;
+  int fan = 0;    // fan split: pieces of the item (0: queue split)
   int slot0 = 0;  // fan split: the item's first record slot
   int ctr = 0;    // fan split: the item's arrival counter
 };
 
-// Key tiles of split item r of XCD x (item_tiles of its query tile, computed on the host).
-__device__ __forceinline__ int split_item_tiles(const AttnArgs& a, int x, int r) { return a.left_tiles[x][r]; }
-
-// Calls f(slot) for every piece of split item `it` in slot order; returns their count (0: the
-// item runs whole on its band-0 workgroup).
+// Calls f(slot) for every piece of split item `it` in slot order; returns their count.
 template <class F>
 __device__ __forceinline__ int for_each_subpiece(const AttnArgs& a, const SplitItem& it, int C, F&& f) {
   if (it.fan > 0) {
     for (int q = 0; q < it.fan; ++q) f(it.slot0 + q);
     return it.fan;
   }
-  const XcdPlan& p = it.plan;
-  if (it.tiles <= p.b) return 0;
-  const int base = it.x * 4 * C;
-  f(base + 2 * it.r);  // band 0
-  int start = 0;       // band-1 layout offset of the item
-  for (int rr = 0; rr < it.r; ++rr) start += band1_len(split_item_tiles(a, it.x, rr), p.b);
-  const int len = it.tiles - p.b;
-  f(base + 2 * C + 2 * it.r);
-  if (start / p.s != (start + len - 1) / p.s) {  // cut by a workgroup boundary
-    f(base + 2 * C + 2 * it.r + 1);
-    return 3;
+  const int base = it.x * 4 * C + kSplitPieces * it.r;
+  int n = 0;
+  for (int k = 0; k < kSplitPieces; ++k) {
+    if (piece_begin(it.tiles, it.share, k + 1) > piece_begin(it.tiles, it.share, k)) {
+      f(base + k);
+      ++n;
+    }
   }
-  return 2;
+  return n;
 }
 
-// Records are written and read with 16-byte buffer stores and loads carrying the device-scope
-// coherence bit (sc1: what a relaxed atomic access at agent scope compiles to, here four
-// dwords per lane at once), which gfx950 performs at the device's coherence point without
+// Records are written and read with relaxed 8-byte atomic stores and loads at device (agent)
+// scope, which gfx950 performs at the device's coherence point (the sc1 cache policy) without
 // touching other data in the XCD's L2.  Ordering: every wave waits for its record stores to
 // complete (vmcnt 0) before the workgroup barrier that precedes the arrival counter update,
 // and the merging workgroup loads records only after its counter update returned.
 // Release/acquire fences at device scope would instead write back and invalidate the whole L2
 // of the XCD, dropping the key pages every other workgroup there is streaming.
-constexpr int kCoherentAux = 16;  // cache-policy operand of the buffer builtins: sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const float* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+__device__ __forceinline__ void rec_put(float* rec, int word, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(rec) + word, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t rec_get(const float* rec, int word) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(rec)) + word, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{x, y}), bf16x2_t));
+}
+__device__ __forceinline__ float bf16_low(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_high(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+__device__ __forceinline__ uint64_t pair64(uint32_t lo, uint32_t hi) { return uint64_t(lo) | (uint64_t(hi) << 32); }
+// The bits of a float, taken by value: __builtin_bit_cast applied directly to an element of an
+// ext_vector_type vector reads the wrong value with this toolchain (every element of the
+// vector came out as element 0), a scalar argument does not.
+__device__ __forceinline__ uint32_t float_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Record layout: 8-byte words, lane-major: word w of lane (wave, lane) at word index
+// (wave * RPL / 2 + w) * 64 + lane, so every store and load of a record is a coalesced 512-byte
+// row per wave.  Per query block, fp32 records (fp32 caches): O^T in words 8 db + k (registers
+// 2k, 2k+1 of output block db), then one word (max, sum).  bf16 records (bf16 and reduced-
+// precision caches, whose outputs are bf16): O^T rounded to bf16 in words 4 db + k (registers
+// 4k .. 4k+3 of block db), then (max, sum) in fp32.
+template <class G>
+constexpr int record_words() {
+  return G::REC16 ? 4 : 8;  // words per 32-feature output block
+}
+template <class G>
+__device__ __forceinline__ uint64_t record_word(const RowState<G>& st, int qb, int db, int k) {
+  const f32x16_t& o = st.acc[qb][db];
+  if constexpr (G::REC16)
+    return pair64(pack_bf16x2(o[4 * k], o[4 * k + 1]), pack_bf16x2(o[4 * k + 2], o[4 * k + 3]));
+  else
+    return pair64(float_bits(o[2 * k]), float_bits(o[2 * k + 1]));
 }
 
-// Record layout: 16-byte chunks, lane-major: chunk j of lane (wave, lane) at byte
-// ((wave * RPL / 4 + j) * 64 + lane) * 16, so every store and load of a record is a coalesced
-// 1 KiB row per wave.  Per query block: O^T in chunks 4 db + ig (registers 4 ig .. 4 ig + 3 of
-// output block db), then one chunk (max, sum, 0, 0).
 template <class G>
 __device__ __forceinline__ void store_record(float* rec, const RowState<G>& st, int wave, int lane) {
-  static_assert(G::RPL % 4 == 0, "records in 16-byte chunks");
-  const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec, G::REC * 4);
-  const int off = (wave * (G::RPL / 4) * 64 + lane) * 16;
+  static_assert(G::RPL % 2 == 0, "records in 8-byte words");
+  constexpr int NK = record_words<G>();
+  static_assert(G::QB * (G::NDB * NK + 1) <= G::RPL / 2, "record fits its slot");
+  const int base = wave * (G::RPL / 2) * 64 + lane;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
-    const int j0 = qb * (G::NDB * 4 + 1);
+    const int w0 = qb * (G::NDB * NK + 1);
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        f32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = st.acc[qb][db][4 * ig + e];
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, off + (j0 + 4 * db + ig) * 1024, 0, kCoherentAux);
-      }
-    const f32x4_t ml = {st.m[qb], st.l[qb], 0.0f, 0.0f};
-    __builtin_amdgcn_raw_buffer_store_b128(ml, r, off + (j0 + 4 * G::NDB) * 1024, 0, kCoherentAux);
+      for (int k = 0; k < NK; ++k) rec_put(rec, base + (w0 + NK * db + k) * 64, record_word<G>(st, qb, db, k));
+    rec_put(rec, base + (w0 + NK * G::NDB) * 64,
+            pair64(float_bits(st.m[qb]), float_bits(st.l[qb])));
   }
 }
 
 // Merges the pieces of a split item in slot order, rescaling to the running max as it goes
-// (O^T and l of each piece times 2^(m_piece - m)).  The merging workgroup's own piece, slot
-// `own`, is taken from its registers (the same values its record holds), the others from
-// their records.
+// (O^T and l of each piece times 2^(m_piece - m)).  Every piece, the merging workgroup's own
+// included, is read back from its record (the own one was completed before the arrival
+// counter moved), so all pieces pass through the same rounding whichever piece merges.
 template <class G>
-__device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int own,
-                                              int wave, int lane) {
-  const int off = (wave * (G::RPL / 4) * 64 + lane) * 16;
-  RowState<G> mg;
+__device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st, const SplitItem& it, int wave,
+                                              int lane) {
+  constexpr int NK = record_words<G>();
+  const int base = wave * (G::RPL / 2) * 64 + lane;
 #pragma unroll
   for (int qb = 0; qb < G::QB; ++qb) {
-    mg.m[qb] = kMaxInit;
-    mg.l[qb] = 0.0f;
+    st.m[qb] = kMaxInit;
+    st.l[qb] = 0.0f;
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) mg.acc[qb][db] = f32x16_t{};
+    for (int db = 0; db < G::NDB; ++db) st.acc[qb][db] = f32x16_t{};
   }
   for_each_subpiece(a, it, a.cus_per_xcd, [&](int slot) {
-    const __amdgpu_buffer_rsrc_t r = rec_rsrc(a.rec + size_t(slot) * G::REC, G::REC * 4);
-    const bool mine = slot == own;
+    const float* rec = a.rec + size_t(slot) * G::REC;
 #pragma unroll
     for (int qb = 0; qb < G::QB; ++qb) {
-      const int j0 = qb * (G::NDB * 4 + 1);
-      f32x4_t ml = {st.m[qb], st.l[qb], 0.0f, 0.0f};
-      if (!mine) ml = __builtin_amdgcn_raw_buffer_load_b128(r, off + (j0 + 4 * G::NDB) * 1024, 0, kCoherentAux);
-      const float mk = ml[0], lk = ml[1];
-      const float mn = fmaxf(mg.m[qb], mk);
-      const float a0 = __builtin_amdgcn_exp2f(mg.m[qb] - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
-      mg.m[qb] = mn;
-      mg.l[qb] = mg.l[qb] * a0 + lk * a1;
+      const int w0 = qb * (G::NDB * NK + 1);
+      const uint64_t ml = rec_get(rec, base + (w0 + NK * G::NDB) * 64);
+      const float mk = __builtin_bit_cast(float, uint32_t(ml)), lk = __builtin_bit_cast(float, uint32_t(ml >> 32));
+      const float mn = fmaxf(st.m[qb], mk);
+      const float a0 = __builtin_amdgcn_exp2f(st.m[qb] - mn), a1 = __builtin_amdgcn_exp2f(mk - mn);
+      st.m[qb] = mn;
+      st.l[qb] = st.l[qb] * a0 + lk * a1;
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          f32x4_t x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = st.acc[qb][db][4 * ig + e];
-          if (!mine) x = __builtin_amdgcn_raw_buffer_load_b128(r, off + (j0 + 4 * db + ig) * 1024, 0, kCoherentAux);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mg.acc[qb][db][4 * ig + e] = mg.acc[qb][db][4 * ig + e] * a0 + x[e] * a1;
+        for (int k = 0; k < NK; ++k) {
+          const uint64_t wv = rec_get(rec, base + (w0 + NK * db + k) * 64);
+          const uint32_t lo = uint32_t(wv), hi = uint32_t(wv >> 32);
+          f32x16_t& o = st.acc[qb][db];
+          if constexpr (G::REC16) {
+            o[4 * k] = o[4 * k] * a0 + bf16_low(lo) * a1;
+            o[4 * k + 1] = o[4 * k + 1] * a0 + bf16_high(lo) * a1;
+            o[4 * k + 2] = o[4 * k + 2] * a0 + bf16_low(hi) * a1;
+            o[4 * k + 3] = o[4 * k + 3] * a0 + bf16_high(hi) * a1;
+          } else {
+            o[2 * k] = o[2 * k] * a0 + __builtin_bit_cast(float, lo) * a1;
+            o[2 * k + 1] = o[2 * k + 1] * a0 + __builtin_bit_cast(float, hi) * a1;
+          }
         }
     }
   });
-  st = mg;
 }
 
 // Iteration i of the key loop (ODD: i odd): mask sub-tile i if partial; P.V of sub-tile i-1
@@ -1332,7 +1354,7 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
     }
     __syncthreads();
     if (*flag == 0) return;
-    merge_records<G>(a, st, it, slot, wave, lane);
+    merge_records<G>(a, st, it, wave, lane);
   }
 
   // Epilogue: O = O^T / l, written token-major; lse = (max + log2 l) * ln 2.
@@ -1358,22 +1380,81 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   }
 }
 
-__device__ __forceinline__ XcdPlan uniform_plan(const XcdPlan& p) {
-  XcdPlan q;
-  q.first = uniform(p.first);
-  q.whole = uniform(p.whole);
-  q.left = uniform(p.left);
-  q.b = uniform(p.b);
-  q.s = uniform(p.s);
-  q.u1 = uniform(p.u1);
-  q.wgs = uniform(p.wgs);
-  return q;
+// The queue split (kernels.hpp): a persistent workgroup takes units from its XCD's queue, then
+// from the other XCDs' queues, until every queue is empty; the last workgroup to finish zeroes
+// the queue counters for the next call.  Thread 0 claims a unit and hands it to the
+// workgroup through LDS; the claim loop ends for every workgroup, since each counter only
+// grows and each workgroup gives up on a queue once it is past its end.
+template <class G>
+__device__ __forceinline__ void queue_split(const AttnArgs& a, char* smem, int* flag, int* claim, int home) {
+  const int C = a.cus_per_xcd;
+  int y = home, passed = 0;  // thread 0: the queue it claims from, queues found empty
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int u = -1;
+      while (passed < 8) {
+        const int units = a.q_whole[y] + kSplitPieces * a.q_left[y];
+        if (units > 0) {
+          const int v = __hip_atomic_fetch_add(a.qctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (v < units) {
+            u = v;
+            break;
+          }
+        }
+        y = (y + 1) & 7;
+        ++passed;
+      }
+      claim[0] = y;
+      claim[1] = u;
+    }
+    __syncthreads();
+    const int x = uniform(claim[0]), u = uniform(claim[1]);
+    __syncthreads();  // every thread has read the claim before thread 0 makes the next one
+    if (u < 0) break;
+    int h, qt, tb = 0, te, slot = -1;
+    SplitItem it{};
+    if (u < a.q_whole[x]) {
+      const int item = a.q_first[x] + u;
+      h = uniform(item / a.q_tiles);
+      qt = uniform(item - h * a.q_tiles);
+      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
+    } else {
+      const int v = u - a.q_whole[x], left = a.q_left[x];
+      const int k = v / left, r = v - k * left;
+      const int T = a.left_tiles[x][r];
+      const int share = a.q_share[x];
+      tb = uniform(piece_begin(T, share, k));
+      te = uniform(piece_begin(T, share, k + 1));
+      const int item = a.q_first[x] + a.q_whole[x] + r;
+      h = uniform(item / a.q_tiles);
+      qt = uniform(item - h * a.q_tiles);
+      if (te <= tb) continue;  // an empty piece of a short item: no work, no record
+      if (split_pieces(T, share) > 1) {
+        slot = x * 4 * C + kSplitPieces * r + k;
+        it.x = x;
+        it.r = r;
+        it.tiles = T;
+        it.share = share;
+      } else {
+        tb = 0;
+        te = T;
+      }
+    }
+    run_piece<G>(a, smem, flag, h, qt, tb, te, slot, it);
+  }
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(a.qctr + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == a.num_wg - 1) {
+      for (int q = 0; q < 9; ++q) __hip_atomic_store(a.qctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 template <class G>
 __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(const AttnArgs a) {
   __shared__ __align__(1024) char smem[G::LDS_BYTES];
   __shared__ int flag;
+  __shared__ int claim[2];
 
   // Workgroups are dispatched round-robin over the 8 XCDs: hardware id i runs on XCD i % 8
   // as the (i / 8)-th workgroup of that XCD.  Integer divisions are expanded on the vector
@@ -1381,12 +1462,6 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
 
-  // The workgroup's first piece; band-1 workgroups then walk further pieces.
-  int h = 0, qt = 0, tb = 0, te = 0, slot = -1;
-  SplitItem it{};
-  bool band1 = false;
-  XcdPlan p{};
-  int r = 0, pos = 0, end = 0, base = 0;  // band-1 walk; base: layout offset of item r's piece
   if (a.fan > 0) {
     // Fan split: workgroup j = (h fan + p) q_tiles + qt, numbered so each XCD gets a contiguous
     // range of j, runs piece p of item (h, qt); the query tiles of a head that read the same
@@ -1394,88 +1469,32 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
     const int j = local + xcd * per + (xcd < rem ? xcd : rem);
     const int hp = j / a.q_tiles;
-    qt = uniform(j - hp * a.q_tiles);
-    h = uniform(hp / a.fan);
+    const int qt = uniform(j - hp * a.q_tiles);
+    const int h = uniform(hp / a.fan);
     const int pc = uniform(hp - h * a.fan);
     const int tiles = item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len);
-    tb = uniform(pc * tiles / a.fan);
-    te = uniform((pc + 1) * tiles / a.fan);
+    const int tb = uniform(pc * tiles / a.fan);
+    const int te = uniform((pc + 1) * tiles / a.fan);
     const int item = h * a.q_tiles + qt;
+    SplitItem it{};
     it.fan = a.fan;
     it.slot0 = item * a.fan;
     it.ctr = item;
     run_piece<G>(a, smem, &flag, h, qt, tb, te, item * a.fan + pc, it);
     return;
   }
-  if (!a.split) {
-    // One workgroup per item, renumbered so each XCD gets a contiguous range of items: the
-    // query tiles of a head then share that XCD's L2 while they stream the same keys.
-    const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
-    const int g = local + xcd * per + (xcd < rem ? xcd : rem);
-    h = uniform(g / a.q_tiles);
-    qt = uniform(g - h * a.q_tiles);
-    te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
-  } else {
-    p = uniform_plan(a.plan[xcd]);
-    if (local < p.whole) {
-      const int item = p.first + local;
-      h = uniform(item / a.q_tiles);
-      qt = uniform(item - h * a.q_tiles);
-      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
-    } else {
-      const int j = local - p.whole;
-      if (j >= p.wgs) return;
-      if (j < p.left) {
-        // Band 0 of split item j: tiles [0, min(b, T)); the whole item if T <= b.
-        r = j;
-        const int tiles = split_item_tiles(a, xcd, r);
-        const int item = p.first + p.whole + r;
-        h = uniform(item / a.q_tiles);
-        qt = uniform(item - h * a.q_tiles);
-        te = tiles < p.b ? tiles : p.b;
-        if (tiles > p.b) {
-          slot = xcd * 4 * a.cus_per_xcd + 2 * r;
-          it = SplitItem{xcd, r, tiles, p};
-        }
-      } else {
-        // Band-1 workgroup q: units [q s, (q+1) s) of the band-1 layout.
-        band1 = true;
-        const int q = j - p.left;
-        pos = q * p.s;
-        end = pos + p.s < p.u1 ? pos + p.s : p.u1;
-        for (; r < p.left; ++r) {
-          const int len = band1_len(split_item_tiles(a, xcd, r), p.b);
-          if (pos < base + len) break;
-          base += len;
-        }
-      }
-    }
+  if (a.split) {
+    queue_split<G>(a, smem, &flag, claim, xcd);
+    return;
   }
-
-  // The bound on r only guards against a malformed plan; a valid one never reaches it.
-  for (;;) {
-    int e = 0, len = 0;
-    if (band1) {
-      if (r >= p.left) break;
-      const int tiles = split_item_tiles(a, xcd, r);
-      len = band1_len(tiles, p.b);
-      e = end < base + len ? end : base + len;
-      tb = p.b + (pos - base);
-      te = tb + (e - pos);
-      const int sub = pos > base ? 1 : 0;  // only a workgroup's first piece can start mid-piece
-      const int item = p.first + p.whole + r;
-      h = uniform(item / a.q_tiles);
-      qt = uniform(item - h * a.q_tiles);
-      slot = xcd * 4 * a.cus_per_xcd + 2 * a.cus_per_xcd + 2 * r + sub;
-      it = SplitItem{xcd, r, tiles, p};
-    }
-    run_piece<G>(a, smem, &flag, h, qt, tb, te, slot, it);
-    if (!band1) break;
-    pos = e;
-    if (pos >= end) break;
-    base += len;
-    for (++r; r < p.left && band1_len(split_item_tiles(a, xcd, r), p.b) == 0;) ++r;
-  }
+  // One workgroup per item, renumbered so each XCD gets a contiguous range of items: the
+  // query tiles of a head then share that XCD's L2 while they stream the same keys.
+  const int nwg = a.num_wg, per = nwg >> 3, rem = nwg & 7;
+  const int g = local + xcd * per + (xcd < rem ? xcd : rem);
+  const int h = uniform(g / a.q_tiles);
+  const int qt = uniform(g - h * a.q_tiles);
+  const int te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
+  run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{});
 }
 
 // Window mode (a.win.n > 0): one workgroup per item (window, head, query tile), window-major
@@ -1543,16 +1562,25 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
   if (a.fan > 0) {
     a.num_wg = a.n_items * a.fan;  // at most 8 C: records and counters fit the workspace
   } else if (a.split) {
-    // Per-XCD plans and split items' tile counts; 8 XCDs x the largest per-XCD count of
-    // whole items + split workgroups.
-    int32_t per = 0;
+    // Queues: XCD x owns items [first, first + n); the last n mod C of them are split.  One
+    // persistent workgroup per compute unit.
+    const int32_t C = ws.cus_per_xcd;
     for (int x = 0; x < 8; ++x) {
-      const XcdPlan p = xcd_plan(x, a.n_items, a.q_tiles, a.fixed_tiles, a.n_q, cb, t.s[t.n - 1].len, ws.cus_per_xcd,
-                                 a.left_tiles[x]);
-      a.plan[x] = p;
-      per = p.whole + p.wgs > per ? p.whole + p.wgs : per;
+      const int32_t first = int32_t(int64_t(x) * a.n_items / 8);
+      const int32_t n = int32_t(int64_t(x + 1) * a.n_items / 8) - first;
+      a.q_first[x] = first;
+      a.q_left[x] = n % C;
+      a.q_whole[x] = n - n % C;
+      int32_t split_tiles = 0;
+      for (int32_t r = 0; r < a.q_left[x]; ++r) {
+        a.left_tiles[x][r] =
+            int16_t(item_tiles((first + a.q_whole[x] + r) % a.q_tiles, a.fixed_tiles, a.n_q, cb, t.s[t.n - 1].len));
+        split_tiles += a.left_tiles[x][r];
+      }
+      a.q_share[x] = (split_tiles + C - 1) / C;
     }
-    a.num_wg = 8 * per;
+    a.qctr = ws.counters + 8 * C;
+    a.num_wg = 8 * C;
   } else {
     a.num_wg = win ? win->item0[win->n] : a.n_items;
   }

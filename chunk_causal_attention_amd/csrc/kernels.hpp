@@ -68,105 +68,47 @@ __host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, i
 // whole 16-byte chunks.
 __host__ __device__ constexpr int32_t attn_record_floats(int32_t head_dim) { return 8 * 64 * (head_dim / 2 + 4); }
 
-// Split schedule.  Workgroup i of a launch runs on XCD i % 8 as that XCD's (i / 8)-th
-// workgroup, and each XCD (own L2, C compute units) gets a contiguous range of the head-major
-// (head, query tile) items.  An XCD runs its items whole, C at a time: the query tiles of a
-// head then stream the same pages at the same time, so each page is fetched past L2 about
-// once per XCD.  The last `left` < C items of an XCD would leave units idle in a final round;
-// instead, split workgroup r < left runs tiles [0, min(b, T_r)) of split item r ("band 0"),
-// and the remaining tiles [b, T_r) of all split items, laid out one item after the other
-// ("band 1"), are dealt in runs of s tiles to the other split workgroups.  Band-0 workgroups
-// stream the same pages together, and so do band-1 workgroups.  A band-1 piece is at most s
-// long (the plan guarantees it), so it is cut by at most one workgroup boundary: sub-piece 0
-// and possibly 1.  Every piece of a split item leaves a partial record, in slot
-// x * 4C + 2r (band 0) or x * 4C + 2C + 2r + sub (band 1); the last piece of an item to
-// finish merges the item's records in slot order and writes its output.
-constexpr int32_t kPieceOverheadTiles = 4;  // measured cost of starting and ending a piece
-constexpr int32_t kMaxCusPerXcd = 64;       // largest C (split items per XCD are fewer)
+// Split schedule.  Workgroup i of a launch runs on XCD i % 8, and each XCD (own L2, C compute
+// units) owns a contiguous range of the head-major (head, query tile) items, so that the query
+// tiles of a head stream the same pages at about the same time and each page is fetched past
+// L2 about once per XCD.  The launch has one persistent workgroup per compute unit (8 C).  XCD
+// x keeps a queue of units: its items run whole, a multiple of C of them ("whole"), then the
+// key-tile pieces of its last `left` < C items ("split" items), which would otherwise leave
+// units idle in a final round.  Split item r of T tiles is cut into kSplitPieces pieces,
+// largest first (piece_begin), and the queue holds all items' piece 0,
+// then all pieces 1, and so on, so the queue ends in small pieces.  A workgroup takes the next
+// unit of its own XCD's queue through an atomic counter; once that queue is empty it takes
+// units from the other XCDs' queues in turn, so XCDs that run faster (they do, by several per
+// cent, depending on the data they stream) take over work of slower ones.  Piece k of split item
+// r leaves a partial record in slot x * 4C + 4r + k; the last piece of an item to finish merges
+// the item's records in slot order and writes its output, so the result does not depend on
+// which workgroup ran which piece.
+constexpr int32_t kMaxCusPerXcd = 64;  // largest C (split items per XCD are fewer)
+constexpr int32_t kSplitPieces = 4;    // pieces of a split item (record slots 4r .. 4r + 3)
+constexpr int32_t kQueueCounters = 16; // per call: 8 queue counters, 1 exit counter, padding
 
-struct XcdPlan {
-  int32_t first;  // first item of the XCD
-  int32_t whole;  // items run whole (a multiple of C, or 0)
-  int32_t left;   // split items (< C), items first + whole ...
-  int32_t b;      // band-0 width
-  int32_t s;      // band-1 tiles per workgroup (0: no band 1)
-  int32_t u1;     // band-1 tiles in all
-  int32_t wgs;    // split workgroups: left band-0 + ceil(u1 / s) band-1
-};
-
-__host__ __device__ inline int32_t band1_len(int32_t t, int32_t b) { return t > b ? t - b : 0; }
-
-// Estimated duration (tiles, plus kPieceOverheadTiles per piece) of the split round of an
-// XCD for band-0 width b; -1 if band 1 would need a run shorter than one of its pieces.
-inline int32_t split_estimate(const int16_t* T, int32_t left, int32_t C, int32_t b, int32_t* s_out, int32_t* u1_out) {
-  int32_t u1 = 0, maxlen = 0, band0 = 0;
-  for (int32_t r = 0; r < left; ++r) {
-    const int32_t l1 = band1_len(T[r], b);
-    u1 += l1;
-    maxlen = l1 > maxlen ? l1 : maxlen;
-    const int32_t l0 = T[r] < b ? T[r] : b;
-    band0 = l0 > band0 ? l0 : band0;
-  }
-  *u1_out = u1;
-  *s_out = 0;
-  int32_t worst = band0 + kPieceOverheadTiles;
-  if (u1 == 0) return worst;
-  const int32_t s = (u1 + (C - left) - 1) / (C - left);
-  if (s < maxlen) return -1;
-  *s_out = s;
-  // Pieces overlapping each run [q s, (q+1) s): two pointers over the band-1 pieces.
-  int32_t i = 0, start = 0;  // piece i starts at unit `start`
-  for (int32_t lo = 0; lo < u1; lo += s) {
-    const int32_t hi = lo + s < u1 ? lo + s : u1;
-    while (i < left && start + band1_len(T[i], b) <= lo) start += band1_len(T[i++], b);
-    int32_t n = 0;
-    for (int32_t k = i, a = start; k < left && a < hi; a += band1_len(T[k++], b)) n += band1_len(T[k], b) > 0;
-    const int32_t w = (hi - lo) + n * kPieceOverheadTiles;
-    worst = w > worst ? w : worst;
-  }
-  return worst;
+// First key tile of piece k (0 .. kSplitPieces) of a split item of T tiles when the XCD's
+// split work is `share` tiles per compute unit: piece 0 takes 85% of the share (the largest
+// unit a unit can take without running past the others), the rest of the item is halved
+// twice (piece_begin(T, kSplitPieces) = T).  A piece may be empty for very short items; empty
+// pieces are skipped and leave no record.
+__host__ __device__ inline int32_t piece_begin(int32_t T, int32_t share, int32_t k) {
+  if (k <= 0) return 0;
+  if (k >= kSplitPieces) return T;
+  int32_t p0 = share * 85 / 100;
+  p0 = p0 < 1 ? 1 : (p0 > T ? T : p0);
+  const int32_t rest = T - p0;
+  return k == 1 ? p0 : k == 2 ? p0 + rest / 2 : p0 + rest / 2 + rest / 4;
 }
-
-// Plan of XCD x; T receives the tile counts of its split items.
-inline XcdPlan xcd_plan(int32_t x, int32_t n_items, int32_t q_tiles, int32_t fixed_tiles, int32_t n_q, int32_t cb,
-                        int32_t cur_len, int32_t C, int16_t* T) {
-  XcdPlan p{};
-  p.first = int32_t(int64_t(x) * n_items / 8);
-  const int32_t n = int32_t(int64_t(x + 1) * n_items / 8) - p.first;
-  p.left = n % C;
-  p.whole = n - p.left;
-  if (p.left == 0) return p;
-  int32_t tmax = 0;
-  for (int32_t r = 0; r < p.left; ++r) {
-    T[r] = int16_t(item_tiles((p.first + p.whole + r) % q_tiles, fixed_tiles, n_q, cb, cur_len));
-    tmax = T[r] > tmax ? T[r] : tmax;
-  }
-  // Best b: every stride-th candidate, then the neighbours of the best one.
-  int32_t best = -1, best_b = tmax;
-  auto consider = [&](int32_t b) {
-    if (b < 1 || b > tmax) return;
-    int32_t s, u1;
-    const int32_t e = split_estimate(T, p.left, C, b, &s, &u1);
-    if (e >= 0 && (best < 0 || e < best || (e == best && b > best_b))) {
-      best = e;
-      best_b = b;
-    }
-  };
-  const int32_t stride = tmax / 64 > 1 ? tmax / 64 : 1;
-  for (int32_t b = 1; b <= tmax; b += stride) consider(b);
-  consider(tmax);
-  for (int32_t d = -stride; d <= stride; ++d) consider(best_b + d);
-  // Split only if it saves at least 1/16 of running the items whole.
-  const int32_t whole_cost = tmax + kPieceOverheadTiles / 2;
-  if (best < 0 || best > whole_cost - (whole_cost >> 4)) best_b = tmax;
-  p.b = best_b;
-  split_estimate(T, p.left, C, p.b, &p.s, &p.u1);
-  p.wgs = p.left + (p.u1 > 0 ? (p.u1 + p.s - 1) / p.s : 0);
-  return p;
+// Non-empty pieces of a split item of T tiles.
+__host__ __device__ inline int32_t split_pieces(int32_t T, int32_t share) {
+  int32_t n = 0;
+  for (int32_t k = 0; k < kSplitPieces; ++k) n += piece_begin(T, share, k + 1) > piece_begin(T, share, k);
+  return n;
 }
 
 // Even ("fan") split for launches with fewer (head, query tile) items than compute units, where
-// the two-band plan above would leave most units idle (a one-GPU share of a head-sharded run):
+// the queues above would leave most units idle (a one-GPU share of a head-sharded run):
 // each item's key tiles are cut into P equal pieces, P at most the units per item, every piece
 // at least kFanMinTiles long (twice the measured start-and-finish cost of a piece), and P at
 // most kFanMaxPieces (the merging piece reads the records one after the other, about a
@@ -189,12 +131,13 @@ inline int32_t split_cus_per_xcd(int32_t num_cus) {
   return C < 1 ? 1 : (C > kMaxCusPerXcd ? kMaxCusPerXcd : C);
 }
 
-// Attention workspace: 8 XCDs x 4C records, then 8C arrival counters (256-byte aligned).
+// Attention workspace: 8 XCDs x 4C records, then 8C arrival counters and the split schedule's
+// kQueueCounters queue counters (256-byte aligned).
 inline size_t attn_records_bytes(int32_t head_dim, int32_t num_cus) {
   return size_t(8) * 4 * split_cus_per_xcd(num_cus) * attn_record_floats(head_dim) * sizeof(float);
 }
 inline size_t attn_counters_bytes(int32_t num_cus) {
-  return (size_t(8) * split_cus_per_xcd(num_cus) * sizeof(int32_t) + 255) & ~size_t(255);
+  return ((size_t(8) * split_cus_per_xcd(num_cus) + kQueueCounters) * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
 // Split schedule of one call (see launch_attention): the XCD width and where partial results go.
@@ -236,7 +179,7 @@ hipError_t launch_gather(const Layout& L, const void* pool, const SegTable& t, i
 
 // Attention of n_q query rows q over the key segments of t (pages of `pool`), the last
 // segment seen per causal block of cb rows (cb == 0: whole; see item_tiles).  With
-// ws.cus_per_xcd > 0 the split schedule (xcd_plan) is used.  win (or nullptr): window mode
+// ws.cus_per_xcd > 0 the split schedule (queues of units, see above) is used.  win (or nullptr): window mode
 // (WinView; n_q is then the packed row count, cb 0, no split).
 hipError_t launch_attention(const Layout& L, const void* pool, const SegTable& t, int32_t n_q, int32_t cb,
                             const void* q, void* o, float* lse, float softmax_scale, const SplitWorkspace& ws,

@@ -174,7 +174,7 @@ def test_one_gpu_share_of_sharded_run(sr):
 
 def test_split_schedule_is_deterministic_and_leaves_counters_zero(sr):
     """Repeated calls give the same bits whichever piece merges; a workspace shared by two
-    caches works; the arrival counters are zero after every call; split and whole schedules
+    caches works; the arrival and queue counters are zero after every call; split and whole schedules
     agree within rounding."""
     import torch
     w = synth.get_workload("t_stream")
@@ -195,9 +195,10 @@ def test_split_schedule_is_deterministic_and_leaves_counters_zero(sr):
     first = harness.to_host(outs[0], w.dtype)
     for o in outs[1:]:
         assert (harness.to_host(o, w.dtype) == first).all()
-    # the counters (C = CUs / 8 per XCD, int32, padded to 256 bytes) end the workspace
+    # the arrival and queue counters (8 C + 16 int32 with C = CUs / 8, padded to 256 bytes)
+    # end the workspace
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    counters = ws[ws.numel() - (8 * max(cus // 8, 1) * 4 + 255) // 256 * 256:].view(torch.int32)
+    counters = ws[ws.numel() - ((8 * max(cus // 8, 1) + 16) * 4 + 255) // 256 * 256:].view(torch.int32)
     assert int(counters.abs().sum()) == 0
     st = gates.error_stats(harness.widen_host(first, w.dtype),
                            harness.widen_host(harness.to_host(whole, w.dtype), w.dtype))

@@ -116,10 +116,10 @@ def test_required_bytes_mx(sr, H, D, P, banks, cap, W):
 def test_attention_workspace_bytes(sr, H, D, cap, cus):
     """Per XCD (C = cus / 8 compute units, at least 1): 4C records of 8 waves x 64 lanes x
     (D/2 output floats + max + sum + 2 pad floats: whole 16-byte chunks), then C int32 arrival
-    counters, padded to 256 bytes."""
+    counters and 16 queue counters of the split schedule, padded to 256 bytes."""
     cfg = sr.config_for(H, D, 0, cap, 1)
     C = max(cus // 8, 1)
-    assert sr.sr_attention_workspace_bytes(cfg, cus) == 8 * 4 * C * 512 * (D // 2 + 4) * 4 + -(-8 * C * 4 // 256) * 256
+    assert sr.sr_attention_workspace_bytes(cfg, cus) == 8 * 4 * C * 512 * (D // 2 + 4) * 4 + -(-(8 * C + 16) * 4 // 256) * 256
 
 
 def test_attention_workspace_bytes_validation(sr):
