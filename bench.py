@@ -213,12 +213,17 @@ def make_inputs(sr, w, n_sets, torch):
 
 
 def copy_calibration(res, torch, dev):
-    """A plain device copy of known size, for scaling the profiler's HBM byte counters."""
+    """A plain device copy of known size, for scaling the profiler's HBM byte counters, and the same
+    bytes read once with the attention kernel's global-to-LDS page loads (sr_probe_lds_read), which
+    shows that one factor serves both."""
+    import chunk_causal_attention_amd as sr
     n = 256 << 20
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
+    sink = torch.empty(n // 256, dtype=torch.float32, device=dev)
     for _ in range(3):
         dst.copy_(src)
+        sr.sr_probe_lds_read(src, sink)
     torch.cuda.synchronize()
     res["copy_calibration_bytes"] = n
 
@@ -910,6 +915,128 @@ def run(args):
     return res
 
 
+# Counter passes of --counters: one rocprofv3 run each (a run may hold at most 8 SQ, 4 TCC,
+# 2 GRBM counters; FETCH_SIZE takes 3 TCC, WRITE_SIZE 2).
+COUNTER_PASSES = [
+    ("fetch", ["FETCH_SIZE"]),
+    ("write", ["WRITE_SIZE"]),
+    ("mfma", ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
+              "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT"]),
+    ("mix", ["SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+             "SQ_INSTS_LDS", "SQ_INSTS_VMEM"]),
+    ("lds", ["SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+             "SQ_LDS_IDX_ACTIVE", "SQ_LDS_CMD_FIFO_FULL"]),
+    ("l2", ["TCC_HIT_sum", "TCC_MISS_sum"]),
+]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def dominant_kernel(workload):
+    """Name fragment of the kernel the roofline is about for `workload`."""
+    return "windows_attention_kernel" if workload in DECODER_WORKLOADS else "chunk_attention_kernel"
+
+
+def attention_bytes(w):
+    """Algorithmic bytes of one chunk-attention call: Q and O once, the K and V of every visible key
+    once (bf16 / fp32 caches)."""
+    es = 2 if w.dtype == "bf16" else 4
+    return es * w.heads * w.head_dim * (2.0 * w.chunk + 2.0 * w.visible_keys)
+
+
+def _counter_means(csv_path, fragment):
+    """Mean per dispatch of every counter of the kernels whose name contains `fragment`, and the
+    mean dispatch duration (ns)."""
+    import csv
+    vals, durs = {}, {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if fragment not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+            durs[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    means = {k: sum(v.values()) / len(v) for k, v in vals.items()}
+    return means, (sum(durs.values()) / len(durs) if durs else None), len(durs)
+
+
+def run_counters(args):
+    """Every pass of COUNTER_PASSES as its own rocprofv3 run of this script (a child process, under a
+    hard time limit), on the workload's default launch with the 256 MiB copy calibration; returns
+    the per-dispatch means of the dominant kernel and the derived figures."""
+    import signal
+    import subprocess
+    import synth
+    out_dir = os.path.abspath(args.counters_dir)
+    os.makedirs(out_dir, exist_ok=True)
+    child = [sys.executable, "-u", os.path.abspath(__file__), "--workload", args.workload, "--no-cpu-baseline",
+             "--no-extra-c3", "--no-probe", "--steps", "4", "--warmup", "2", "--layers", str(args.layers),
+             "--copy-calibration"]
+    if args.no_split:
+        child.append("--no-split")
+    env = dict(os.environ, TMPDIR="/tmp")
+    frag = dominant_kernel(args.workload)
+    raw, dur, calib, cmds = {}, None, {}, []
+    for name, ctrs in COUNTER_PASSES:
+        cmd = ["rocprofv3", "--pmc"] + ctrs + ["--output-format", "csv", "-d", os.path.join(out_dir, name),
+                                               "-o", name, "--"] + child
+        cmds.append(" ".join(cmd))
+        print(f"[counters] pass {name}: {' '.join(ctrs)}", file=sys.stderr, flush=True)
+        p = subprocess.Popen(cmd, cwd="/tmp", env=env, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE,
+                             start_new_session=True)
+        try:
+            _, err = p.communicate(timeout=args.counters_timeout)
+        except subprocess.TimeoutExpired:
+            os.killpg(p.pid, signal.SIGKILL)
+            p.wait()
+            raise SystemExit(f"counter pass {name} exceeded {args.counters_timeout} s")
+        csv_path = os.path.join(out_dir, name, f"{name}_counter_collection.csv")
+        if not os.path.exists(csv_path):
+            raise SystemExit(f"counter pass {name} failed (exit {p.returncode}): {err.decode()[-2000:]}")
+        means, d, n = _counter_means(csv_path, frag)
+        raw.update(means)
+        dur = d if dur is None else dur
+        if name in ("fetch", "write"):
+            cm, _, _ = _counter_means(csv_path, COPY_KERNEL)
+            calib.update(cm)
+        if name == "fetch":
+            lm, _, _ = _counter_means(csv_path, "lds_read_probe_kernel")
+            calib["LDS_FETCH_SIZE"] = lm.get("FETCH_SIZE")
+    copy_bytes = 256 << 20
+    fetch_factor = copy_bytes / (calib["FETCH_SIZE"] * 1024.0)   # about 2: FETCH_SIZE counts half of each request
+    write_factor = copy_bytes / (calib["WRITE_SIZE"] * 1024.0)
+    fetched = fetch_factor * raw["FETCH_SIZE"] * 1024.0
+    written = write_factor * raw["WRITE_SIZE"] * 1024.0
+    xcds = 8
+    gui = raw.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+    res = {
+        "workload": args.workload, "kernel": frag, "dispatches_per_pass": n,
+        "mean_dispatch_us_under_counters": round(dur / 1e3, 2) if dur else None,
+        "counters": {k: round(v, 1) for k, v in sorted(raw.items())},
+        "copy_calibration": {"fetch_factor": round(fetch_factor, 3), "write_factor": round(write_factor, 3),
+                             "lds_read_fetch_factor": (round(copy_bytes / (calib["LDS_FETCH_SIZE"] * 1024.0), 3)
+                                                       if calib.get("LDS_FETCH_SIZE") else None)},
+        "fetch_kib": round(raw["FETCH_SIZE"], 1), "write_kib": round(raw["WRITE_SIZE"], 1),
+        "traffic_bytes": round(fetched + written),
+        "attention_sha256": attention_source_sha256(),
+        "commands": cmds,
+    }
+    if args.workload not in DECODER_WORKLOADS and args.workload not in MX_WORKLOADS:
+        w = synth.get_workload(args.workload)
+        res["algorithmic_bytes"] = round(attention_bytes(w))
+        res["traffic_ratio"] = round((fetched + written) / attention_bytes(w), 3)
+    if gui > 0 and dur:
+        res["clock_ghz_from_gui_active"] = round(gui / dur, 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in raw:
+            res["mfma_busy_frac"] = round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024.0), 4)
+    if raw.get("SQ_INSTS_MFMA"):
+        res["valu_per_mfma"] = round(raw["SQ_INSTS_VALU"] / raw["SQ_INSTS_MFMA"], 3)
+        res["lds_insts_per_mfma"] = round(raw.get("SQ_INSTS_LDS", 0.0) / raw["SQ_INSTS_MFMA"], 3)
+    if raw.get("SQ_WAVE_CYCLES"):
+        res["wait_any_frac"] = round(raw.get("SQ_WAIT_ANY", 0.0) / raw["SQ_WAVE_CYCLES"], 4)
+    if raw.get("TCC_HIT_sum") is not None and raw.get("TCC_MISS_sum") is not None:
+        res["l2_hit_frac"] = round(raw["TCC_HIT_sum"] / max(raw["TCC_HIT_sum"] + raw["TCC_MISS_sum"], 1.0), 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -937,12 +1064,17 @@ def main():
                     help="also run a 256 MiB device copy (reference for the profiler's byte counters)")
     ap.add_argument("--traffic-kib", type=float, default=None,
                     help="override: scaled KiB per attention launch from rocprofv3 FETCH/WRITE runs")
+    ap.add_argument("--counters", action="store_true",
+                    help="instead of timing: run rocprofv3 counter passes of this workload (traffic, MFMA busy, "
+                         "instruction mix, LDS, L2) as child runs and print their per-dispatch means as JSON")
+    ap.add_argument("--counters-dir", default="gpurun_out/counters", help="--counters: where rocprofv3 writes")
+    ap.add_argument("--counters-timeout", type=float, default=240.0, help="--counters: seconds per pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU: the multi-GPU path is not implemented",
                           "n_gpus": args.gpus}))
         raise SystemExit(2)
-    res = run(args)
+    res = run_counters(args) if args.counters else run(args)
     print(json.dumps(res), flush=True)
 
 

@@ -124,6 +124,7 @@ def load():
         "sr_windows_attention": [P, I32, P, P, P, F32, P],
         "sr_global_attention": [P, I32, P, I32, P, P, F32, P],
         "sr_probe_mfma_bf16": [P, I32, I32, P],
+        "sr_probe_lds_read": [P, I64, P, P],
         "sr_global_attention_static": [P, I32, P, I32, P, P, F32, P],
     }
     for name, args in sig.items():
@@ -237,6 +238,15 @@ def sr_probe_mfma_bf16(out, workgroups, iters, stream=None):
     if out.numel() < workgroups * 512:
         raise ValueError("out holds fewer than workgroups * 512 floats")
     _check(load().sr_probe_mfma_bf16(_ptr(out), workgroups, iters, _stream(stream)))
+
+
+def sr_probe_lds_read(src, out, stream=None):
+    """Global-to-LDS read probe over the bytes of device tensor src (a multiple of 64 KiB); out a
+    device float tensor of >= src bytes / 256 elements."""
+    nbytes = src.numel() * src.element_size()
+    if out.numel() < nbytes // 256:
+        raise ValueError("out holds fewer than bytes / 256 floats")
+    _check(load().sr_probe_lds_read(_ptr(src), nbytes, _ptr(out), _stream(stream)))
 
 
 def sr_window_layout_check(cfg, layout):

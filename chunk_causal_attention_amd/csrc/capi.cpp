@@ -481,6 +481,15 @@ sr_status sr_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, void
   return device_status(sr::launch_mfma_probe(out, workgroups, iters, static_cast<hipStream_t>(stream)), "mfma probe");
 }
 
+sr_status sr_probe_lds_read(const void* src, int64_t bytes, float* out, void* stream) {
+  sr::clear_error();
+  if (!src || !out) return sr::fail(SR_E_INVALID, "null buffer");
+  if (bytes <= 0 || bytes % sr::kLdsProbeBlock != 0 || bytes / sr::kLdsProbeBlock > (int64_t(1) << 24))
+    return sr::fail(SR_E_INVALID, "bytes %lld is not a positive multiple of %d up to 2^24 blocks",
+                    static_cast<long long>(bytes), sr::kLdsProbeBlock);
+  return device_status(sr::launch_lds_read_probe(src, bytes, out, static_cast<hipStream_t>(stream)), "lds probe");
+}
+
 sr_status sr_global_attention_static(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out,
                                      float* lse, float softmax_scale, void* stream) {
   sr::clear_error();

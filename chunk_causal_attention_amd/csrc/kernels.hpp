@@ -199,6 +199,13 @@ constexpr int32_t kProbeThreads = 512;
 constexpr int32_t kProbeChains = 4;
 hipError_t launch_mfma_probe(float* out, int32_t workgroups, int32_t iters, hipStream_t st);
 
+// Global-to-LDS read probe (probe.hip): reads `bytes` of src (a whole number of kLdsProbeBlock
+// blocks) once with global_load_lds_dwordx4, one block per workgroup of kLdsProbeThreads threads,
+// each thread writing one float to out.
+constexpr int32_t kLdsProbeBlock = 65536;
+constexpr int32_t kLdsProbeThreads = 256;
+hipError_t launch_lds_read_probe(const void* src, int64_t bytes, float* out, hipStream_t st);
+
 // Library-owned scratch of sr_global_attention_static (static_scratch.hip): records of the
 // split-K global-token kernel (at most kStaticRecordFloats floats: 4 MiB) and kStaticCounters
 // arrival counters.  Fills *ws with this device's copy (looked up, and its counters zeroed on

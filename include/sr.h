@@ -403,6 +403,15 @@ sr_status sr_kvcache_gather(const sr_kvcache* c, int32_t bank, void* k_out, void
  * workgroups outside [1, 2^20] or iters outside [1, 2^24]; SR_E_DEVICE for a launch failure. */
 sr_status sr_probe_mfma_bf16(float* out, int32_t workgroups, int32_t iters, void* stream);
 
+/* Measurement aid (not part of the attention path): reads `bytes` of src (device) once with the
+ * global-to-LDS 16-byte loads the attention kernel streams its cache pages with, one 64 KiB
+ * block per 256-thread workgroup, each thread writing one float to out (device, >= bytes / 256
+ * floats, owned by the caller).  Run beside a plain device copy under the profiler, it shows
+ * that the fetch counter counts these loads as it counts the copy's, so one scale factor serves
+ * both.  SR_E_INVALID for a null buffer or bytes not a positive multiple of 65536 (at most 2^24
+ * blocks); SR_E_DEVICE for a launch failure. */
+sr_status sr_probe_lds_read(const void* src, int64_t bytes, float* out, void* stream);
+
 /* The handle's ring state, for inspection (owned by the cache). */
 const sr_ring* sr_kvcache_ring(const sr_kvcache* c);
 

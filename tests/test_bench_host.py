@@ -70,3 +70,37 @@ def test_peaks():
     assert abs(bench.PEAK_BF16_TFLOPS - 256 * 4096 * 2.4e9 / 1e12) < 0.1
     assert abs(bench.PEAK_MX_TFLOPS - 2.0 / (1.0 / 10100.0 + 1.0 / 5000.0)) < 0.1
     assert bench.PEAK_HBM_GBS == 8000.0 and np.isclose(bench.PEAK_F32_TFLOPS, 157.3)
+
+
+def test_attention_bytes_by_hand():
+    """c1: Q and O (4680 x 24 x 128 bf16 each) once, K and V of the 16112 visible keys once."""
+    w = synth.get_workload("c1")
+    assert bench.attention_bytes(w) == 2 * 24 * 128 * (2 * 4680 + 2 * 16112)
+    assert abs(bench.attention_bytes(w) / 1e6 - 255.5) < 0.1
+
+
+def test_counter_csv_means(tmp_path):
+    """--counters averages each counter over the dispatches of the named kernel only, and the
+    dispatch durations from the timestamps."""
+    head = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id","Grid_Size","Kernel_Id",'
+            '"Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count","Accum_VGPR_Count","SGPR_Count",'
+            '"Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
+    rows = [(1, "void sr::chunk_attention_kernel<G>(A)", "FETCH_SIZE", 100.0, 1000, 3000),
+            (2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 131072.0, 5000, 6000),
+            (3, "void sr::chunk_attention_kernel<G>(A)", "FETCH_SIZE", 300.0, 7000, 11000)]
+    p = tmp_path / "p_counter_collection.csv"
+    p.write_text(head + "\n" + "\n".join(
+        f'{d},{d},"Agent 1",1,1,1,1,1,"{k}",512,0,0,0,0,0,"{c}",{v},{s},{e}' for d, k, c, v, s, e in rows) + "\n")
+    means, dur, n = bench._counter_means(str(p), "chunk_attention_kernel")
+    assert means == {"FETCH_SIZE": 200.0} and dur == 3000.0 and n == 2
+    means, dur, n = bench._counter_means(str(p), bench.COPY_KERNEL)
+    assert means == {"FETCH_SIZE": 131072.0} and n == 1
+
+
+def test_counter_passes_fit_the_hardware():
+    """Each pass holds at most 8 SQ, 4 TCC (FETCH_SIZE uses 3, WRITE_SIZE 2) and 2 GRBM counters."""
+    tcc_cost = {"FETCH_SIZE": 3, "WRITE_SIZE": 2}
+    for name, ctrs in bench.COUNTER_PASSES:
+        assert sum(c.startswith("SQ_") for c in ctrs) <= 8, name
+        assert sum(tcc_cost.get(c, 1) for c in ctrs if c.startswith("TCC_") or c in tcc_cost) <= 4, name
+        assert sum(c.startswith("GRBM_") for c in ctrs) <= 2, name

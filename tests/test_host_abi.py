@@ -180,6 +180,19 @@ def test_init_validation_before_device_work(sr):
     assert lib.sr_kvcache_destroy(None) == 0
 
 
+def test_probe_validation_before_device_work(sr):
+    """The measurement probes refuse bad arguments on the host, before any launch."""
+    lib = sr.load()
+    P = ctypes.c_void_p
+    assert lib.sr_probe_mfma_bf16(None, 1, 1, None) == 1
+    assert lib.sr_probe_mfma_bf16(P(4096), 0, 1, None) == 1
+    assert lib.sr_probe_mfma_bf16(P(4096), 1, 0, None) == 1
+    assert lib.sr_probe_lds_read(None, 65536, P(4096), None) == 1
+    assert lib.sr_probe_lds_read(P(4096), 65536, None, None) == 1
+    for nbytes in (0, -65536, 65536 + 16, (1 << 24) * 65536 + 65536):
+        assert lib.sr_probe_lds_read(P(4096), nbytes, P(4096), None) == 1, nbytes
+
+
 def _ring_vs_model(sr, W, P, banks, cap, seed, n_ops=600):
     r = np.random.default_rng(seed)
     cfg = sr.config_for(1, 64, P, cap, W, None, banks, sr.SR_F32)
