@@ -973,7 +973,7 @@ def run_counters(args):
     if args.no_split:
         child.append("--no-split")
     env = dict(os.environ, TMPDIR="/tmp")
-    frag = dominant_kernel(args.workload)
+    frag = args.counters_kernel or dominant_kernel(args.workload)
     raw, dur, calib, cmds = {}, None, {}, []
     for name, ctrs in COUNTER_PASSES:
         cmd = ["rocprofv3", "--pmc"] + ctrs + ["--output-format", "csv", "-d", os.path.join(out_dir, name),
@@ -1019,7 +1019,8 @@ def run_counters(args):
         "attention_sha256": attention_source_sha256(),
         "commands": cmds,
     }
-    if args.workload not in DECODER_WORKLOADS and args.workload not in MX_WORKLOADS:
+    if frag == dominant_kernel(args.workload) and args.workload not in DECODER_WORKLOADS + ("c1w",) \
+            and args.workload not in MX_WORKLOADS:
         w = synth.get_workload(args.workload)
         res["algorithmic_bytes"] = round(attention_bytes(w))
         res["traffic_ratio"] = round((fetched + written) / attention_bytes(w), 3)
@@ -1069,6 +1070,8 @@ def main():
                          "instruction mix, LDS, L2) as child runs and print their per-dispatch means as JSON")
     ap.add_argument("--counters-dir", default="gpurun_out/counters", help="--counters: where rocprofv3 writes")
     ap.add_argument("--counters-timeout", type=float, default=240.0, help="--counters: seconds per pass")
+    ap.add_argument("--counters-kernel", default=None,
+                    help="--counters: name fragment of the kernel to report (default: the workload's attention kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU: the multi-GPU path is not implemented",
