@@ -60,17 +60,17 @@ MX_WORKLOADS = {"c1x": "c1"}
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 220806.4, "write_kib": 103851.7,
-           "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
-    "c1p": {"fetch_kib": 222259.8, "write_kib": 103827.6,
-            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
-    "c1w": {"fetch_kib": 320252.2, "write_kib": 125268.2,
-            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
-    "c1x": {"fetch_kib": 106744.0, "write_kib": 146810.5,
-            "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
+    "c1": {"fetch_kib": 286842.4, "write_kib": 91774.2,
+           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
+    "c3": {"fetch_kib": 1181028.6, "write_kib": 119961.0,
+           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
+    "c1w": {"fetch_kib": 332530.2, "write_kib": 106281.1,
+            "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
+    "c1x": {"fetch_kib": 146990.8, "write_kib": 125664.4,
+            "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
     # the decoder layer's dominant kernel: windows_attention_kernel
-    "d1": {"fetch_kib": 115755.9, "write_kib": 32166.4,
-           "attention_sha256": "b9f2cecc9136be7152f88bd1e25e829693f15c58e14b9cb5d69b6cc7c732c26a"},
+    "d1": {"fetch_kib": 115264.1, "write_kib": 31084.0,
+           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
@@ -549,8 +549,8 @@ def global_bytes(w):
 
 # Bytes past L2 per launch of the few-row split-K kernel (few_attention_kernel), as TRAFFIC.
 FEW_TRAFFIC = {
-    "d1": {"fetch_kib": 30546.9, "write_kib": 1307.5,
-           "few_sha256": "fa20788a3e2c7f86260e946df07eb20baa138bd197b344c81f48a9827915d382"},
+    "d1": {"fetch_kib": 30548.6, "write_kib": 1307.4,
+           "few_sha256": "2ea6211328f5d548a20b653284e8886942e4d94d45839d22f16a2caecd9d5dad"},
 }
 FEW_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "few_attention.hip")
 
