@@ -173,7 +173,9 @@ struct AttnArgs {
   WinView win;                              // window mode (win.n > 0): see WinView
   int32_t q_first[8], q_whole[8], q_left[8];  // split: each XCD's first item, whole items, split items
   int32_t q_share[8];                         // split: each XCD's split tiles per compute unit
-  int16_t left_tiles[8][kMaxCusPerXcd];       // split: key tiles of each XCD's split items
+  int32_t q_split0[9];                        // split: split items of the XCDs before x (q_split0[8]: all)
+  int32_t q_levels;                           // split: most pieces of a split item
+  alignas(4) int16_t left_tiles[8][kMaxCusPerXcd];  // split: key tiles of each XCD's split items
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
@@ -203,9 +205,10 @@ struct Geo {
     Op op[QB][KSTEPS];  // query operands, resident for the whole piece
   };
   static_assert(BN == 2 * SUB && SUB % 32 == 0, "a tile is two sub-tiles");
-  static constexpr int RPL = QB * (NDB * 16 + 4);  // record floats per lane: O^T, max, sum, 2 pad
-  static constexpr int REC = NW * 64 * RPL;        // record floats per workgroup
   static constexpr bool REC16 = ES == 2;           // O^T kept as bf16 in the record (bf16 caches)
+  static constexpr int RPL = 2 * kRecordWordsPerLane;  // record floats per lane: O^T, (max, sum)
+  static constexpr int REC = NW * 64 * RPL;            // record floats per workgroup
+  static_assert(QB * (NDB * (REC16 ? 4 : 8) + 1) <= kRecordWordsPerLane, "record fits its slot");
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
 };
 
@@ -229,7 +232,7 @@ struct GeoMx {
   static constexpr int TABLE = VBASE + 2 * VPAGE;
   static constexpr int LIMS = TABLE + kMaxTiles * 16;  // per-lane causal limits (int), read on partial tiles
   static constexpr int LDS_BYTES = LIMS + NW * 64 * 4;
-  static constexpr int RPL = QB * (NDB * 16 + 4);
+  static constexpr int RPL = 2 * kRecordWordsPerLane;
   static constexpr int REC = NW * 64 * RPL;
   static constexpr bool REC16 = true;
   static_assert(BM == kQueryTile && REC == attn_record_floats(D), "record layout shared with the host");
@@ -245,31 +248,40 @@ struct GeoMx {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// One 16-byte global-to-LDS load per lane: lane i's 16 bytes at `g` land at LDS byte
-// lds_base + 16 * i.  Issued as inline asm so the compiler's wait-count insertion does not
-// treat every later LDS read as dependent on it (it cannot tell the page buffers apart);
-// the kernel orders these loads itself with explicit vmcnt waits and barriers.  M0 is
-// written here and used by nothing else in this kernel (it is a reserved register that the
-// compiler only sets right before instructions that read it).  The LDS-DMA load reads M0, and a
-// scalar write of M0 needs one wait state before such a read (the compiler cannot insert it
-// inside the asm block), hence the s_nop.
-__device__ __forceinline__ void lds_load16(const void* g, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+// One 16-byte global-to-LDS load per lane: lane i's 16 bytes at `block` + lane_off land at
+// LDS byte lds_base + 16 * i (lane_off = 16 i).  The block address is uniform and goes in a
+// scalar register pair, the lane's offset in one vector register, so a page's loads hold no
+// 64-bit vector addresses across the key loop.  Issued as inline asm so the compiler's
+// wait-count insertion does not treat every later LDS read as dependent on it (it cannot tell
+// the page buffers apart); the kernel orders these loads itself with explicit vmcnt waits and
+// barriers.  M0 is written here and used by nothing else in this kernel (it is a reserved
+// register that the compiler only sets right before instructions that read it).  The LDS-DMA
+// load reads M0, and a scalar write of M0 needs one wait state before such a read (the
+// compiler cannot insert it inside the asm block), hence the s_nop.
+__device__ __forceinline__ void lds_load16(const char* block, int lane_off, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(lane_off),
+               "s"(block)
+               : "memory");
 }
 
 // Issues the global-to-LDS loads of one page of BYTES bytes (`src` = its first byte) into
-// `dst`: a contiguous copy; load j of wave w moves 1 KiB block (j*NW + w), lane i its piece
-// i.  BYTES is a whole number of KiB, so a wave loads whole blocks or none (the last round
-// may leave waves out).
+// `dst`: a contiguous copy by the first NI = NW / 2 waves; load j of wave w < NI moves 1 KiB
+// block (j*NI + w), lane i its piece i.  BYTES is a whole number of KiB, so a wave loads
+// whole blocks or none (the last round may leave waves out).  Waves w and w + NW/2 share a
+// SIMD, and the first (older) one wins the matrix unit's arbitration and reaches the page
+// barrier first; giving it the loads evens out the time the two need per page (measured 0.7%
+// faster than spreading them over all waves, 0.5% slower when the other half issues them).
 template <int BYTES, int NW>
 __device__ __forceinline__ void issue_bytes(const char* src, char* dst, int wave, int lane) {
   static_assert(BYTES % 1024 == 0, "pages are copied in 1 KiB blocks");
   constexpr int BLOCKS = BYTES / 1024;
+  constexpr int NI = NW / 2;
+  if (wave >= NI) return;
   const unsigned base = unsigned(size_t((lds_ptr_t)dst));
 #pragma unroll
-  for (int j = 0; j < (BLOCKS + NW - 1) / NW; ++j) {
-    const int b = j * NW + wave;
-    if ((j + 1) * NW <= BLOCKS || b < BLOCKS) lds_load16(src + b * 1024 + lane * 16, uniform(int(base) + b * 1024));
+  for (int j = 0; j < (BLOCKS + NI - 1) / NI; ++j) {
+    const int b = j * NI + wave;
+    if ((j + 1) * NI <= BLOCKS || b < BLOCKS) lds_load16(src + b * 1024, lane * 16, uniform(int(base) + b * 1024));
   }
 }
 template <class G>
@@ -488,8 +500,9 @@ __device__ __forceinline__ void prob(const Scores<G>& sc, Probs<G>& pop, float (
 // (one per MFMA) in the shadow of its MFMAs.  LOADED: the ring already holds the first AH V
 // operands (read during the previous block B); else they are read here.  SOFTMAX: false for
 // the closing step (no sub-tile i).  With SOFTMAX, the last AH regions also read the first AH
-// score operands of sub-tile i+1 (block B) into the ring.
-template <class G, bool LOADED, bool SOFTMAX>
+// score operands of sub-tile i+1 (block B) into the ring, unless LAST (i is the piece's last
+// sub-tile: there is no sub-tile i+1).
+template <class G, bool LOADED, bool SOFTMAX, bool LAST = false>
 __device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, Probs<G>& pop, float (&lpart)[2],
                                         float sl2, float mneg, const char* vpage, int vsub, const char* kpage,
                                         int ksub, typename G::Op (&ring)[AH], int c, int hl) {
@@ -511,7 +524,7 @@ __device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, Pr
     st.acc[0][db] = M::mma(ring[r % AH], pop[kb][0][kq], st.acc[0][db]);
     if (r + AH < NP)
       ring[r % AH] = pv_operand<G>(vpage, vsub, r + AH, c, hl);
-    else if (SOFTMAX)
+    else if (SOFTMAX && !LAST)
       ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH - NP, c, hl);
     if constexpr (SOFTMAX) {
 #pragma unroll
@@ -524,8 +537,9 @@ __device__ __forceinline__ void block_a(RowState<G>& st, const Scores<G>& sc, Pr
 // Block B: S^T = K Q^T of sub-tile i+1 alongside the second half of sub-tile i's
 // probabilities.  The ring holds the first AH score operands on entry.  NEXT_V: the last AH
 // regions read the first AH V operands of the next block A (half `vsub_next` of the V page at
-// `vnext`) into the ring.
-template <class G, bool NEXT_V>
+// `vnext`) into the ring.  LAST: sub-tile i is the piece's last, so there are no scores to
+// compute (and no score operands in the ring), only the probabilities and the V operands.
+template <class G, bool NEXT_V, bool LAST = false>
 __device__ __forceinline__ void block_b(const Scores<G>& sc, Probs<G>& pop, float (&lpart)[2], Scores<G>& sn,
                                         const typename G::Op (&qop)[1][G::KSTEPS], const char* kpage, int ksub,
                                         const char* vnext, int vsub_next, typename G::Op (&ring)[AH], float sl2,
@@ -534,15 +548,18 @@ __device__ __forceinline__ void block_b(const Scores<G>& sc, Probs<G>& pop, floa
   constexpr int NS = G::KSTEPS * G::NKB;
   static_assert(NS % AH == 0, "ring slots must line up across blocks");
   constexpr int NE = 16 * G::NKB, EA = NE / 2, NB = NE - EA;
+  if constexpr (!LAST) {
 #pragma unroll
-  for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
+    for (int kb = 0; kb < G::NKB; ++kb) sn[kb][0] = f32x16_t{};
+  }
   float grp[8];
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
-    const int ks = r / G::NKB, kb = r % G::NKB;
-    sn[kb][0] = M::mma(ring[r % AH], qop[0][ks], sn[kb][0]);
-    if (r + AH < NS)
-      ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH, c, hl);
+    [[maybe_unused]] const int ks = r / G::NKB, kb = r % G::NKB;
+    if constexpr (!LAST) sn[kb][0] = M::mma(ring[r % AH], qop[0][ks], sn[kb][0]);
+    if (r + AH < NS) {
+      if constexpr (!LAST) ring[r % AH] = qk_operand<G>(kpage, ksub, r + AH, c, hl);
+    }
     else if (NEXT_V)
       ring[r % AH] = pv_operand<G>(vnext, vsub_next, r + AH - NS, c, hl);
 #pragma unroll
@@ -593,9 +610,9 @@ __device__ __forceinline__ int for_each_subpiece(const AttnArgs& a, const SplitI
     for (int q = 0; q < it.fan; ++q) f(it.slot0 + q);
     return it.fan;
   }
-  const int base = it.x * 4 * C + kSplitPieces * it.r;
+  const int base = (it.x * C + it.r) * kMaxPieces;
   int n = 0;
-  for (int k = 0; k < kSplitPieces; ++k) {
+  for (int k = 0; k < kMaxPieces; ++k) {
     if (piece_begin(it.tiles, it.share, k + 1) > piece_begin(it.tiles, it.share, k)) {
       f(base + k);
       ++n;
@@ -726,7 +743,7 @@ __device__ __forceinline__ void merge_records(const AttnArgs& a, RowState<G>& st
 struct NoWork {
   __device__ void operator()() const {}
 };
-template <class G, int ODD, bool CLOSING = false, class Mid = NoWork>
+template <class G, int ODD, bool CLOSING = false, bool LAST = false, class Mid = NoWork>
 __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const int (&lim_cur)[G::QB], char* smem,
                                          RowState<G>& st, Scores<G>& sc, Scores<G>& sn, Probs<G>& pop,
                                          const typename G::Op (&qop)[G::QB][G::KSTEPS], typename G::Op (&ring)[AH],
@@ -749,12 +766,12 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
   if constexpr (G::ES == 2 && G::QB == 1) {
     float lpart[2] = {0.0f, 0.0f};
     const float mneg = -st.m[0];
-    block_a<G, !ODD, !CLOSING>(st, sc, pop, lpart, sl2, mneg, vpage, NEXT, kpage, NEXT, ring, c, hl);
+    block_a<G, !ODD, !CLOSING, LAST>(st, sc, pop, lpart, sl2, mneg, vpage, NEXT, kpage, NEXT, ring, c, hl);
     if (CLOSING) return;  // nothing follows the last sub-tile's P.V
     mid();
     // Odd i: the next iteration's P.V reads sub-tile i, the second half of V page i / 2.
     const char* vnext = smem + G::VBASE + ((i >> 1) & 1) * G::VPAGE;
-    block_b<G, ODD == 1>(sc, pop, lpart, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, mneg, c, hl);
+    block_b<G, ODD == 1, LAST>(sc, pop, lpart, sn, qop, kpage, NEXT, vnext, 1, ring, sl2, mneg, c, hl);
     float lsum = lpart[0] + lpart[1];
     // Some probability of the sub-tile may exceed 2^kSumLimit: take its row max (rare).
     if (__any(!(lsum <= kSumLimit))) lsum = rescale_and_redo<G>(st, sc, pop, sl2);
@@ -765,7 +782,7 @@ __device__ __forceinline__ void key_step(int i, const int4& ent, int nsub, const
     row_max<G>(sc, rmax);
     rescale<G>(st, rmax, sl2);
     mid();
-    scores<G>(sn, qop, kpage, NEXT, c, hl);
+    if constexpr (!LAST) scores<G>(sn, qop, kpage, NEXT, c, hl);
     softmax_exp<G>(st, sc, pop, sl2);
   }
 }
@@ -1180,12 +1197,77 @@ __device__ __forceinline__ int tile_page_index(const AttnArgs& a, int win, int t
   return uniform(seg_page(a, win, s) + (t - first));
 }
 
-// One piece of work: query tile qt of head h over tiles [tb, te) of its tile list.  slot < 0:
-// the whole list (write the output); else a sub-piece of split item `it` (record `slot`).
-// win >= 0: window mode, the rows and keys of that window (WinView).
+// A unit of work: query tile qt of head h over tiles [tb, te) of its tile list; slot < 0:
+// the whole list (the unit writes the output), else a piece of split item `it` (record
+// `slot`).
+struct Unit {
+  int h = 0, qt = 0, tb = 0, te = 0, slot = -1;
+  SplitItem it{};
+};
+
+// Whole item u of XCD x's queue.
+__device__ __forceinline__ Unit whole_unit(const AttnArgs& a, int x, int u) {
+  Unit un;
+  const int item = a.q_first[x] + u;
+  un.h = uniform(item / a.q_tiles);
+  un.qt = uniform(item - un.h * a.q_tiles);
+  un.te = uniform(item_tiles(un.qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
+  return un;
+}
+
+// Piece k of split item r of XCD x.  False for an empty piece of a short item (no work, no
+// record).
+__device__ __forceinline__ bool piece_unit(const AttnArgs& a, int x, int r, int k, Unit& un) {
+  const int C = a.cus_per_xcd;
+  // A dword-aligned read of the tile counts keeps the load scalar.
+  const int pair = reinterpret_cast<const int32_t*>(a.left_tiles[x])[r >> 1];
+  const int T = uniform((pair << (16 * (1 - (r & 1)))) >> 16);
+  const int share = a.q_share[x];
+  un = Unit{};
+  un.tb = uniform(piece_begin(T, share, k));
+  un.te = uniform(piece_begin(T, share, k + 1));
+  const int item = a.q_first[x] + a.q_whole[x] + r;
+  un.h = uniform(item / a.q_tiles);
+  un.qt = uniform(item - un.h * a.q_tiles);
+  if (un.te <= un.tb) return false;
+  if (split_pieces(T, share) > 1) {
+    un.slot = (x * C + r) * kMaxPieces + k;
+    un.it.x = x;
+    un.it.r = r;
+    un.it.tiles = T;
+    un.it.share = share;
+  } else {
+    un.tb = 0;
+    un.te = T;
+  }
+  return true;
+}
+
+// Unit u of XCD x's queue: its whole items, then piece 0 of each of its split items.
+__device__ __forceinline__ bool xcd_unit(const AttnArgs& a, int x, int u, Unit& un) {
+  if (u < a.q_whole[x]) {
+    un = whole_unit(a, x, u);
+    return true;
+  }
+  return piece_unit(a, x, uniform(u - a.q_whole[x]), 0, un);
+}
+
+// Unit v of the device's piece queue: piece k = 1 + v / S of split item j = v % S, the S split
+// items of all XCDs in XCD order.
+__device__ __forceinline__ bool device_unit(const AttnArgs& a, int v, Unit& un) {
+  const int S = a.q_split0[8];
+  const int k = uniform(1 + v / S), j = uniform(v - (v / S) * S);
+  int x = 0;
+  while (x < 7 && j >= a.q_split0[x + 1]) ++x;
+  x = uniform(x);
+  return piece_unit(a, x, uniform(j - a.q_split0[x]), k, un);
+}
+
+// One unit of work (Unit).  win >= 0: window mode, the rows and keys of that window (WinView).
 template <class G>
-__device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* flag, int h, int qt, int tb, int te,
-                                          int slot, const SplitItem& it, int win = -1) {
+__device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* flag, const Unit& un, int win) {
+  const int h = un.h, qt = un.qt, tb = un.tb, te = un.te, slot = un.slot;
+  const SplitItem& it = un.it;
   using M = typename G::M;
   using Op = typename G::Op;
   using T = typename G::Elem;
@@ -1316,22 +1398,30 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   // The table entries for tile t+1 and the page index of tile t+2 are read at the end of
   // iteration 2t, where the barrier waits for all LDS reads anyway (read earlier, they would
   // make the wave wait for the operand reads queued behind them).
-  for (int t = 0; t < ntiles; ++t) {  // ent: table entry of tile t
+  for (int t = 0; t + 1 < ntiles; ++t) {  // ent: table entry of tile t
     key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
-    const int4 ent_next = tab[min(t + 1, ntiles - 1)];
+    const int4 ent_next = tab[t + 1];
     const int kpage_next = tab[min(t + 2, ntiles - 1)].x;  // K of tile t+2, requested at 2t+1
     const int vpage_next = ent_next.x;                     // V of tile t+1, requested at 2t+1
     if (t >= 1) wait_loads<0>();
     __syncthreads();
-    if (t + 1 < ntiles)
-      issue_v<G>(a.vpool + (head_page + uniform(vpage_next)) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE,
-                 wave, lane);
+    issue_v<G>(a.vpool + (head_page + uniform(vpage_next)) * G::VPAGE, smem + G::VBASE + ((t + 1) & 1) * G::VPAGE,
+               wave, lane);
     const auto request_k = [&] {
       if (t + 2 < ntiles)
         issue_k<G>(a.kpool + (head_page + uniform(kpage_next)) * G::KPAGE, smem + (t & 1) * G::KPAGE, wave, lane);
     };
     key_step<G, 1>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, ring, sl2, c, hl, request_k);
     ent = ent_next;
+  }
+  {
+    // The last page, t = ntiles - 1: no pages to request and, in its odd iteration, no scores
+    // of a next sub-tile.
+    const int t = ntiles - 1;
+    key_step<G, 0>(2 * t, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
+    if (t >= 1) wait_loads<0>();
+    __syncthreads();
+    key_step<G, 1, false, true>(2 * t + 1, ent, nsub, lim_cur, smem, st, sc_odd, sc, pop, qop, ring, sl2, c, hl);
   }
   key_step<G, 0, true>(nsub, ent, nsub, lim_cur, smem, st, sc, sc_odd, pop, qop, ring, sl2, c, hl);
   }
@@ -1380,23 +1470,38 @@ __device__ __forceinline__ void run_piece(const AttnArgs& a, char* smem, int* fl
   }
 }
 
-// The queue split (kernels.hpp): a persistent workgroup takes units from its XCD's queue, then
-// from the other XCDs' queues, until every queue is empty; the last workgroup to finish zeroes
-// the queue counters for the next call.  Thread 0 claims a unit and hands it to the
-// workgroup through LDS; the claim loop ends for every workgroup, since each counter only
-// grows and each workgroup gives up on a queue once it is past its end.
+// A unit given by its fields.
+template <class G>
+__device__ __forceinline__ void run_unit(const AttnArgs& a, char* smem, int* flag, int h, int qt, int tb, int te,
+                                         int slot, const SplitItem& it, int win = -1) {
+  Unit un;
+  un.h = h;
+  un.qt = qt;
+  un.tb = tb;
+  un.te = te;
+  un.slot = slot;
+  un.it = it;
+  run_piece<G>(a, smem, flag, un, win);
+}
+
+// The queue split (kernels.hpp): a persistent workgroup takes whole items from its XCD's queue,
+// then from the other XCDs' queues, then units of the device's piece queue, until all are
+// empty; the last workgroup to finish zeroes the counters for the next call.  Thread 0 claims a
+// unit and hands it to the workgroup through LDS; the claim loop ends for every workgroup,
+// since each counter only grows and a workgroup gives up on a queue once it is past its end.
 template <class G>
 __device__ __forceinline__ void queue_split(const AttnArgs& a, char* smem, int* flag, int* claim, int home) {
-  const int C = a.cus_per_xcd;
-  int y = home, passed = 0;  // thread 0: the queue it claims from, queues found empty
+  const int dev_units = (a.q_levels - 1) * a.q_split0[8];  // units of the device's piece queue
+  int y = home, passed = 0;  // thread 0: the XCD queue it claims from, XCD queues found empty
   for (;;) {
     if (threadIdx.x == 0) {
-      int u = -1;
+      int kind = -1, u = -1;
       while (passed < 8) {
-        const int units = a.q_whole[y] + kSplitPieces * a.q_left[y];
+        const int units = a.q_whole[y] + a.q_left[y];
         if (units > 0) {
           const int v = __hip_atomic_fetch_add(a.qctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (v < units) {
+            kind = 0;
             u = v;
             break;
           }
@@ -1404,48 +1509,31 @@ __device__ __forceinline__ void queue_split(const AttnArgs& a, char* smem, int* 
         y = (y + 1) & 7;
         ++passed;
       }
-      claim[0] = y;
-      claim[1] = u;
+      if (kind < 0 && dev_units > 0) {
+        const int v = __hip_atomic_fetch_add(a.qctr + kPieceCounter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v < dev_units) {
+          kind = 1;
+          u = v;
+        }
+      }
+      claim[0] = kind;
+      claim[1] = y;
+      claim[2] = u;
     }
     __syncthreads();
-    const int x = uniform(claim[0]), u = uniform(claim[1]);
+    const int kind = uniform(claim[0]), x = uniform(claim[1]), u = uniform(claim[2]);
     __syncthreads();  // every thread has read the claim before thread 0 makes the next one
-    if (u < 0) break;
-    int h, qt, tb = 0, te, slot = -1;
-    SplitItem it{};
-    if (u < a.q_whole[x]) {
-      const int item = a.q_first[x] + u;
-      h = uniform(item / a.q_tiles);
-      qt = uniform(item - h * a.q_tiles);
-      te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
-    } else {
-      const int v = u - a.q_whole[x], left = a.q_left[x];
-      const int k = v / left, r = v - k * left;
-      const int T = a.left_tiles[x][r];
-      const int share = a.q_share[x];
-      tb = uniform(piece_begin(T, share, k));
-      te = uniform(piece_begin(T, share, k + 1));
-      const int item = a.q_first[x] + a.q_whole[x] + r;
-      h = uniform(item / a.q_tiles);
-      qt = uniform(item - h * a.q_tiles);
-      if (te <= tb) continue;  // an empty piece of a short item: no work, no record
-      if (split_pieces(T, share) > 1) {
-        slot = x * 4 * C + kSplitPieces * r + k;
-        it.x = x;
-        it.r = r;
-        it.tiles = T;
-        it.share = share;
-      } else {
-        tb = 0;
-        te = T;
-      }
-    }
-    run_piece<G>(a, smem, flag, h, qt, tb, te, slot, it);
+    if (kind < 0) break;
+    Unit un;
+    if (!(kind == 0 ? xcd_unit(a, x, u, un) : device_unit(a, u, un)))
+      continue;  // an empty piece of a short item: no work, no record
+    run_piece<G>(a, smem, flag, un, -1);
   }
   if (threadIdx.x == 0) {
-    const int done = __hip_atomic_fetch_add(a.qctr + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int done = __hip_atomic_fetch_add(a.qctr + kExitCounter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == a.num_wg - 1) {
-      for (int q = 0; q < 9; ++q) __hip_atomic_store(a.qctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 0; q < kQueueCounters; ++q)
+        __hip_atomic_store(a.qctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1454,7 +1542,7 @@ template <class G>
 __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(const AttnArgs a) {
   __shared__ __align__(1024) char smem[G::LDS_BYTES];
   __shared__ int flag;
-  __shared__ int claim[2];
+  __shared__ int claim[3];
 
   // Workgroups are dispatched round-robin over the 8 XCDs: hardware id i runs on XCD i % 8
   // as the (i / 8)-th workgroup of that XCD.  Integer divisions are expanded on the vector
@@ -1480,7 +1568,7 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
     it.fan = a.fan;
     it.slot0 = item * a.fan;
     it.ctr = item;
-    run_piece<G>(a, smem, &flag, h, qt, tb, te, item * a.fan + pc, it);
+    run_unit<G>(a, smem, &flag, h, qt, tb, te, item * a.fan + pc, it);
     return;
   }
   if (a.split) {
@@ -1494,7 +1582,7 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void chunk_attention_kernel(
   const int h = uniform(g / a.q_tiles);
   const int qt = uniform(g - h * a.q_tiles);
   const int te = uniform(item_tiles(qt, a.fixed_tiles, a.n_q, a.causal_block, a.t.s[a.t.n - 1].len));
-  run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{});
+  run_unit<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{});
 }
 
 // Window mode (a.win.n > 0): one workgroup per item (window, head, query tile), window-major
@@ -1520,7 +1608,7 @@ __global__ __launch_bounds__(G::NW * 64, G::NW / 4) void windows_attention_kerne
   int fixed = 0;
   for (int s = 0; s < a.t.n - 1; ++s) fixed += (seg_len(a, w, s) + G::BN - 1) / G::BN;
   const int te = uniform(item_tiles(qt, fixed, rows, 0, seg_len(a, w, a.t.n - 1)));
-  run_piece<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{}, w);
+  run_unit<G>(a, smem, &flag, h, qt, 0, te, -1, SplitItem{}, w);
 }
 
 template <class G>
@@ -1562,9 +1650,11 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
   if (a.fan > 0) {
     a.num_wg = a.n_items * a.fan;  // at most 8 C: records and counters fit the workspace
   } else if (a.split) {
-    // Queues: XCD x owns items [first, first + n); the last n mod C of them are split.  One
-    // persistent workgroup per compute unit.
+    // Queues: XCD x owns items [first, first + n); the last n mod C of them are split, their
+    // pieces in the device's piece queue.  One persistent workgroup per compute unit.
     const int32_t C = ws.cus_per_xcd;
+    a.q_levels = 0;
+    a.q_split0[0] = 0;
     for (int x = 0; x < 8; ++x) {
       const int32_t first = int32_t(int64_t(x) * a.n_items / 8);
       const int32_t n = int32_t(int64_t(x + 1) * a.n_items / 8) - first;
@@ -1578,6 +1668,11 @@ hipError_t launch_t(const Layout& L, const void* pool, const SegTable& t, int32_
         split_tiles += a.left_tiles[x][r];
       }
       a.q_share[x] = (split_tiles + C - 1) / C;
+      for (int32_t r = 0; r < a.q_left[x]; ++r) {
+        const int32_t np = split_pieces(a.left_tiles[x][r], a.q_share[x]);
+        a.q_levels = np > a.q_levels ? np : a.q_levels;
+      }
+      a.q_split0[x + 1] = a.q_split0[x] + a.q_left[x];
     }
     a.qctr = ws.counters + 8 * C;
     a.num_wg = 8 * C;

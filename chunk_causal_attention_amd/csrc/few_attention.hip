@@ -288,7 +288,7 @@ bool few_attention_shape_ok(const Layout& L, const SegTable& t, int32_t n_q) {
 
 bool few_attention_fits(const Layout& L, const SegTable& t, int32_t n_q, const SplitWorkspace& ws) {
   if (ws.cus_per_xcd <= 0 || !few_attention_shape_ok(L, t, n_q)) return false;
-  const int64_t have = int64_t(8) * 4 * ws.cus_per_xcd * attn_record_floats(L.D);
+  const int64_t have = int64_t(8) * kMaxPieces * ws.cus_per_xcd * attn_record_floats(L.D);  // the records area
   return L.H <= 8 * ws.cus_per_xcd && few_attention_record_floats(L, t, n_q) <= have;
 }
 

@@ -63,47 +63,59 @@ __host__ __device__ inline int32_t item_tiles(int32_t qt, int32_t fixed_tiles, i
   return fixed_tiles + (any + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
 }
 
-// Floats of one workgroup's partial result in the split schedule: per lane of the 8 waves,
-// the head_dim/2 output accumulators it holds plus its running max and sum, padded to
-// whole 16-byte chunks.
-__host__ __device__ constexpr int32_t attn_record_floats(int32_t head_dim) { return 8 * 64 * (head_dim / 2 + 4); }
+// Floats of one workgroup's partial result in the split schedule: per lane of the 8 waves, 17
+// eight-byte words: its output accumulators (head_dim 128 rounded to bf16, or head_dim 64 in
+// fp32 or bf16) and one (max, sum) pair.
+constexpr int32_t kRecordWordsPerLane = 17;
+__host__ __device__ constexpr int32_t attn_record_floats(int32_t /*head_dim*/) {
+  return 8 * 64 * 2 * kRecordWordsPerLane;
+}
 
 // Split schedule.  Workgroup i of a launch runs on XCD i % 8, and each XCD (own L2, C compute
 // units) owns a contiguous range of the head-major (head, query tile) items, so that the query
 // tiles of a head stream the same pages at about the same time and each page is fetched past
 // L2 about once per XCD.  The launch has one persistent workgroup per compute unit (8 C).  XCD
-// x keeps a queue of units: its items run whole, a multiple of C of them ("whole"), then the
-// key-tile pieces of its last `left` < C items ("split" items), which would otherwise leave
-// units idle in a final round.  Split item r of T tiles is cut into kSplitPieces pieces,
-// largest first (piece_begin), and the queue holds all items' piece 0,
-// then all pieces 1, and so on, so the queue ends in small pieces.  A workgroup takes the next
-// unit of its own XCD's queue through an atomic counter; once that queue is empty it takes
-// units from the other XCDs' queues in turn, so XCDs that run faster (they do, by several per
-// cent, depending on the data they stream) take over work of slower ones.  Piece k of split item
-// r leaves a partial record in slot x * 4C + 4r + k; the last piece of an item to finish merges
-// the item's records in slot order and writes its output, so the result does not depend on
-// which workgroup ran which piece.
+// x runs a multiple of C of its items whole ("whole" items); its last `left` < C items, which
+// would otherwise leave units idle in a final round, are cut into key-tile pieces ("split"
+// items).  XCD x's queue holds its whole items, then piece 0 of each of its split items (the
+// largest pieces, which stream the pages of heads the XCD's L2 already holds).  The later
+// pieces of all XCDs' split items form one queue for the device, every item's piece 1 first,
+// then every piece 2, and so on, so that the queue ends in the smallest pieces whichever XCD is
+// late.  A workgroup takes the next unit of its own XCD's queue through an atomic counter, then
+// of the other XCDs' queues, then of the device's piece queue.  (With all pieces in per-XCD
+// queues, an XCD that ran its whole items more slowly than the others, by several per cent
+// depending on the data it streams, took its own big pieces late and ended up to 120 us after
+// them; with all pieces in the device queue, the first pieces ran on other XCDs than the one
+// holding their pages, 0.7% slower on 456 items of 128 tiles.)  Piece k of split item r of XCD
+// x leaves a partial record in slot (x C + r) kMaxPieces + k; the last piece of an item to
+// finish merges the item's records in slot order and writes its output, so the result does not
+// depend on which workgroup ran which piece.
 constexpr int32_t kMaxCusPerXcd = 64;  // largest C (split items per XCD are fewer)
-constexpr int32_t kSplitPieces = 4;    // pieces of a split item (record slots 4r .. 4r + 3)
-constexpr int32_t kQueueCounters = 16; // per call: 8 queue counters, 1 exit counter, padding
+constexpr int32_t kMaxPieces = 8;      // pieces of a split item (record slots r kMaxPieces + k)
+constexpr int32_t kMinPiece = 8;       // key tiles below which the rest of an item is not halved
+constexpr int32_t kQueueCounters = 16; // per call: 8 whole-item queues, exit, piece queue, padding
+constexpr int32_t kExitCounter = 8, kPieceCounter = 9;
 
-// First key tile of piece k (0 .. kSplitPieces) of a split item of T tiles when the XCD's
-// split work is `share` tiles per compute unit: piece 0 takes 85% of the share (the largest
-// unit a unit can take without running past the others), the rest of the item is halved
-// twice (piece_begin(T, kSplitPieces) = T).  A piece may be empty for very short items; empty
-// pieces are skipped and leave no record.
+// First key tile of piece k (0 .. kMaxPieces) of a split item of T tiles when the XCD's split
+// work is `share` tiles per compute unit: piece 0 takes 85% of the share (the largest unit a
+// unit can take without running past the others), then each piece takes half of what is left
+// while that half is at least kMinPiece tiles, and the last piece takes the rest
+// (piece_begin(T, share, k) = T past the last piece).  Piece 0 may take the whole item.
 __host__ __device__ inline int32_t piece_begin(int32_t T, int32_t share, int32_t k) {
   if (k <= 0) return 0;
-  if (k >= kSplitPieces) return T;
-  int32_t p0 = share * 85 / 100;
-  p0 = p0 < 1 ? 1 : (p0 > T ? T : p0);
-  const int32_t rest = T - p0;
-  return k == 1 ? p0 : k == 2 ? p0 + rest / 2 : p0 + rest / 2 + rest / 4;
+  int32_t b = share * 85 / 100;
+  b = b < 1 ? 1 : (b > T ? T : b);
+  for (int32_t j = 1; j < k; ++j) {  // piece j starts at b
+    const int32_t half = (T - b) / 2;
+    if (half < kMinPiece || j == kMaxPieces - 1) return T;  // piece j is the last
+    b += half;
+  }
+  return b;
 }
 // Non-empty pieces of a split item of T tiles.
 __host__ __device__ inline int32_t split_pieces(int32_t T, int32_t share) {
   int32_t n = 0;
-  for (int32_t k = 0; k < kSplitPieces; ++k) n += piece_begin(T, share, k + 1) > piece_begin(T, share, k);
+  for (int32_t k = 0; k < kMaxPieces; ++k) n += piece_begin(T, share, k + 1) > piece_begin(T, share, k);
   return n;
 }
 
@@ -131,10 +143,10 @@ inline int32_t split_cus_per_xcd(int32_t num_cus) {
   return C < 1 ? 1 : (C > kMaxCusPerXcd ? kMaxCusPerXcd : C);
 }
 
-// Attention workspace: 8 XCDs x 4C records, then 8C arrival counters and the split schedule's
-// kQueueCounters queue counters (256-byte aligned).
+// Attention workspace: 8 XCDs x C x kMaxPieces records, then 8C arrival counters and the split
+// schedule's kQueueCounters queue counters (256-byte aligned).
 inline size_t attn_records_bytes(int32_t head_dim, int32_t num_cus) {
-  return size_t(8) * 4 * split_cus_per_xcd(num_cus) * attn_record_floats(head_dim) * sizeof(float);
+  return size_t(8) * kMaxPieces * split_cus_per_xcd(num_cus) * attn_record_floats(head_dim) * sizeof(float);
 }
 inline size_t attn_counters_bytes(int32_t num_cus) {
   return ((size_t(8) * split_cus_per_xcd(num_cus) + kQueueCounters) * sizeof(int32_t) + 255) & ~size_t(255);

@@ -267,18 +267,19 @@ sr_status sr_prefix_attention(sr_kvcache* c, int32_t bank, const void* q, void* 
  * each over that tile's whole key list, and the last round of workgroups can leave compute
  * units idle.  With a workspace attached, each of the device's 8 XCDs (C = compute units / 8,
  * at most 64) owns a share of the (head, query tile) items: it runs them whole, C at a time,
- * and cuts the key tiles of its last (< C) items into four pieces.  One persistent workgroup
- * per compute unit takes these units from its XCD's queue, then from the other XCDs' queues,
- * so that faster XCDs take over work of slower ones.  A piece of a split item leaves fp32
- * partial results (output, running max and sum per query) in the workspace, and the last of
- * the item's pieces to finish merges them in a fixed order and writes out / lse.  No
- * workgroup waits for another.  The kernel shape is tuned per device ("3.3 Inference
- * Acceleration and End-to-End Deployment", attention kernel tuning); this split is the MI355X
- * choice.
+ * and cuts the key tiles of its last (< C) items into up to eight pieces, largest first.  One
+ * persistent workgroup per compute unit takes whole items from its XCD's queue, then from the
+ * other XCDs' queues, then pieces from one queue for the device that holds every split item's
+ * first piece, then every second piece, and so on, so that the last units taken anywhere are
+ * the smallest.  A piece of a split item leaves its partial result (output, running max and
+ * sum per query; the output rounded to bf16 for bf16 and reduced-precision caches) in the
+ * workspace, and the last of the item's pieces to finish merges them in a fixed order and
+ * writes out / lse.  No workgroup waits for another.  The kernel shape is tuned per device
+ * ("3.3 Inference Acceleration and End-to-End Deployment", attention kernel tuning); this
+ * split is the MI355X choice.
  *
- * Layout: 32 C records of 8 x 64 x (head_dim / 2 + 4) floats, then 8 C int32 arrival
- * counters and 16 int32 queue counters (rounded up to 256 bytes).  The counters must be zero
- * when a call starts;
+ * Layout: 64 C records of 8 x 64 x 34 floats, then 8 C int32 arrival counters and 16 int32
+ * queue counters (rounded up to 256 bytes).  The counters must be zero when a call starts;
  * sr_kvcache_set_workspace zeroes them and every call leaves them zero.  Results with and
  * without a workspace agree within rounding (different summation order); with a workspace
  * they are bit-reproducible from call to call.

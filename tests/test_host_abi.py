@@ -114,12 +114,13 @@ def test_required_bytes_mx(sr, H, D, P, banks, cap, W):
 
 @pytest.mark.parametrize("H,D,cap,cus", [(24, 128, 4680, 256), (2, 64, 32, 8), (40, 128, 7200, 304), (3, 64, 1, 1)])
 def test_attention_workspace_bytes(sr, H, D, cap, cus):
-    """Per XCD (C = cus / 8 compute units, at least 1): 4C records of 8 waves x 64 lanes x
-    (D/2 output floats + max + sum + 2 pad floats: whole 16-byte chunks), then C int32 arrival
-    counters and 16 queue counters of the split schedule, padded to 256 bytes."""
+    """Per XCD (C = cus / 8 compute units, at least 1): up to 8 pieces of C split items, one
+    record each of 8 waves x 64 lanes x 17 eight-byte words (the output accumulators as bf16 at
+    head_dim 128 or fp32 at 64, and the running max and sum), then C int32 arrival counters and
+    16 queue counters of the split schedule, padded to 256 bytes."""
     cfg = sr.config_for(H, D, 0, cap, 1)
     C = max(cus // 8, 1)
-    assert sr.sr_attention_workspace_bytes(cfg, cus) == 8 * 4 * C * 512 * (D // 2 + 4) * 4 + -(-(8 * C + 16) * 4 // 256) * 256
+    assert sr.sr_attention_workspace_bytes(cfg, cus) == 8 * 8 * C * 512 * 17 * 8 + -(-(8 * C + 16) * 4 // 256) * 256
 
 
 def test_attention_workspace_bytes_validation(sr):
