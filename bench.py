@@ -60,17 +60,17 @@ MX_WORKLOADS = {"c1x": "c1"}
 # WRITE_SIZE).  Each entry holds the SHA-256 of the attention kernel source it was measured
 # on; the figure is reported only while that source is unchanged.
 TRAFFIC = {
-    "c1": {"fetch_kib": 286842.4, "write_kib": 91774.2,
-           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
-    "c3": {"fetch_kib": 1181028.6, "write_kib": 119961.0,
-           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
-    "c1w": {"fetch_kib": 332530.2, "write_kib": 106281.1,
-            "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
-    "c1x": {"fetch_kib": 146990.8, "write_kib": 125664.4,
-            "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
+    "c1": {"fetch_kib": 327292.3, "write_kib": 92316.6,
+           "attention_sha256": "bb1ab0dc1a53ce62094c5886dacc69e54838bc79bec8f7fefea6d55f9146c6e0"},
+    "c3": {"fetch_kib": 1234596.9, "write_kib": 139502.6,
+           "attention_sha256": "bb1ab0dc1a53ce62094c5886dacc69e54838bc79bec8f7fefea6d55f9146c6e0"},
+    "c1w": {"fetch_kib": 344903.0, "write_kib": 109618.2,
+            "attention_sha256": "bb1ab0dc1a53ce62094c5886dacc69e54838bc79bec8f7fefea6d55f9146c6e0"},
+    "c1x": {"fetch_kib": 179635.4, "write_kib": 125190.2,
+            "attention_sha256": "bb1ab0dc1a53ce62094c5886dacc69e54838bc79bec8f7fefea6d55f9146c6e0"},
     # the decoder layer's dominant kernel: windows_attention_kernel
-    "d1": {"fetch_kib": 115264.1, "write_kib": 31084.0,
-           "attention_sha256": "5c7a724f6407dfc31a27955c42ac098b1ee5f169fbe12f5311370bf3f575f7b0"},
+    "d1": {"fetch_kib": 115315.1, "write_kib": 31079.7,
+           "attention_sha256": "bb1ab0dc1a53ce62094c5886dacc69e54838bc79bec8f7fefea6d55f9146c6e0"},
 }
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
@@ -549,8 +549,8 @@ def global_bytes(w):
 
 # Bytes past L2 per launch of the few-row split-K kernel (few_attention_kernel), as TRAFFIC.
 FEW_TRAFFIC = {
-    "d1": {"fetch_kib": 30548.6, "write_kib": 1307.4,
-           "few_sha256": "2ea6211328f5d548a20b653284e8886942e4d94d45839d22f16a2caecd9d5dad"},
+    "d1": {"fetch_kib": 30548.7, "write_kib": 1307.5,
+           "few_sha256": "c47b5a7dee38b9a415ba41cfdfa833fc444d982db23737508d2b67378f3ea274"},
 }
 FEW_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "few_attention.hip")
 
