@@ -376,6 +376,23 @@ def test_degenerate_and_ragged_shapes(sr, case, schedule):
     _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, 31, chunks, SCHEDULES[schedule])
 
 
+# Queue split with more items than compute units, not a multiple of the 8 XCDs, so that the
+# XCDs own different item counts and different numbers of split items (none on some of them);
+# causal blocks inside the chunk give the items different tile counts, so split items have
+# different piece counts and some levels of the device queue hold empty pieces.
+QUEUE_EDGE = [  # H, D, P, cap, W, cb, dtype, chunks
+    ("308 items, causal blocks, D=128", 11, 128, 500, 7000, 1, 1000, "bf16", [7000, 7000]),
+    ("260 items, half the XCDs without split items, D=64", 20, 64, 0, 3300, 2, 3300, "bf16", [3300] * 3),
+]
+
+
+@pytest.mark.parametrize("case", QUEUE_EDGE, ids=[c[0] for c in QUEUE_EDGE])
+def test_queue_split_uneven_xcds(sr, case):
+    name, H, D, P, cap, W, cb, dtype, chunks = case
+    say(f"[queue edge] {name}")
+    _stream_vs_oracle(sr, H, D, P, cap, W, cb, dtype, 33, chunks, "own")
+
+
 @pytest.mark.parametrize("schedule", ["split", "whole"])
 def test_most_visible_pages(sr, schedule):
     """A call visiting exactly SR_MAX_VISIBLE_PAGES pages (1023 persistent + 1 current) runs and
