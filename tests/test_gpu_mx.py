@@ -258,6 +258,30 @@ def test_mx_degenerate_shapes(sr):
         cache.close()
 
 
+def test_mx_queue_split_uneven_xcds(sr):
+    """The queue split on an SR_MX cache with 260 items (20 heads x 13 query tiles at head_dim
+    64): XCDs own 32 or 33 items, so half of them have one split item and half none."""
+    import torch
+    rng = np.random.default_rng(29)
+    mk = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    H, D, n, W = 20, 64, 3300, 2
+    say(f"[mx queue edge] H={H} D={D} n={n} W={W}")
+    cache = sr.KVCache(sr.config_for(H, D, 0, n, W, n, 1, sr.SR_MX), None, None)
+    none = mk(1, 0, H, D)
+    model = oracle.StreamingCache(deq_k(none), deq_v(none), W)
+    for c in range(W + 1):
+        k, v = mk(n, H, D), mk(n, H, D)
+        cache.append(c, harness.to_dev(k, "bf16"), harness.to_dev(v, "bf16"))
+        model.append(c, deq_k(k), deq_v(v))
+    q = mk(n, H, D)
+    lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
+    out = cache.attention(0, harness.to_dev(q, "bf16"), lse=lse, softmax_scale=0.125)
+    ref = mx_reference(model, 0, q, 0.125, np.arange(n), causal_block=n)
+    ratio = gates.assert_mx(bf16_values(harness.to_host(out, "bf16")), lse.cpu().numpy(), *ref, ("queue", H, n))
+    say(f"[mx queue edge] err/bound {ratio}")
+    cache.close()
+
+
 def test_mx_call_errors(sr):
     """The fused qkv append is not offered on SR_MX caches; the ring stays as it was."""
     import torch

@@ -383,6 +383,7 @@ def test_degenerate_and_ragged_shapes(sr, case, schedule):
 QUEUE_EDGE = [  # H, D, P, cap, W, cb, dtype, chunks
     ("308 items, causal blocks, D=128", 11, 128, 500, 7000, 1, 1000, "bf16", [7000, 7000]),
     ("260 items, half the XCDs without split items, D=64", 20, 64, 0, 3300, 2, 3300, "bf16", [3300] * 3),
+    ("260 items, fp32", 20, 64, 0, 3300, 2, 3300, "f32", [3300] * 3),
 ]
 
 
