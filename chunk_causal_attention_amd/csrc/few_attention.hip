@@ -51,6 +51,18 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
 }
 
+// Maximum and sum over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 __device__ __forceinline__ void rec_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -236,18 +248,20 @@ __global__ __launch_bounds__(kWaves * 64) void few_attention_kernel(const FewArg
     wsum[j] = rec_load(head_rec + size_t(p) * a.stride + 32 + q);
   }
   __syncthreads();
-  if (tid < n_q) {
+  // Row q's maximum and sum over the pieces by wave q % 4, its lanes taking the pieces; then
+  // the weights of the row's pieces.
+  for (int q = wave; q < n_q; q += kWaves) {
     float mm = kMasked;
-    for (int p = 0; p < a.pieces; ++p) mm = fmaxf(mm, wmax[p * n_q + tid]);
+    for (int p = lane; p < a.pieces; p += 64) mm = fmaxf(mm, wmax[p * n_q + q]);
+    mm = wave_max(mm);
     float ll = 0.0f;
-    for (int p = 0; p < a.pieces; ++p) ll += wsum[p * n_q + tid] * __builtin_amdgcn_exp2f(wmax[p * n_q + tid] - mm);
-    mq[tid] = mm;
-    lq[tid] = ll;
-  }
-  __syncthreads();
-  for (int j = tid; j < np; j += kWaves * 64) {
-    const int q = j - (j / n_q) * n_q;
-    wmax[j] = __builtin_amdgcn_exp2f(wmax[j] - mq[q]) / lq[q];
+    for (int p = lane; p < a.pieces; p += 64) ll += wsum[p * n_q + q] * __builtin_amdgcn_exp2f(wmax[p * n_q + q] - mm);
+    ll = wave_sum(ll);
+    for (int p = lane; p < a.pieces; p += 64) wmax[p * n_q + q] = __builtin_amdgcn_exp2f(wmax[p * n_q + q] - mm) / ll;
+    if (lane == 0) {
+      mq[q] = mm;
+      lq[q] = ll;
+    }
   }
   __syncthreads();
   // Up to 32 records' loads in flight at a time, so a head of up to 64 pages takes one round
