@@ -549,8 +549,8 @@ def global_bytes(w):
 
 # Bytes past L2 per launch of the few-row split-K kernel (few_attention_kernel), as TRAFFIC.
 FEW_TRAFFIC = {
-    "d1": {"fetch_kib": 30543.1, "write_kib": 1307.5,
-           "few_sha256": "ab1e7145ace991e049df33267a975b4ece2ddd5ed8f341bd7b3d14480505d0de"},
+    "d1": {"fetch_kib": 30209.5, "write_kib": 684.9,
+           "few_sha256": "d8e1fecb5cf618f8d94159acbf7b53df3c0f5337c9f65ef3d0e297511606532d"},
 }
 FEW_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "few_attention.hip")
 

@@ -8,14 +8,15 @@
 // few rows only, so the call is bound by HBM, not by the matrix units.
 //
 // Decomposition.  Wave w of workgroup (head h, piece p) takes half a cache page -- keys
-// [64 (w % 2), 64 (w % 2) + 64) of page 2p + w / 2 of the head's key list -- with all the query
+// [64 (w % 2), 64 (w % 2) + 64) of page 4p + w / 2 of the head's key list -- with all the query
 // rows (at most 32) as the columns of the 32x32 matrix instructions.  Its K and V operands are
 // read straight from HBM into registers (each byte once, 32 lanes reading 512 contiguous
 // bytes): the page layout is the one the chunk-attention kernel reads from LDS, K rows in
 // operand order and V transposed, so the score registers of a lane are the P operand as they
 // stand.  A wave computes S^T = K Q^T, the probabilities against its own row max, and
-// O^T = V^T P^T; the four waves are merged in LDS into one record per workgroup (row max, row
-// sum, unnormalised O of the valid rows).  The last workgroup of a head to arrive merges the
+// O^T = V^T P^T; the eight waves (four pages) are merged in LDS into one record per workgroup
+// (row max, row sum, unnormalised O of the valid rows): four pages per record rather than two
+// halve the records that each head's merge loads, whose rate sets the kernel's tail.  The last workgroup of a head to arrive merges the
 // head's records in piece order -- the result does not depend on the order of arrival -- and
 // writes the output and the log-sum-exp.
 //
@@ -35,7 +36,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMasked = -1.0e30f;  // score of a key past the segment; also the empty-wave max
-constexpr int kWaves = 4;            // waves per workgroup: two pages, half a page each
+constexpr int kWaves = 8;            // waves per workgroup: half a page each
+constexpr int kPagesPerGroup = kWaves / 2;
 constexpr int kPad = 33;             // LDS row pitch (floats) of the wave-merge buffer
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -81,7 +83,7 @@ struct FewArgs {
   const char* vpool;
   int32_t n_q, H, total_pages;
   int32_t npages;     // pages of the key list (segments in order)
-  int32_t pieces;     // workgroups per head: ceil(npages / 2)
+  int32_t pieces;     // workgroups per head: ceil(npages / kPagesPerGroup)
   int32_t stride;     // floats per record: 64 + n_q * D
   float scale_log2;
   float* rec;         // H * pieces records
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kWaves * 64) void few_attention_kernel(const FewArg
   const int c = lane & 31, hl = lane >> 5;
   const int h = uniform(int(blockIdx.x) / a.pieces);
   const int piece = uniform(int(blockIdx.x) - h * a.pieces);
-  const int pi = 2 * piece + (wave >> 1), half = wave & 1;
+  const int pi = kPagesPerGroup * piece + (wave >> 1), half = wave & 1;
 
   // Page pi of the key list: its pool page and the valid keys of this wave's half.
   int page = 0, valid = 0;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kWaves * 64) void few_attention_kernel(const FewArg
       for (int sl = 0; sl < 4; ++sl) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[sl][db], p[sl], o[db], 0, 0, 0);
   }
 
-  // Merge the four waves: rescale to the workgroup's row max, sum in LDS.
+  // Merge the eight waves: rescale to the workgroup's row max, sum in LDS.
   if (hl == 0) {
     wm[wave][c] = m;
     wl[wave][c] = l;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kWaves * 64) void few_attention_kernel(const FewArg
 int64_t few_attention_record_floats(const Layout& L, const SegTable& t, int32_t n_q) {
   int64_t npages = 0;
   for (int s = 0; s < t.n; ++s) npages += (t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
-  const int64_t pieces = (npages + 1) / 2;
+  const int64_t pieces = (npages + kPagesPerGroup - 1) / kPagesPerGroup;
   return int64_t(L.H) * pieces * (64 + int64_t(n_q) * L.D);
 }
 
@@ -296,7 +298,7 @@ bool few_attention_shape_ok(const Layout& L, const SegTable& t, int32_t n_q) {
   if (L.dtype != SR_BF16 || (L.D != 64 && L.D != 128) || n_q < 1 || n_q > kFewRows) return false;
   int64_t npages = 0;
   for (int s = 0; s < t.n; ++s) npages += (t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
-  const int64_t pieces = (npages + 1) / 2;
+  const int64_t pieces = (npages + kPagesPerGroup - 1) / kPagesPerGroup;
   return npages > 0 && 2 * pieces * n_q <= int64_t(kWaves) * L.D * kPad;
 }
 
@@ -319,7 +321,7 @@ hipError_t launch_few_attention(const Layout& L, const void* pool, const SegTabl
   a.total_pages = L.total_pages;
   a.npages = 0;
   for (int s = 0; s < t.n; ++s) a.npages += (t.s[s].len + SR_PAGE_TOKENS - 1) / SR_PAGE_TOKENS;
-  a.pieces = (a.npages + 1) / 2;
+  a.pieces = (a.npages + kPagesPerGroup - 1) / kPagesPerGroup;
   a.stride = 64 + n_q * L.D;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.rec = ws.records;

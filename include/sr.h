@@ -363,7 +363,7 @@ sr_status sr_windows_attention(sr_kvcache* c, int32_t bank, const void* q, void*
  * attend to the persistent tokens of `bank` and to every window's tokens of the current chunk
  * (the whole frame), all visible.  out [n_rows][H][D], lse [H][n_rows] or NULL.  Iteration 6:
  * split-K.  On a bf16 cache with a workspace attached and n_rows <= 32, every head's keys are
- * split two pages per workgroup over the device and each head's partial results are merged by
+ * split four pages per workgroup over the device and each head's partial results are merged by
  * its last workgroup (in a fixed order: repeated calls give the same bits); otherwise the call
  * runs on the chunk-attention kernel (with its split schedule when a workspace is attached).
  * The workspace must not be in use by a call on another stream.  SR_E_STATE without a window
@@ -382,7 +382,7 @@ sr_status sr_global_attention(sr_kvcache* c, int32_t bank, const void* q, int32_
  * one small kernel on `stream` that zeroes its counters; every call leaves them at zero.
  * Same arguments and errors as sr_global_attention, plus SR_E_UNSUPPORTED when the call does
  * not fit the few-row kernel (a cache other than SR_BF16, head_dim other than 64 or 128, more
- * than 32 rows) or needs more scratch than the array holds (H * ceil(pages / 2) * (64 + n_rows *
+ * than 32 rows) or needs more scratch than the array holds (H * ceil(pages / 4) * (64 + n_rows *
  * head_dim) floats of records, pages = the call's key pages; H <= 4096); nothing is enqueued
  * then. */
 sr_status sr_global_attention_static(sr_kvcache* c, int32_t bank, const void* q, int32_t n_rows, void* out, float* lse,

@@ -88,15 +88,16 @@ def test_static_scratch_global_attention_two_calls(sr):
 
 
 def test_static_scratch_refuses_oversize_calls(sr):
-    """64 heads x 5 pieces x (64 + 32 x 128) floats of records exceed the 2^20-float array: the
-    call is refused before anything is enqueued and the output stays untouched."""
+    """64 heads x 5 pieces (17 pages, four per piece) x (64 + 32 x 128) floats of records exceed
+    the 2^20-float array: the call is refused before anything is enqueued and the output stays
+    untouched."""
     import torch
-    H, D, G, cap = 64, 128, 5, 8 * 128
+    H, D, G, cap = 64, 128, 5, 16 * 128
     cfg = sr.config_for(H, D, G, cap, 1, cap, 1, sr.SR_BF16)
     z = torch.zeros((1, G, H, D), dtype=torch.bfloat16, device="cuda")
     cache = sr.KVCache(cfg, z, z, workspace="own")
-    cache.set_window_layout([512], 2, 8)
-    x = torch.zeros((1024, H, D), dtype=torch.bfloat16, device="cuda")
+    cache.set_window_layout([1024], 2, 16)
+    x = torch.zeros((2048, H, D), dtype=torch.bfloat16, device="cuda")
     cache.append_windows(0, x, x)
     q = torch.zeros((32, H, D), dtype=torch.bfloat16, device="cuda")
     out = torch.full((32, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
