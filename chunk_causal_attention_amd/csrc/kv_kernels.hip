@@ -148,10 +148,10 @@ __device__ __forceinline__ u32x4_t narrow_piece(const float (&f)[4]) {
 }
 
 // RMS-normalises and rotates one piece (features x*E .. x*E+E-1) of one (token, head) row;
-// the CPR lanes holding the pieces of the row are consecutive and reduce together.  cs holds
-// the row's (cos, sin) per rotation pair.
+// the CPR lanes holding the pieces of the row are consecutive and reduce together.  gain holds
+// the piece's E gains, cs the row's (cos, sin) per rotation pair.
 template <int E, int CPR, int D>
-__device__ __forceinline__ void prep_piece(float (&f)[E], int x, const float* __restrict__ gain, float eps,
+__device__ __forceinline__ void prep_piece(float (&f)[E], int x, const float (&gain)[E], float eps,
                                            const float2* cs) {
   float ss = 0.0f;
 #pragma unroll
@@ -160,7 +160,7 @@ __device__ __forceinline__ void prep_piece(float (&f)[E], int x, const float* __
   for (int m = CPR / 2; m >= 1; m /= 2) ss += __shfl_xor(ss, m, CPR);
   const float scale = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + eps);
 #pragma unroll
-  for (int e = 0; e < E; ++e) f[e] = f[e] * scale * gain[x * E + e];
+  for (int e = 0; e < E; ++e) f[e] = f[e] * scale * gain[e];
 #pragma unroll
   for (int e = 0; e < E; e += 2) {
     const float2 r = cs[(x * E + e) / 2];
@@ -176,7 +176,10 @@ constexpr int kPrepHeads = 4;  // heads per workgroup of the fused append (they 
 // (cos, sin) of every (token, rotation pair) of the tile is computed once, into LDS: the angle
 // pos * theta in fp64, reduced to [-pi, pi], then the fp32 sine and cosine.  Per head, Q goes
 // straight to q_out; normalised, rotated K and plain V go through LDS into the page, as in
-// append_kernel.
+// append_kernel.  A thread always holds the same feature piece x (256 is a multiple of the D / E
+// pieces of a row), so its gains sit in registers for the whole kernel, and all IT of a head's
+// row pieces it handles are requested before the first is used: one memory round trip per head
+// instead of one (plus one for the gains) per piece.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prep_append_kernel(const T* __restrict__ qkv, const int32_t* __restrict__ pos,
                                                           int n, int H, const float* __restrict__ gq,
@@ -193,10 +196,19 @@ __global__ __launch_bounds__(256) void prep_append_kernel(const T* __restrict__ 
   __shared__ __align__(16) T vtile[kAppendTokens * PITCH];
   __shared__ float2 rot[kAppendTokens * CSP];
 
+  static_assert(256 % CPR == 0 && (kAppendTokens * CPR) % 256 == 0, "a thread keeps its feature piece");
+  constexpr int IT = kAppendTokens * CPR / 256;  // row pieces per thread and head
   const int t0 = blockIdx.x * kAppendTokens;
   const int tp = t0 % SR_PAGE_TOKENS;
   const u32x4_t z = {0, 0, 0, 0};
   const size_t hd = size_t(H) * D;
+  const int x = threadIdx.x % CPR;
+  float gqr[E], gkr[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    gqr[e] = gq[x * E + e];
+    gkr[e] = gk[x * E + e];
+  }
 
   for (int i = threadIdx.x; i < kAppendTokens * NP; i += blockDim.x) {
     const int r = i / NP, j = i % NP, t = t0 + r;
@@ -215,21 +227,28 @@ __global__ __launch_bounds__(256) void prep_append_kernel(const T* __restrict__ 
     const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
     // Every lane of a row group runs the reduction, also for rows past n (their values are
     // zero and their results are dropped).
-    for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
-      const int r = ci / CPR, x = ci % CPR, t = t0 + r;
+    u32x4_t wq[IT], wk[IT], wv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (threadIdx.x + it * 256) / CPR, t = t0 + r;
       const bool ok = t < n;
       const size_t src = (size_t(ok ? t : 0) * 3 * H + h) * D + x * E;
-      const u32x4_t wq = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src) : z;
-      const u32x4_t wk = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + hd) : z;
-      const u32x4_t wv = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + 2 * hd) : z;
+      wq[it] = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src) : z;
+      wk[it] = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + hd) : z;
+      wv[it] = ok ? *reinterpret_cast<const u32x4_t*>(qkv + src + 2 * hd) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (threadIdx.x + it * 256) / CPR, t = t0 + r;
+      const bool ok = t < n;
       float fq[E], fk[E];
-      widen_piece(wq, fq);
-      widen_piece(wk, fk);
-      prep_piece<E, CPR, D>(fq, x, gq, eps, rot + r * CSP);
-      prep_piece<E, CPR, D>(fk, x, gk, eps, rot + r * CSP);
+      widen_piece(wq[it], fq);
+      widen_piece(wk[it], fk);
+      prep_piece<E, CPR, D>(fq, x, gqr, eps, rot + r * CSP);
+      prep_piece<E, CPR, D>(fk, x, gkr, eps, rot + r * CSP);
       if (ok) *reinterpret_cast<u32x4_t*>(qout + (size_t(t) * H + h) * D + x * E) = narrow_piece(fq);
       *reinterpret_cast<u32x4_t*>(ktile + r * PITCH + x * E) = ok ? narrow_piece(fk) : z;
-      *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = wv;
+      *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = wv[it];
     }
     __syncthreads();
     T* kpage = kpool + page * SR_PAGE_TOKENS * D;
