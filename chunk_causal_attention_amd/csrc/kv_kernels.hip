@@ -47,9 +47,10 @@ __device__ __forceinline__ u32x4_t column_piece(const float* p, int pitch) {
                  __float_as_uint(p[3 * pitch])};
 }
 
-// One workgroup's share of an append: half page `half` (64 tokens) of head h.  Both K and V
-// rows go through LDS (coalesced 16-byte reads along the features), then are written piece by
-// piece in page order (coalesced 16-byte writes).  Tokens >= n are written as zeros.
+// One workgroup's share of an append (256 threads): half page `half` (64 tokens) of head h.
+// Both K and V rows go through LDS (coalesced 16-byte reads along the features), then are
+// written piece by piece in page order (coalesced 16-byte writes).  Tokens >= n are written as
+// zeros.
 template <typename T, int D>
 __device__ __forceinline__ void append_half_page(const T* __restrict__ k, const T* __restrict__ v, int n, int H,
                                                  T* __restrict__ kpool, T* __restrict__ vpool, int total_pages,
@@ -65,11 +66,22 @@ __device__ __forceinline__ void append_half_page(const T* __restrict__ k, const 
   const size_t page = size_t(h) * total_pages + page0 + t0 / SR_PAGE_TOKENS;
   const u32x4_t z = {0, 0, 0, 0};
 
-  for (int ci = threadIdx.x; ci < kAppendTokens * CPR; ci += blockDim.x) {
-    const int r = ci / CPR, x = ci % CPR, t = t0 + r;
+  // All IT row pieces of a thread (256 threads) are requested before the first is stored.
+  static_assert((kAppendTokens * CPR) % 256 == 0, "whole rounds of 256 threads");
+  constexpr int IT = kAppendTokens * CPR / 256;
+  u32x4_t wk[IT], wv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int ci = threadIdx.x + it * 256, r = ci / CPR, x = ci % CPR, t = t0 + r;
     const size_t src = (size_t(t) * H + h) * D + x * E;
-    *reinterpret_cast<u32x4_t*>(ktile + r * PITCH + x * E) = t < n ? *reinterpret_cast<const u32x4_t*>(k + src) : z;
-    *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = t < n ? *reinterpret_cast<const u32x4_t*>(v + src) : z;
+    wk[it] = t < n ? *reinterpret_cast<const u32x4_t*>(k + src) : z;
+    wv[it] = t < n ? *reinterpret_cast<const u32x4_t*>(v + src) : z;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int ci = threadIdx.x + it * 256, r = ci / CPR, x = ci % CPR;
+    *reinterpret_cast<u32x4_t*>(ktile + r * PITCH + x * E) = wk[it];
+    *reinterpret_cast<u32x4_t*>(vtile + r * PITCH + x * E) = wv[it];
   }
   __syncthreads();
 
