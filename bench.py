@@ -75,8 +75,8 @@ TRAFFIC = {
 ATTENTION_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "attention.hip")
 # The same counts for the fused-append kernel (prep_append_kernel in kv_kernels.hip), per launch.
 PREP_TRAFFIC = {
-    "c1p": {"fetch_kib": 42327.6, "write_kib": 84912.0,
-            "kv_sha256": "6c91f3f157b106b4fd69881c29a8ffd2055510af4731edc79645f9b6b27bdf1f"},
+    "c1p": {"fetch_kib": 42327.2, "write_kib": 84912.0,
+            "kv_sha256": "fa43d4c0a4050000aba2dd574b944cc817eb06ccaf5f22b74b50a422f45d25b6"},
 }
 KV_SRC = os.path.join(ROOT, "chunk_causal_attention_amd", "csrc", "kv_kernels.hip")
 
