@@ -61,7 +61,7 @@ typedef enum sr_status {
   SR_E_STATE = 2,       /* call not allowed in the current cache state (e.g. window full) */
   SR_E_NOMEM = 3,       /* pool smaller than sr_kvcache_required_bytes, or host allocation failed */
   SR_E_DEVICE = 4,      /* HIP runtime error while enqueuing */
-  SR_E_UNSUPPORTED = 5  /* valid request this build does not implement (e.g. head_dim) */
+  SR_E_UNSUPPORTED = 5  /* valid request the library does not implement (e.g. head_dim) */
 } sr_status;
 
 /* Cache element types.  SR_MX is the reduced-precision video attention of "The road to the
